@@ -1,0 +1,66 @@
+// Internal helpers shared by the libmt sources (device and host).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mt.h"
+#include "../../include/mt_kernels.h"
+
+namespace mt {
+
+// ---------------------------------------------------------------- bf16 bits
+// Round-to-nearest-even fp32 -> bf16; NaN stays a (quiet) NaN.
+__host__ __device__ inline uint16_t f2bf(float f) {
+  uint32_t u;
+#if defined(__HIP_DEVICE_COMPILE__)
+  u = __float_as_uint(f);
+#else
+  __builtin_memcpy(&u, &f, 4);
+#endif
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__host__ __device__ inline float bf2f(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __uint_as_float(u);
+#else
+  float f;
+  __builtin_memcpy(&f, &u, 4);
+  return f;
+#endif
+}
+
+__host__ __device__ inline uint32_t pack_bf2(float lo, float hi) {
+  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+
+// ---------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error; shapes are validated by the
+// C-ABI wrappers before these are called.
+hipError_t launch_gemm(const mt_gemm_args& a, hipStream_t s);
+hipError_t launch_rmsnorm_fwd(const float* x, const uint16_t* g, uint16_t* out, float* rstd,
+                              int64_t T, int h, float eps, hipStream_t s);
+hipError_t launch_rmsnorm_bwd(const float* dn, const float* x, const float* rstd,
+                              const uint16_t* g, const float* resid, float* dx,
+                              uint16_t* dx_bf16, float* dg, float* partial, int64_t T, int h,
+                              hipStream_t s);
+size_t rmsnorm_bwd_partial_bytes(int64_t T, int h);
+hipError_t launch_rope(uint16_t* qkv, int64_t T, int seq, int nq, int nkv, int d,
+                       const float* cos_t, const float* sin_t, int inverse, hipStream_t s);
+hipError_t launch_attn_fwd(const uint16_t* qkv, uint16_t* o, float* lse, int batch, int seq,
+                           int nq, int nkv, int d, hipStream_t s);
+hipError_t launch_attn_bwd(const uint16_t* qkv, const uint16_t* o, const uint16_t* dout,
+                           const float* lse, float* dsum, uint16_t* dqkv, int batch, int seq,
+                           int nq, int nkv, int d, hipStream_t s);
+hipError_t launch_cross_entropy(const float* logits, int64_t ld, const int32_t* labels, int64_t T,
+                                int V, float grad_scale, int64_t n_valid, uint16_t* dlogits,
+                                int64_t ld_d, float* loss_rows, float* loss_out, hipStream_t s);
+
+// Shape checks shared by the C-ABI wrappers and the engine.
+bool gemm_shape_ok(const mt_gemm_args& a, const char** why);
+
+}  // namespace mt

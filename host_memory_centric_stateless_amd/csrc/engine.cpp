@@ -1,0 +1,934 @@
+// The streaming engine behind mt_forward / mt_backward / mt_flush_grads /
+// mt_adamw_step.
+//
+// Method (citations by page and section):
+//   * fp32 master, grad and Adam m/v stay in host memory; the GPU only holds a
+//     ping-pong pair of flat bf16 layer buffers, one K-layer activation window
+//     and a pool of flat gradient slabs (zhichai.net
+//     "MegaTrain：单卡训百亿大模型的突破与实践", design points 1-2; m.lqnn.cn
+//     MegaTrain article, 二 and 三.1).
+//   * three streams -- prefetch (host->device weights), compute, offload
+//     (device->host gradients) -- ordered by events: a compute step waits for
+//     its buffer's weight_ready event, a copy into a buffer waits for the
+//     buffer_free event recorded after the last step that read it (lqnn 三.2;
+//     zhichai design point 4; blog.travelaiplan.net
+//     "單卡也能練 100B+：MegaTrain 實戰", 核心功能 2).
+//   * each streamed unit's gradient is written into a free slab, copied to a
+//     pinned host slab and added into the fp32 host gradient by a CPU worker;
+//     the slab returns to the pool afterwards (lqnn 三.3, 12 slabs by
+//     default).  Gradients are never accumulated across units on the GPU.
+//   * a checkpoint (the layer input, fp32) every K layers; backward walks the
+//     segments last to first, recomputes a segment's forwards into the window
+//     from its checkpoint, then runs its blocks backwards (zhichai design
+//     point 3; lqnn 三.4).
+//
+// MI355X choices (not from the pages): which buffer a load goes into is
+// decided ahead of time by simulating the two buffers over the whole
+// micro-batch (a unit still resident is reused instead of re-copied, e.g. the
+// last layers of a segment when its backward starts); the forward of the last
+// segment writes the window directly, so that segment is not recomputed; the
+// LM head is streamed through the same buffers in vocabulary chunks.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <atomic>
+#include <chrono>
+#include <deque>
+#include <memory>
+#include <string>
+#include <vector>
+
+#include "common.h"
+#include "host_ops.h"
+#include "plan.h"
+
+using namespace mt;
+
+namespace {
+
+enum Kind { K_FWD, K_HEAD_LOGITS, K_CE, K_HEAD_GRAD, K_RECOMP, K_BWD, K_EMBED_GRAD };
+
+struct Step {
+  Kind kind;
+  int layer = -1, chunk = -1, slot = -1;
+  bool write_y = true;
+  int unit = -1;  // streamed unit needed (layer l -> l, head chunk c -> L + c)
+  int buf = -1;   // buffer holding it
+  int load = -1;  // load that brings it in (first user only), else -1
+};
+
+struct Load {
+  int unit, buf, after;  // issue once step `after` is enqueued (-1: at once)
+};
+
+struct Job {
+  enum { SLAB, EMBED } kind;
+  int slab = -1, group = 0, parity = 0;
+  int64_t e0 = 0, n = 0;
+  bool add = false;
+  std::vector<int32_t> tok;
+};
+
+enum State { ST_UNBOUND, ST_IDLE, ST_FWD, ST_BWD, ST_FLUSHED };
+
+double now_s() {
+  return std::chrono::duration<double>(std::chrono::steady_clock::now().time_since_epoch())
+      .count();
+}
+
+}  // namespace
+
+struct mt_ctx {
+  Plan p;
+  int device = 0;
+  hipStream_t sp = nullptr, sc = nullptr, so = nullptr;
+  uint16_t* wbuf[2] = {nullptr, nullptr};
+  float* dslab[64] = {};
+  uint8_t* window = nullptr;
+  uint8_t* ckpt = nullptr;
+  uint8_t* ws = nullptr;
+  int nslab = 0;
+
+  struct Bind {
+    float *master = nullptr, *grad = nullptr, *m = nullptr, *v = nullptr;
+    int64_t n = 0;
+    uint16_t* pinned = nullptr;  // bf16 working copy (blocks, head)
+  };
+  std::vector<Bind> layers;
+  Bind head, embed;
+
+  float* hslab[64] = {};
+  float* x0_stage[2] = {};
+  float* dx0_stage[2] = {};
+  int32_t* lab_stage[2] = {};
+  float* loss_pin = nullptr;
+  static constexpr int kLossRing = 4096;
+
+  hipEvent_t ev_ready[2] = {}, ev_free[2] = {}, ev_x0[2] = {}, ev_bwd_done[2] = {};
+  hipEvent_t ev_written[64] = {}, ev_copied[64] = {}, ev_dx0[2] = {}, ev_dx0_copied[2] = {};
+  bool x0_used[2] = {false, false}, bwd_used[2] = {false, false};
+
+  int buf_unit[2] = {-1, -1};
+  std::vector<Step> steps;
+  std::vector<Load> loads;
+  size_t next_load = 0, next_step = 0, split = 0;
+  int64_t mb = 0;
+  int parity = 0;
+  int dy_idx = 0;
+  bool head_grad_first = true;
+  std::vector<int32_t> tok_cur;
+  State state = ST_UNBOUND;
+  int accumulate = 0;
+
+  std::unique_ptr<ThreadPool> pool;
+  std::thread worker;
+  std::mutex mu;
+  std::condition_variable cv, slab_cv, idle_cv;
+  std::deque<Job> jobs;
+  int outstanding = 0;
+  bool stop = false;
+  std::vector<int> free_slabs;
+  int embed_busy[2] = {0, 0};
+  int delay_us = 0;
+
+  std::mutex err_mu;
+  std::string err;
+  std::atomic<bool> poisoned{false};
+  std::vector<std::pair<float*, int>> pending_loss;
+  int loss_next = 0;
+  mt_stats st{};
+
+  void set_err(const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    std::lock_guard<std::mutex> g(err_mu);
+    err = buf;
+  }
+  mt_status fail_hip(hipError_t e, const char* what) {
+    set_err("%s: %s", what, hipGetErrorString(e));
+    poisoned = true;
+    return MT_E_HIP;
+  }
+
+  uint8_t* slot_base(int w) const { return window + (size_t)w * p.slot.bytes; }
+  float* ckpt_ptr(int j) {
+    if (j == 0) return reinterpret_cast<float*>(ws + p.ws.x0[parity]);
+    return reinterpret_cast<float*>(ckpt + (size_t)(j - 1) * round_bytes((size_t)p.T * p.c.hidden * 4));
+  }
+  float* slot_x(int w) { return reinterpret_cast<float*>(slot_base(w) + p.slot.x); }
+  template <class T>
+  T* wsp(size_t off) { return reinterpret_cast<T*>(ws + off); }
+
+  const Bind& bind_of(int group) const {
+    if (group == MT_GROUP_HEAD) return head;
+    if (group == MT_GROUP_EMBED) return embed;
+    return layers[group];
+  }
+  // Pinned source and element count of a streamed unit.
+  void unit_src(int u, const uint16_t** src, int64_t* n) const {
+    const int L = p.c.n_layers;
+    if (u < L) {
+      *src = layers[u].pinned;
+      *n = p.layer_elems;
+    } else {
+      const int c = u - L;
+      *src = head.pinned + p.chunk_e0[c];
+      *n = p.chunk_e0[c + 1] - p.chunk_e0[c];
+    }
+  }
+};
+
+#define MT_HIP(ctx, expr)                                          \
+  do {                                                             \
+    hipError_t e_ = (expr);                                        \
+    if (e_ != hipSuccess) return (ctx)->fail_hip(e_, #expr);       \
+  } while (0)
+
+namespace {
+
+// ------------------------------------------------------------ activations
+struct Acts {
+  float* x;
+  float* rstd1;
+  uint16_t* n1;
+  uint16_t* qkv;
+  uint16_t* o;
+  float* lse;
+  float* h1;
+  float* rstd2;
+  uint16_t* n2;
+  uint16_t* gu;
+  uint16_t* m;
+};
+
+Acts acts_of(mt_ctx* c, int w, float* x) {
+  uint8_t* b = c->slot_base(w);
+  const SlotLayout& s = c->p.slot;
+  return Acts{x,
+              reinterpret_cast<float*>(b + s.rstd1),
+              reinterpret_cast<uint16_t*>(b + s.n1),
+              reinterpret_cast<uint16_t*>(b + s.qkv),
+              reinterpret_cast<uint16_t*>(b + s.o),
+              reinterpret_cast<float*>(b + s.lse),
+              reinterpret_cast<float*>(b + s.h1),
+              reinterpret_cast<float*>(b + s.rstd2),
+              reinterpret_cast<uint16_t*>(b + s.n2),
+              reinterpret_cast<uint16_t*>(b + s.gu),
+              reinterpret_cast<uint16_t*>(b + s.m)};
+}
+
+hipError_t gemm(hipStream_t s, int layout, int epi, int64_t M, int64_t N, int64_t K,
+                const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, void* C,
+                int64_t ldc, const float* R = nullptr, int64_t ldr = 0, uint16_t* gu = nullptr,
+                int64_t ldgu = 0, int64_t ffn = 0) {
+  mt_gemm_args a{layout, epi, M, N, K, A, lda, B, ldb, C, ldc, R, ldr, gu, ldgu, ffn};
+  return launch_gemm(a, s);
+}
+
+#define CK(expr)                            \
+  do {                                      \
+    hipError_t e_ = (expr);                 \
+    if (e_ != hipSuccess) return e_;        \
+  } while (0)
+
+// One decoder block forward on weights W (flat bf16 layer).  y == nullptr
+// skips the down projection (its output is not needed).
+hipError_t block_forward(mt_ctx* c, const uint16_t* W, const Acts& a, float* y) {
+  const Plan& p = c->p;
+  const mt_config& g = p.c;
+  const int64_t T = p.T, h = g.hidden, F = g.ffn;
+  hipStream_t s = c->sc;
+  const TensorOff* L = p.layer;
+  CK(launch_rmsnorm_fwd(a.x, W + L[T_ATTN_NORM].off, a.n1, a.rstd1, T, (int)h, g.rms_eps, s));
+  CK(gemm(s, MT_GEMM_NT, MT_EPI_BF16, T, p.ldq, h, a.n1, h, W + L[T_WQ].off, h, a.qkv, p.ldq));
+  CK(launch_rope(a.qkv, T, g.seq_len, g.n_heads, g.n_kv_heads, g.head_dim,
+                 c->wsp<float>(p.ws.cos_t), c->wsp<float>(p.ws.sin_t), 0, s));
+  CK(launch_attn_fwd(a.qkv, a.o, a.lse, g.micro_batch, g.seq_len, g.n_heads, g.n_kv_heads,
+                     g.head_dim, s));
+  CK(gemm(s, MT_GEMM_NT, MT_EPI_F32_RESID, T, h, p.qd, a.o, p.qd, W + L[T_WO].off, p.qd, a.h1, h,
+          a.x, h));
+  CK(launch_rmsnorm_fwd(a.h1, W + L[T_MLP_NORM].off, a.n2, a.rstd2, T, (int)h, g.rms_eps, s));
+  CK(gemm(s, MT_GEMM_NT, MT_EPI_SWIGLU, T, F, h, a.n2, h, W + L[T_WGATE].off, h, a.m, F, nullptr,
+          0, a.gu, 2 * F, F));
+  if (y)
+    CK(gemm(s, MT_GEMM_NT, MT_EPI_F32_RESID, T, h, F, a.m, F, W + L[T_WDOWN].off, F, y, h, a.h1,
+            h));
+  return hipSuccess;
+}
+
+// One decoder block backward.  dy/dyb: gradient of the block output (fp32 and
+// bf16); writes dx/dxb (gradient of the block input) and every weight
+// gradient into `slab` at the layer's flat offsets.
+hipError_t block_backward(mt_ctx* c, const uint16_t* W, const Acts& a, const float* dy,
+                          uint16_t* dyb, float* dx, float* slab) {
+  const Plan& p = c->p;
+  const mt_config& g = p.c;
+  const int64_t T = p.T, h = g.hidden, F = g.ffn;
+  hipStream_t s = c->sc;
+  const TensorOff* L = p.layer;
+  uint16_t* dgu = c->wsp<uint16_t>(p.ws.dgu);
+  float* dn = c->wsp<float>(p.ws.dn);
+  float* dh1 = c->wsp<float>(p.ws.dh1);
+  uint16_t* dh1b = c->wsp<uint16_t>(p.ws.dh1b);
+  uint16_t* dout = c->wsp<uint16_t>(p.ws.dout);
+  uint16_t* dqkv = c->wsp<uint16_t>(p.ws.dqkv);
+  float* partial = c->wsp<float>(p.ws.partial);
+  // MLP: dm = dy Wd, fused SwiGLU backward -> dgu = [da | du]
+  CK(gemm(s, MT_GEMM_NN, MT_EPI_SWIGLU_BWD, T, F, h, dyb, h, W + L[T_WDOWN].off, F, dgu, 2 * F,
+          nullptr, 0, a.gu, 2 * F, F));
+  CK(gemm(s, MT_GEMM_TN, MT_EPI_F32, h, F, T, dyb, h, a.m, F, slab + L[T_WDOWN].off, F));
+  CK(gemm(s, MT_GEMM_TN, MT_EPI_F32, 2 * F, h, T, dgu, 2 * F, a.n2, h, slab + L[T_WGATE].off, h));
+  CK(gemm(s, MT_GEMM_NN, MT_EPI_F32, T, h, 2 * F, dgu, 2 * F, W + L[T_WGATE].off, h, dn, h));
+  CK(launch_rmsnorm_bwd(dn, a.h1, a.rstd2, W + L[T_MLP_NORM].off, dy, dh1, dh1b,
+                        slab + L[T_MLP_NORM].off, partial, T, (int)h, s));
+  // attention
+  CK(gemm(s, MT_GEMM_NN, MT_EPI_BF16, T, p.qd, h, dh1b, h, W + L[T_WO].off, p.qd, dout, p.qd));
+  CK(gemm(s, MT_GEMM_TN, MT_EPI_F32, h, p.qd, T, dh1b, h, a.o, p.qd, slab + L[T_WO].off, p.qd));
+  CK(launch_attn_bwd(a.qkv, a.o, dout, a.lse, c->wsp<float>(p.ws.dsum), dqkv, g.micro_batch,
+                     g.seq_len, g.n_heads, g.n_kv_heads, g.head_dim, s));
+  CK(launch_rope(dqkv, T, g.seq_len, g.n_heads, g.n_kv_heads, g.head_dim,
+                 c->wsp<float>(p.ws.cos_t), c->wsp<float>(p.ws.sin_t), 1, s));
+  CK(gemm(s, MT_GEMM_TN, MT_EPI_F32, p.ldq, h, T, dqkv, p.ldq, a.n1, h, slab + L[T_WQ].off, h));
+  CK(gemm(s, MT_GEMM_NN, MT_EPI_F32, T, h, p.ldq, dqkv, p.ldq, W + L[T_WQ].off, h, dn, h));
+  CK(launch_rmsnorm_bwd(dn, a.x, a.rstd1, W + L[T_ATTN_NORM].off, dh1, dx, dyb,
+                        slab + L[T_ATTN_NORM].off, partial, T, (int)h, s));
+  return hipSuccess;
+}
+
+// ------------------------------------------------------------- schedule
+void build_steps(mt_ctx* c) {
+  const Plan& p = c->p;
+  const int L = p.c.n_layers, K = p.c.ckpt_interval, nseg = p.n_segments;
+  const int last0 = (nseg - 1) * K;
+  std::vector<Step>& st = c->steps;
+  st.clear();
+  for (int l = 0; l < L; ++l) {
+    Step s{K_FWD};
+    s.layer = l;
+    s.slot = l % K;
+    s.unit = l;
+    st.push_back(s);
+  }
+  for (int ch = 0; ch < p.n_chunks; ++ch) {
+    Step s{K_HEAD_LOGITS};
+    s.chunk = ch;
+    s.unit = L + ch;
+    st.push_back(s);
+  }
+  st.push_back(Step{K_CE});
+  c->split = st.size();
+  for (int ch = p.n_chunks - 1; ch >= 0; --ch) {
+    Step s{K_HEAD_GRAD};
+    s.chunk = ch;
+    s.unit = L + ch;
+    st.push_back(s);
+  }
+  for (int seg = nseg - 1; seg >= 0; --seg) {
+    const int lo = seg * K, hi = std::min(L, lo + K);
+    if (lo != last0) {
+      for (int l = lo; l < hi; ++l) {
+        Step s{K_RECOMP};
+        s.layer = l;
+        s.slot = l - lo;
+        s.unit = l;
+        s.write_y = (l + 1 < hi);
+        st.push_back(s);
+      }
+    }
+    for (int l = hi - 1; l >= lo; --l) {
+      Step s{K_BWD};
+      s.layer = l;
+      s.slot = l - lo;
+      s.unit = l;
+      st.push_back(s);
+    }
+  }
+  st.push_back(Step{K_EMBED_GRAD});
+
+  // Two-buffer simulation: reuse a resident unit; otherwise evict the buffer
+  // whose content is needed latest (or never), and issue the copy right after
+  // the last step that reads that buffer.
+  c->loads.clear();
+  int content[2] = {c->buf_unit[0], c->buf_unit[1]};
+  int last_use[2] = {-1, -1};
+  const int n = (int)st.size();
+  for (int i = 0; i < n; ++i) {
+    Step& s = st[i];
+    if (s.unit < 0) continue;
+    int b = -1;
+    for (int k = 0; k < 2; ++k)
+      if (content[k] == s.unit) b = k;
+    if (b < 0) {
+      int nu[2];
+      for (int k = 0; k < 2; ++k) {
+        nu[k] = n + 1;
+        for (int j = i; j < n; ++j)
+          if (st[j].unit >= 0 && st[j].unit == content[k]) {
+            nu[k] = j;
+            break;
+          }
+      }
+      // never evict the buffer the previous step uses (it may still run)
+      int prev = -1;
+      for (int j = i - 1; j >= 0; --j)
+        if (st[j].unit >= 0) {
+          prev = st[j].buf;
+          break;
+        }
+      if (prev >= 0)
+        b = 1 - prev;
+      else
+        b = (nu[0] >= nu[1]) ? 0 : 1;
+      c->loads.push_back(Load{s.unit, b, last_use[b]});
+      s.load = (int)c->loads.size() - 1;
+      content[b] = s.unit;
+    }
+    s.buf = b;
+    last_use[b] = i;
+  }
+  c->buf_unit[0] = content[0];
+  c->buf_unit[1] = content[1];
+  c->next_load = 0;
+  c->next_step = 0;
+}
+
+mt_status issue_load(mt_ctx* c, const Load& ld) {
+  const uint16_t* src;
+  int64_t n;
+  c->unit_src(ld.unit, &src, &n);
+  MT_HIP(c, hipStreamWaitEvent(c->sp, c->ev_free[ld.buf], 0));
+  MT_HIP(c, hipMemcpyAsync(c->wbuf[ld.buf], src, (size_t)n * 2, hipMemcpyHostToDevice, c->sp));
+  MT_HIP(c, hipEventRecord(c->ev_ready[ld.buf], c->sp));
+  c->st.h2d_bytes += n * 2;
+  c->st.weight_loads += 1;
+  return MT_OK;
+}
+
+mt_status issue_ready_loads(mt_ctx* c, int enqueued_upto) {
+  while (c->next_load < c->loads.size() && c->loads[c->next_load].after <= enqueued_upto) {
+    mt_status r = issue_load(c, c->loads[c->next_load]);
+    if (r != MT_OK) return r;
+    ++c->next_load;
+  }
+  return MT_OK;
+}
+
+// --------------------------------------------------------------- slabs
+int acquire_slab(mt_ctx* c) {
+  std::unique_lock<std::mutex> lk(c->mu);
+  if (c->free_slabs.empty()) {
+    c->st.slab_waits += 1;
+    const double t0 = now_s();
+    c->slab_cv.wait(lk, [&] { return !c->free_slabs.empty() || c->poisoned.load(); });
+    c->st.slab_wait_s += now_s() - t0;
+  }
+  if (c->free_slabs.empty()) return -1;
+  int s = c->free_slabs.back();
+  c->free_slabs.pop_back();
+  return s;
+}
+
+// Gradient of a unit is complete in device slab s: copy it out and hand it to
+// the worker.
+mt_status offload_slab(mt_ctx* c, int s, int group, int64_t e0, int64_t n) {
+  MT_HIP(c, hipEventRecord(c->ev_written[s], c->sc));
+  MT_HIP(c, hipStreamWaitEvent(c->so, c->ev_written[s], 0));
+  MT_HIP(c, hipMemcpyAsync(c->hslab[s], c->dslab[s], (size_t)n * 4, hipMemcpyDeviceToHost, c->so));
+  MT_HIP(c, hipEventRecord(c->ev_copied[s], c->so));
+  c->st.d2h_bytes += n * 4;
+  Job j;
+  j.kind = Job::SLAB;
+  j.slab = s;
+  j.group = group;
+  j.e0 = e0;
+  j.n = n;
+  j.add = c->accumulate != 0;
+  {
+    std::lock_guard<std::mutex> g(c->mu);
+    c->jobs.push_back(std::move(j));
+    c->outstanding += 1;
+  }
+  c->cv.notify_all();
+  return MT_OK;
+}
+
+void worker_main(mt_ctx* c) {
+  (void)hipSetDevice(c->device);
+  for (;;) {
+    Job j;
+    {
+      std::unique_lock<std::mutex> lk(c->mu);
+      c->cv.wait(lk, [&] { return c->stop || !c->jobs.empty(); });
+      if (c->jobs.empty()) return;
+      j = std::move(c->jobs.front());
+      c->jobs.pop_front();
+    }
+    hipError_t e = hipEventSynchronize(j.kind == Job::SLAB ? c->ev_copied[j.slab]
+                                                           : c->ev_dx0_copied[j.parity]);
+    if (e != hipSuccess) {
+      c->set_err("worker: hipEventSynchronize: %s", hipGetErrorString(e));
+      c->poisoned = true;
+    } else {
+      if (c->delay_us > 0) std::this_thread::sleep_for(std::chrono::microseconds(c->delay_us));
+      const double t0 = now_s();
+      if (j.kind == Job::SLAB) {
+        const mt_ctx::Bind& b = c->bind_of(j.group);
+        accumulate(*c->pool, b.grad + j.e0, c->hslab[j.slab], j.n, j.add);
+      } else {
+        const int64_t h = c->p.c.hidden;
+        if (!j.add) memset(c->embed.grad, 0, (size_t)c->embed.n * sizeof(float));
+        embed_scatter(*c->pool, c->embed.grad, j.tok.data(), (int64_t)j.tok.size(), h,
+                      c->dx0_stage[j.parity]);
+      }
+      std::lock_guard<std::mutex> g(c->mu);
+      c->st.accumulate_s += now_s() - t0;
+    }
+    {
+      std::lock_guard<std::mutex> g(c->mu);
+      if (j.kind == Job::SLAB)
+        c->free_slabs.push_back(j.slab);
+      else
+        c->embed_busy[j.parity] = 0;
+      c->outstanding -= 1;
+    }
+    c->slab_cv.notify_all();
+    c->idle_cv.notify_all();
+  }
+}
+
+// ---------------------------------------------------------- step bodies
+mt_status run_step(mt_ctx* c, const Step& s) {
+  const Plan& p = c->p;
+  const mt_config& g = p.c;
+  const int L = g.n_layers, K = g.ckpt_interval;
+  const int64_t T = p.T, h = g.hidden, V = g.vocab;
+  hipStream_t cs = c->sc;
+  const uint16_t* W = s.buf >= 0 ? c->wbuf[s.buf] : nullptr;
+  if (s.load >= 0) MT_HIP(c, hipStreamWaitEvent(cs, c->ev_ready[s.buf], 0));
+
+  switch (s.kind) {
+    case K_FWD:
+    case K_RECOMP: {
+      const int l = s.layer;
+      const int w = s.slot;
+      float* x = (l % K == 0) ? c->ckpt_ptr(l / K) : c->slot_x(w);
+      float* y = nullptr;
+      if (s.kind == K_FWD) {
+        if (l == L - 1)
+          y = c->wsp<float>(p.ws.xL);
+        else if ((l + 1) % K == 0)
+          y = c->ckpt_ptr((l + 1) / K);
+        else
+          y = c->slot_x(w + 1);
+      } else if (s.write_y) {
+        y = c->slot_x(w + 1);
+      }
+      MT_HIP(c, block_forward(c, W, acts_of(c, w, x), y));
+      c->st.layer_forwards += 1;
+      break;
+    }
+    case K_HEAD_LOGITS: {
+      const int ch = s.chunk;
+      const uint16_t* Wr = W + (ch == 0 ? p.head[1].off : 0);
+      const int64_t r0 = p.chunk_row0[ch], nr = p.chunk_row0[ch + 1] - r0;
+      if (ch == 0)
+        MT_HIP(c, launch_rmsnorm_fwd(c->wsp<float>(p.ws.xL), W + p.head[0].off,
+                                     c->wsp<uint16_t>(p.ws.xf), c->wsp<float>(p.ws.rstd_f), T,
+                                     (int)h, g.rms_eps, cs));
+      MT_HIP(c, gemm(cs, MT_GEMM_NT, MT_EPI_F32, T, nr, h, c->wsp<uint16_t>(p.ws.xf), h, Wr, h,
+                     c->wsp<float>(p.ws.logits) + r0, V));
+      break;
+    }
+    case K_CE: {
+      break;  // launched by mt_forward, which knows the labels
+    }
+    case K_HEAD_GRAD: {
+      const int ch = s.chunk;
+      const int sl = acquire_slab(c);
+      if (sl < 0) return MT_E_ABORTED;
+      float* slab = c->dslab[sl];
+      const int64_t e0 = p.chunk_e0[ch], ne = p.chunk_e0[ch + 1] - e0;
+      const uint16_t* Wr = W + (ch == 0 ? p.head[1].off : 0);
+      float* dWr = slab + (ch == 0 ? p.head[1].off : 0);
+      const int64_t r0 = p.chunk_row0[ch], nr = p.chunk_row0[ch + 1] - r0;
+      if (ch == 0 && p.head[1].off > p.head[0].numel)
+        MT_HIP(c, hipMemsetAsync(slab, 0, (size_t)p.head[1].off * 4, cs));
+      const uint16_t* dl = c->wsp<uint16_t>(p.ws.dlogits) + r0;
+      MT_HIP(c, gemm(cs, MT_GEMM_NN, c->head_grad_first ? MT_EPI_F32 : MT_EPI_F32_ACCUM, T, h, nr,
+                     dl, V, Wr, h, c->wsp<float>(p.ws.dxf), h));
+      c->head_grad_first = false;
+      MT_HIP(c, gemm(cs, MT_GEMM_TN, MT_EPI_F32, nr, h, T, dl, V, c->wsp<uint16_t>(p.ws.xf), h,
+                     dWr, h));
+      if (ch == 0) {
+        c->dy_idx = 0;
+        MT_HIP(c, launch_rmsnorm_bwd(c->wsp<float>(p.ws.dxf), c->wsp<float>(p.ws.xL),
+                                     c->wsp<float>(p.ws.rstd_f), W + p.head[0].off, nullptr,
+                                     c->wsp<float>(p.ws.dy0), c->wsp<uint16_t>(p.ws.dyb), slab,
+                                     c->wsp<float>(p.ws.partial), T, (int)h, cs));
+      }
+      mt_status r = offload_slab(c, sl, MT_GROUP_HEAD, e0, ne);
+      if (r != MT_OK) return r;
+      break;
+    }
+    case K_BWD: {
+      const int l = s.layer, w = s.slot;
+      const int sl = acquire_slab(c);
+      if (sl < 0) return MT_E_ABORTED;
+      float* slab = c->dslab[sl];
+      if (p.layer_elems != p.layer[T_WDOWN].off + p.layer[T_WDOWN].numel ||
+          p.layer[T_WQ].off != p.layer[T_ATTN_NORM].numel ||
+          p.layer[T_MLP_NORM].numel + p.layer[T_MLP_NORM].off != p.layer[T_WGATE].off)
+        MT_HIP(c, hipMemsetAsync(slab, 0, (size_t)p.layer_elems * 4, cs));
+      float* x = (l % K == 0) ? c->ckpt_ptr(l / K) : c->slot_x(w);
+      float* dy = c->wsp<float>(c->dy_idx ? p.ws.dy1 : p.ws.dy0);
+      float* dx = c->wsp<float>(c->dy_idx ? p.ws.dy0 : p.ws.dy1);
+      MT_HIP(c, block_backward(c, W, acts_of(c, w, x), dy, c->wsp<uint16_t>(p.ws.dyb), dx, slab));
+      c->dy_idx ^= 1;
+      c->st.layer_backwards += 1;
+      mt_status r = offload_slab(c, sl, l, 0, p.layer_elems);
+      if (r != MT_OK) return r;
+      break;
+    }
+    case K_EMBED_GRAD: {
+      const int par = c->parity;
+      {  // the staging buffer of two micro-batches ago must be consumed
+        std::unique_lock<std::mutex> lk(c->mu);
+        c->idle_cv.wait(lk, [&] { return c->embed_busy[par] == 0 || c->poisoned.load(); });
+        if (c->poisoned) return MT_E_ABORTED;
+        c->embed_busy[par] = 1;
+      }
+      float* dx0 = c->wsp<float>(c->dy_idx ? p.ws.dy1 : p.ws.dy0);
+      MT_HIP(c, hipEventRecord(c->ev_dx0[par], cs));
+      MT_HIP(c, hipStreamWaitEvent(c->so, c->ev_dx0[par], 0));
+      MT_HIP(c, hipMemcpyAsync(c->dx0_stage[par], dx0, (size_t)T * h * 4, hipMemcpyDeviceToHost,
+                               c->so));
+      MT_HIP(c, hipEventRecord(c->ev_dx0_copied[par], c->so));
+      c->st.d2h_bytes += T * h * 4;
+      Job j;
+      j.kind = Job::EMBED;
+      j.parity = par;
+      j.add = c->accumulate != 0;
+      j.tok = c->tok_cur;
+      {
+        std::lock_guard<std::mutex> gd(c->mu);
+        c->jobs.push_back(std::move(j));
+        c->outstanding += 1;
+      }
+      c->cv.notify_all();
+      MT_HIP(c, hipEventRecord(c->ev_bwd_done[par], cs));
+      c->bwd_used[par] = true;
+      break;
+    }
+  }
+  if (s.buf >= 0) MT_HIP(c, hipEventRecord(c->ev_free[s.buf], cs));
+  return MT_OK;
+}
+
+// Enqueue steps [next_step, end), issuing each copy as soon as the step that
+// frees its buffer is enqueued.
+mt_status run_until(mt_ctx* c, size_t end, int64_t n_valid, float grad_scale) {
+  mt_status r = issue_ready_loads(c, (int)c->next_step - 1);
+  if (r != MT_OK) return r;
+  for (; c->next_step < end; ++c->next_step) {
+    const Step& s = c->steps[c->next_step];
+    if (s.load >= 0 && (size_t)s.load >= c->next_load) {
+      c->set_err("internal: copy for step %zu not issued", c->next_step);
+      c->poisoned = true;
+      return MT_E_STATE;
+    }
+    if (s.kind == K_CE) {
+      const Plan& p = c->p;
+      MT_HIP(c, launch_cross_entropy(c->wsp<float>(p.ws.logits), p.c.vocab,
+                                     c->wsp<int32_t>(p.ws.labels[c->parity]), p.T, p.c.vocab,
+                                     grad_scale, n_valid, c->wsp<uint16_t>(p.ws.dlogits),
+                                     p.c.vocab, c->wsp<float>(p.ws.loss_rows),
+                                     c->wsp<float>(p.ws.loss), c->sc));
+    } else {
+      r = run_step(c, s);
+      if (r != MT_OK) return r;
+    }
+    r = issue_ready_loads(c, (int)c->next_step);
+    if (r != MT_OK) return r;
+  }
+  return MT_OK;
+}
+
+mt_status check_live(const mt_ctx* c) {
+  if (!c) return MT_E_ARG;
+  if (c->poisoned) return MT_E_ABORTED;
+  return MT_OK;
+}
+
+}  // namespace
+
+// =================================================================== C ABI
+extern "C" mt_status mt_create(const mt_config* cfg, const mt_device_arena* a, mt_ctx** out) {
+  if (!cfg || !a || !out) return MT_E_ARG;
+  *out = nullptr;
+  std::unique_ptr<mt_ctx> c(new (std::nothrow) mt_ctx());
+  if (!c) return MT_E_NOMEM;
+  if (!make_plan(*cfg, &c->p).empty()) return MT_E_ARG;
+  const Plan& p = c->p;
+  c->nslab = cfg->n_grad_slabs;
+  auto al = [](const void* q) { return q && ((uintptr_t)q % 256) == 0; };
+  if (!al(a->weight_buf[0]) || !al(a->weight_buf[1]) || !al(a->window) || !al(a->workspace))
+    return MT_E_ARG;
+  if (p.n_segments > 1 && !al(a->checkpoints)) return MT_E_ARG;
+  for (int i = 0; i < c->nslab; ++i)
+    if (!al(a->grad_slab[i])) return MT_E_ARG;
+  if (!a->stream_prefetch || !a->stream_compute || !a->stream_offload ||
+      a->stream_prefetch == a->stream_compute || a->stream_prefetch == a->stream_offload ||
+      a->stream_compute == a->stream_offload)
+    return MT_E_ARG;
+  if (a->weight_buf_bytes < p.weight_buf_bytes || a->grad_slab_bytes < p.slab_bytes ||
+      a->window_bytes < p.window_bytes || a->workspace_bytes < p.ws.bytes ||
+      (p.n_segments > 1 && a->checkpoints_bytes < p.ckpt_bytes))
+    return MT_E_NOMEM;
+
+  hipError_t e = hipGetDevice(&c->device);
+  if (e != hipSuccess) return MT_E_HIP;
+  c->sp = (hipStream_t)a->stream_prefetch;
+  c->sc = (hipStream_t)a->stream_compute;
+  c->so = (hipStream_t)a->stream_offload;
+  c->wbuf[0] = (uint16_t*)a->weight_buf[0];
+  c->wbuf[1] = (uint16_t*)a->weight_buf[1];
+  for (int i = 0; i < c->nslab; ++i) c->dslab[i] = (float*)a->grad_slab[i];
+  c->window = (uint8_t*)a->window;
+  c->ckpt = (uint8_t*)a->checkpoints;
+  c->ws = (uint8_t*)a->workspace;
+  c->layers.resize(cfg->n_layers);
+
+  auto ev = [&](hipEvent_t* x) { return hipEventCreateWithFlags(x, hipEventDisableTiming); };
+  for (int i = 0; i < 2; ++i) {
+    if (ev(&c->ev_ready[i]) || ev(&c->ev_free[i]) || ev(&c->ev_x0[i]) || ev(&c->ev_bwd_done[i]) ||
+        ev(&c->ev_dx0[i]) || ev(&c->ev_dx0_copied[i]))
+      return MT_E_HIP;
+  }
+  for (int i = 0; i < c->nslab; ++i)
+    if (ev(&c->ev_written[i]) || ev(&c->ev_copied[i])) return MT_E_HIP;
+
+  const size_t T = (size_t)p.T, h = (size_t)cfg->hidden;
+  for (int i = 0; i < c->nslab; ++i)
+    if (hipHostMalloc((void**)&c->hslab[i], p.slab_bytes, hipHostMallocDefault) != hipSuccess)
+      return MT_E_NOMEM;
+  for (int i = 0; i < 2; ++i) {
+    if (hipHostMalloc((void**)&c->x0_stage[i], T * h * 4, hipHostMallocDefault) != hipSuccess ||
+        hipHostMalloc((void**)&c->dx0_stage[i], T * h * 4, hipHostMallocDefault) != hipSuccess ||
+        hipHostMalloc((void**)&c->lab_stage[i], T * 4, hipHostMallocDefault) != hipSuccess)
+      return MT_E_NOMEM;
+  }
+  if (hipHostMalloc((void**)&c->loss_pin, mt_ctx::kLossRing * 4, hipHostMallocDefault) !=
+      hipSuccess)
+    return MT_E_NOMEM;
+
+  // RoPE table: angles in float64, stored fp32 (host-computed once).
+  {
+    const size_t n = (size_t)cfg->seq_len * (cfg->head_dim / 2);
+    std::vector<float> cs(n), sn(n);
+    rope_table(cfg->seq_len, cfg->head_dim, cfg->rope_base, cs.data(), sn.data());
+    if (hipMemcpy(c->ws + p.ws.cos_t, cs.data(), n * 4, hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemcpy(c->ws + p.ws.sin_t, sn.data(), n * 4, hipMemcpyHostToDevice) != hipSuccess)
+      return MT_E_HIP;
+  }
+
+  c->pool.reset(new ThreadPool(cfg->host_threads > 0 ? cfg->host_threads : default_threads()));
+  if (const char* d = getenv("MT_TEST_WORKER_DELAY_US")) c->delay_us = atoi(d);
+  for (int i = c->nslab - 1; i >= 0; --i) c->free_slabs.push_back(i);
+  c->worker = std::thread(worker_main, c.get());
+  *out = c.release();
+  return MT_OK;
+}
+
+extern "C" void mt_destroy(mt_ctx* c) {
+  if (!c) return;
+  (void)hipStreamSynchronize(c->sp);
+  (void)hipStreamSynchronize(c->sc);
+  (void)hipStreamSynchronize(c->so);
+  {
+    std::lock_guard<std::mutex> g(c->mu);
+    c->stop = true;
+  }
+  c->cv.notify_all();
+  if (c->worker.joinable()) c->worker.join();
+  for (auto& b : c->layers)
+    if (b.pinned) (void)hipHostFree(b.pinned);
+  if (c->head.pinned) (void)hipHostFree(c->head.pinned);
+  for (int i = 0; i < c->nslab; ++i)
+    if (c->hslab[i]) (void)hipHostFree(c->hslab[i]);
+  for (int i = 0; i < 2; ++i) {
+    if (c->x0_stage[i]) (void)hipHostFree(c->x0_stage[i]);
+    if (c->dx0_stage[i]) (void)hipHostFree(c->dx0_stage[i]);
+    if (c->lab_stage[i]) (void)hipHostFree(c->lab_stage[i]);
+  }
+  if (c->loss_pin) (void)hipHostFree(c->loss_pin);
+  hipEvent_t* evs[] = {c->ev_ready, c->ev_free, c->ev_x0, c->ev_bwd_done, c->ev_dx0,
+                       c->ev_dx0_copied};
+  for (auto* e : evs)
+    for (int i = 0; i < 2; ++i)
+      if (e[i]) (void)hipEventDestroy(e[i]);
+  for (int i = 0; i < c->nslab; ++i) {
+    if (c->ev_written[i]) (void)hipEventDestroy(c->ev_written[i]);
+    if (c->ev_copied[i]) (void)hipEventDestroy(c->ev_copied[i]);
+  }
+  delete c;
+}
+
+extern "C" const char* mt_last_error(const mt_ctx* c) {
+  if (!c) return "null context";
+  return c->err.c_str();
+}
+
+extern "C" mt_status mt_bind_layer(mt_ctx* c, int32_t group, float* master, float* grad,
+                                   float* adam_m, float* adam_v, int64_t numel) {
+  mt_status r = check_live(c);
+  if (r != MT_OK) return r;
+  if (!master || !grad || !adam_m || !adam_v) return MT_E_ARG;
+  const Plan& p = c->p;
+  int64_t want;
+  mt_ctx::Bind* b;
+  if (group == MT_GROUP_EMBED) {
+    want = p.embed_elems;
+    b = &c->embed;
+  } else if (group == MT_GROUP_HEAD) {
+    want = p.head_elems;
+    b = &c->head;
+  } else if (group >= 0 && group < p.c.n_layers) {
+    want = p.layer_elems;
+    b = &c->layers[group];
+  } else {
+    return MT_E_ARG;
+  }
+  if (numel != want) {
+    c->set_err("group %d: numel %lld, layout needs %lld", group, (long long)numel,
+               (long long)want);
+    return MT_E_ARG;
+  }
+  if (c->state == ST_FWD || c->state == ST_BWD) return MT_E_STATE;
+  b->master = master;
+  b->grad = grad;
+  b->m = adam_m;
+  b->v = adam_v;
+  b->n = numel;
+  if (group != MT_GROUP_EMBED) {
+    if (!b->pinned &&
+        hipHostMalloc((void**)&b->pinned, (size_t)numel * 2, hipHostMallocDefault) != hipSuccess) {
+      b->pinned = nullptr;
+      return MT_E_NOMEM;
+    }
+    cast_bf16(*c->pool, master, b->pinned, numel);
+  }
+  c->buf_unit[0] = c->buf_unit[1] = -1;
+  bool all = c->embed.master && c->head.master;
+  for (auto& x : c->layers) all = all && x.master;
+  if (all && c->state == ST_UNBOUND) c->state = ST_IDLE;
+  return MT_OK;
+}
+
+extern "C" mt_status mt_forward(mt_ctx* c, const int32_t* tokens, const int32_t* labels,
+                                float grad_scale, float* loss_out) {
+  mt_status r = check_live(c);
+  if (r != MT_OK) return r;
+  if (c->state == ST_UNBOUND) return MT_E_UNBOUND;
+  if (c->state == ST_FWD) return MT_E_STATE;
+  if (!tokens || !labels || !(grad_scale == grad_scale)) return MT_E_ARG;
+  const Plan& p = c->p;
+  const int64_t T = p.T, h = p.c.hidden;
+  int64_t n_valid = 0;
+  for (int64_t t = 0; t < T; ++t) {
+    if (tokens[t] < 0 || tokens[t] >= p.c.vocab) return MT_E_ARG;
+    if (labels[t] >= p.c.vocab || labels[t] < -1) return MT_E_ARG;
+    n_valid += labels[t] >= 0;
+  }
+  c->parity = (int)(c->mb & 1);
+  const int par = c->parity;
+  // staging of two micro-batches ago must have reached the device
+  if (c->x0_used[par]) MT_HIP(c, hipEventSynchronize(c->ev_x0[par]));
+  embed_gather(*c->pool, c->embed.master, tokens, T, h, c->x0_stage[par]);
+  memcpy(c->lab_stage[par], labels, (size_t)T * 4);
+  c->tok_cur.assign(tokens, tokens + T);
+  // the device copies of x0 / labels of two micro-batches ago are free once
+  // that micro-batch's backward has finished
+  if (c->bwd_used[par]) MT_HIP(c, hipStreamWaitEvent(c->sp, c->ev_bwd_done[par], 0));
+  MT_HIP(c, hipMemcpyAsync(c->ws + p.ws.x0[par], c->x0_stage[par], (size_t)T * h * 4,
+                           hipMemcpyHostToDevice, c->sp));
+  MT_HIP(c, hipMemcpyAsync(c->ws + p.ws.labels[par], c->lab_stage[par], (size_t)T * 4,
+                           hipMemcpyHostToDevice, c->sp));
+  MT_HIP(c, hipEventRecord(c->ev_x0[par], c->sp));
+  c->x0_used[par] = true;
+  MT_HIP(c, hipStreamWaitEvent(c->sc, c->ev_x0[par], 0));
+
+  build_steps(c);
+  c->head_grad_first = true;
+  c->dy_idx = 0;
+  r = run_until(c, c->split, n_valid, grad_scale);
+  if (r != MT_OK) return r;
+  // loss -> pinned ring, resolved at flush
+  const int slot = c->loss_next;
+  c->loss_next = (c->loss_next + 1) % mt_ctx::kLossRing;
+  MT_HIP(c, hipMemcpyAsync(c->loss_pin + slot, c->ws + p.ws.loss, 4, hipMemcpyDeviceToHost, c->sc));
+  if (loss_out) c->pending_loss.emplace_back(loss_out, slot);
+  c->state = ST_FWD;
+  return MT_OK;
+}
+
+extern "C" mt_status mt_backward(mt_ctx* c, int32_t accumulate_flag) {
+  mt_status r = check_live(c);
+  if (r != MT_OK) return r;
+  if (c->state != ST_FWD) return MT_E_STATE;
+  if (accumulate_flag != 0 && accumulate_flag != 1) return MT_E_ARG;
+  c->accumulate = accumulate_flag;
+  r = run_until(c, c->steps.size(), 0, 0.0f);
+  if (r != MT_OK) return r;
+  c->mb += 1;
+  c->st.microbatches += 1;
+  c->state = ST_BWD;
+  return MT_OK;
+}
+
+extern "C" mt_status mt_flush_grads(mt_ctx* c) {
+  mt_status r = check_live(c);
+  if (r != MT_OK) return r;
+  if (c->state == ST_FWD) return MT_E_STATE;
+  {
+    std::unique_lock<std::mutex> lk(c->mu);
+    c->idle_cv.wait(lk, [&] { return c->outstanding == 0 || c->poisoned.load(); });
+  }
+  if (c->poisoned) return MT_E_ABORTED;
+  MT_HIP(c, hipStreamSynchronize(c->sp));
+  MT_HIP(c, hipStreamSynchronize(c->sc));
+  MT_HIP(c, hipStreamSynchronize(c->so));
+  for (auto& pl : c->pending_loss) *pl.first = c->loss_pin[pl.second];
+  c->pending_loss.clear();
+  if (c->state == ST_BWD) c->state = ST_FLUSHED;
+  return MT_OK;
+}
+
+extern "C" mt_status mt_adamw_step(mt_ctx* c, const mt_adamw_hparams* hp, int64_t step) {
+  mt_status r = check_live(c);
+  if (r != MT_OK) return r;
+  if (!hp || step < 1) return MT_E_ARG;
+  if (c->state != ST_FLUSHED) return MT_E_STATE;
+  const double t0 = now_s();
+  adamw(*c->pool, c->embed.master, c->embed.grad, c->embed.m, c->embed.v, nullptr, c->embed.n,
+        *hp, step);
+  for (auto& b : c->layers) adamw(*c->pool, b.master, b.grad, b.m, b.v, b.pinned, b.n, *hp, step);
+  adamw(*c->pool, c->head.master, c->head.grad, c->head.m, c->head.v, c->head.pinned, c->head.n,
+        *hp, step);
+  c->buf_unit[0] = c->buf_unit[1] = -1;  // working copies changed
+  c->st.adamw_s += now_s() - t0;
+  c->state = ST_IDLE;
+  return MT_OK;
+}
+
+extern "C" mt_status mt_get_stats(mt_ctx* c, mt_stats* out) {
+  if (!c || !out) return MT_E_ARG;
+  std::lock_guard<std::mutex> g(c->mu);
+  *out = c->st;
+  return MT_OK;
+}

@@ -1,0 +1,217 @@
+// Host kernels: bf16 working-copy cast, AdamW, gradient-slab accumulation,
+// embedding gather / scatter-add, RoPE table.
+//
+// The optimizer runs on the CPU where the fp32 master, grad and Adam m/v live,
+// so optimizer state is never moved to the GPU (zhichai.net
+// "MegaTrain：单卡训百亿大模型的突破与实践", design point 1; m.lqnn.cn MegaTrain
+// article, 二: SIMD CPU Adam over ParameterState).  A CPU worker adds each
+// gradient slab into the fp32 host gradient (lqnn 三.3).
+//
+// Arithmetic order is fixed and written out (compiled without FP contraction)
+// so results do not depend on the thread count.
+#include "host_ops.h"
+
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+
+namespace mt {
+
+ThreadPool::ThreadPool(int n) {
+  for (int i = 1; i < n; ++i) workers_.emplace_back([this] { loop(); });
+}
+
+ThreadPool::~ThreadPool() {
+  {
+    std::lock_guard<std::mutex> g(mu_);
+    stop_ = true;
+  }
+  cv_.notify_all();
+  for (auto& t : workers_) t.join();
+}
+
+void ThreadPool::loop() {
+  uint64_t seen = 0;
+  for (;;) {
+    std::unique_lock<std::mutex> lk(mu_);
+    cv_.wait(lk, [&] { return stop_ || gen_ != seen; });
+    if (stop_) return;
+    seen = gen_;
+    for (;;) {
+      if (next_ >= n_) break;
+      int64_t i = next_++;
+      lk.unlock();
+      (*fn_)(i);
+      lk.lock();
+      if (--pending_ == 0) done_cv_.notify_all();
+    }
+  }
+}
+
+void ThreadPool::run(int64_t n, const std::function<void(int64_t)>& fn) {
+  if (n <= 0) return;
+  std::lock_guard<std::mutex> rg(run_mu_);
+  std::unique_lock<std::mutex> lk(mu_);
+  fn_ = &fn;
+  n_ = n;
+  next_ = 0;
+  pending_ = n;
+  ++gen_;
+  cv_.notify_all();
+  for (;;) {
+    if (next_ >= n_) break;
+    int64_t i = next_++;
+    lk.unlock();
+    fn(i);
+    lk.lock();
+    --pending_;
+  }
+  done_cv_.wait(lk, [&] { return pending_ == 0; });
+  fn_ = nullptr;
+  n_ = 0;
+}
+
+int default_threads() {
+  unsigned hc = std::thread::hardware_concurrency();
+  int n = hc ? (int)hc : 4;
+  return std::max(1, std::min(n, 16));
+}
+
+static inline uint16_t rne_bf16(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+static constexpr int64_t kChunk = 1 << 18;  // elements per task
+
+template <class F>
+static void chunked(ThreadPool& pool, int64_t n, F&& f) {
+  const int64_t nt = (n + kChunk - 1) / kChunk;
+  pool.run(nt, [&](int64_t t) {
+    const int64_t b = t * kChunk, e = std::min(n, b + kChunk);
+    f(b, e);
+  });
+}
+
+void cast_bf16(ThreadPool& pool, const float* src, uint16_t* dst, int64_t n) {
+  chunked(pool, n, [&](int64_t b, int64_t e) {
+    for (int64_t i = b; i < e; ++i) dst[i] = rne_bf16(src[i]);
+  });
+}
+
+void adamw(ThreadPool& pool, float* p, const float* g, float* m, float* v, uint16_t* bf, int64_t n,
+           const mt_adamw_hparams& hp, int64_t step) {
+  // Coefficients formed in double, used in fp32 (as a float32 array op would).
+  const float decay = (float)(1.0 - hp.lr * hp.weight_decay);
+  const float b1 = (float)hp.beta1, b2 = (float)hp.beta2;
+  const float c1 = (float)(1.0 - hp.beta1), c2 = (float)(1.0 - hp.beta2);
+  const float bc1 = (float)(1.0 - pow(hp.beta1, (double)step));
+  const float bc2 = (float)(1.0 - pow(hp.beta2, (double)step));
+  const float lr = (float)hp.lr, eps = (float)hp.eps;
+  chunked(pool, n, [&](int64_t b, int64_t e) {
+    for (int64_t i = b; i < e; ++i) {
+      const float gi = g[i];
+      float pi = p[i] * decay;
+      float mi = m[i] * b1;
+      mi = mi + c1 * gi;
+      float vi = v[i] * b2;
+      vi = vi + c2 * (gi * gi);
+      const float mh = mi / bc1;
+      const float vh = vi / bc2;
+      pi = pi - (lr * mh) / (sqrtf(vh) + eps);
+      p[i] = pi;
+      m[i] = mi;
+      v[i] = vi;
+      if (bf) bf[i] = rne_bf16(pi);
+    }
+  });
+}
+
+void accumulate(ThreadPool& pool, float* grad, const float* src, int64_t n, bool add) {
+  chunked(pool, n, [&](int64_t b, int64_t e) {
+    if (add) {
+      for (int64_t i = b; i < e; ++i) grad[i] += src[i];
+    } else {
+      memcpy(grad + b, src + b, (size_t)(e - b) * sizeof(float));
+    }
+  });
+}
+
+void embed_gather(ThreadPool& pool, const float* emb, const int32_t* tok, int64_t T, int64_t h,
+                  float* x0) {
+  const int64_t per = 64;
+  pool.run((T + per - 1) / per, [&](int64_t k) {
+    for (int64_t t = k * per; t < std::min(T, (k + 1) * per); ++t)
+      memcpy(x0 + t * h, emb + (int64_t)tok[t] * h, (size_t)h * sizeof(float));
+  });
+}
+
+void embed_scatter(ThreadPool& pool, float* demb, const int32_t* tok, int64_t T, int64_t h,
+                   const float* dx0) {
+  const int64_t cols = 64;
+  pool.run((h + cols - 1) / cols, [&](int64_t k) {
+    const int64_t c0 = k * cols, c1 = std::min(h, c0 + cols);
+    for (int64_t t = 0; t < T; ++t) {
+      float* dst = demb + (int64_t)tok[t] * h;
+      const float* s = dx0 + t * h;
+      for (int64_t c = c0; c < c1; ++c) dst[c] += s[c];
+    }
+  });
+}
+
+void rope_table(int seq, int d, float base, float* cos_out, float* sin_out) {
+  const int half = d / 2;
+  for (int i = 0; i < half; ++i) {
+    const double theta = pow((double)base, -2.0 * (double)i / (double)d);
+    for (int pos = 0; pos < seq; ++pos) {
+      const double a = (double)pos * theta;
+      cos_out[(int64_t)pos * half + i] = (float)cos(a);
+      sin_out[(int64_t)pos * half + i] = (float)sin(a);
+    }
+  }
+}
+
+}  // namespace mt
+
+// ---------------------------------------------------------------- C ABI
+using namespace mt;
+
+static int nthreads(int32_t t) { return t > 0 ? std::min<int>(t, 256) : default_threads(); }
+
+extern "C" mt_status mt_host_cast_bf16(const float* src, uint16_t* dst, int64_t n,
+                                       int32_t threads) {
+  if (n < 0 || (n > 0 && (!src || !dst))) return MT_E_ARG;
+  ThreadPool pool(nthreads(threads));
+  cast_bf16(pool, src, dst, n);
+  return MT_OK;
+}
+
+extern "C" mt_status mt_host_adamw(float* master, const float* grad, float* m, float* v,
+                                   uint16_t* bf16_out, int64_t n, const mt_adamw_hparams* hp,
+                                   int64_t step, int32_t threads) {
+  if (n < 0 || !hp || step < 1) return MT_E_ARG;
+  if (n > 0 && (!master || !grad || !m || !v)) return MT_E_ARG;
+  ThreadPool pool(nthreads(threads));
+  adamw(pool, master, grad, m, v, bf16_out, n, *hp, step);
+  return MT_OK;
+}
+
+extern "C" mt_status mt_host_accumulate(float* grad, const float* src, int64_t n,
+                                        int32_t accumulate_flag, int32_t threads) {
+  if (n < 0 || (n > 0 && (!grad || !src))) return MT_E_ARG;
+  ThreadPool pool(nthreads(threads));
+  accumulate(pool, grad, src, n, accumulate_flag != 0);
+  return MT_OK;
+}
+
+extern "C" mt_status mt_host_rope_table(int32_t seq_len, int32_t head_dim, float base,
+                                        float* cos_out, float* sin_out) {
+  if (seq_len < 1 || head_dim < 2 || head_dim % 2 || !(base > 0.0f) || !cos_out || !sin_out)
+    return MT_E_ARG;
+  rope_table(seq_len, head_dim, base, cos_out, sin_out);
+  return MT_OK;
+}

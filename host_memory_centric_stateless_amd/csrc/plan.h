@@ -1,0 +1,63 @@
+// Static plan of a configuration: flat layout, streamed units, device regions.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/mt.h"
+
+namespace mt {
+
+constexpr int64_t kAlign = 256;  // elements; every tensor starts at a multiple
+inline int64_t round_up(int64_t n, int64_t a) { return (n + a - 1) / a * a; }
+inline size_t round_bytes(size_t n) { return (n + 255) / 256 * 256; }
+
+struct TensorOff {
+  const char* name;
+  int64_t off, numel;
+  int32_t rows, cols;
+};
+
+// Byte offsets of one window slot (activations of one block kept for its
+// backward).
+struct SlotLayout {
+  size_t x, rstd1, n1, qkv, o, lse, h1, rstd2, n2, gu, m, bytes;
+};
+
+// Byte offsets inside the workspace region.
+struct WorkLayout {
+  size_t xL, xf, rstd_f, logits, dlogits, loss_rows, loss, dxf, dy0, dy1, dyb, dgu, dn, dh1, dh1b,
+      dout, dsum, dqkv, partial, cos_t, sin_t, labels[2], x0[2], bytes;
+};
+
+// Indices into Plan::layer[].
+enum { T_ATTN_NORM = 0, T_WQ, T_WK, T_WV, T_WO, T_MLP_NORM, T_WGATE, T_WUP, T_WDOWN, T_COUNT };
+
+struct Plan {
+  mt_config c;
+  int64_t T;            // tokens per micro-batch
+  int64_t qd, kvd, ldq; // q width, kv width, qkv row width
+  TensorOff layer[T_COUNT];
+  int64_t layer_elems;
+  TensorOff head[2];    // final_norm, w_head
+  int64_t head_elems;
+  int64_t embed_elems;
+  // LM head streamed in vocabulary chunks: rows [row0[c], row0[c+1]).  Chunk c
+  // covers flat elements [chunk_e0[c], chunk_e0[c+1]) of the head group; chunk
+  // 0 starts at element 0 so it also carries final_norm.
+  int n_chunks;
+  std::vector<int64_t> chunk_row0, chunk_e0;
+  int64_t unit_elems;
+  int n_segments;
+  SlotLayout slot;
+  WorkLayout ws;
+  size_t weight_buf_bytes, slab_bytes, window_bytes, ckpt_bytes;
+};
+
+// Fills *p; returns an empty string or the reason the config is unsupported.
+std::string make_plan(const mt_config& c, Plan* p);
+
+}  // namespace mt

@@ -1,0 +1,133 @@
+"""A training session: host state, device arena and one libmt context.
+
+Plumbing only.  Host state (fp32 master / grad / Adam m / v per group) is
+plain numpy memory owned here; the device arena and the three streams are
+torch allocations handed to libmt; every step runs inside libmt.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from typing import Dict, Iterable, Optional, Tuple
+
+import numpy as np
+import torch
+
+from . import (MT_GROUP_EMBED, MT_GROUP_HEAD, make_config, mt_adamw_hparams, mt_adamw_step,
+               mt_backward, mt_bind_layer, mt_create, mt_destroy, mt_device_arena,
+               mt_device_requirements, mt_flush_grads, mt_forward, mt_get_stats, mt_layout)
+
+
+def aligned_zeros(n: int, align: int = 64) -> np.ndarray:
+    """fp32 zeros whose data pointer is `align`-byte aligned."""
+    raw = np.zeros(n + align // 4, dtype=np.float32)
+    off = (-raw.ctypes.data % align) // 4
+    return raw[off:off + n]
+
+
+class Session:
+    def __init__(self, cfg, host_threads: int = 0, device: str = "cuda:0",
+                 ckpt_interval: Optional[int] = None, n_grad_slabs: Optional[int] = None):
+        if ckpt_interval is not None:
+            cfg = cfg.replace(ckpt_interval=ckpt_interval)
+        if n_grad_slabs is not None:
+            cfg = cfg.replace(n_grad_slabs=n_grad_slabs)
+        self.cfg = cfg
+        self.c = make_config(cfg, host_threads)
+        self.req = mt_device_requirements(self.c)
+        self.groups = [MT_GROUP_EMBED] + list(range(cfg.n_layers)) + [MT_GROUP_HEAD]
+        self.layout: Dict[int, Tuple[list, int]] = {g: mt_layout(self.c, g) for g in self.groups}
+        self.master, self.grad, self.m, self.v = {}, {}, {}, {}
+        for g in self.groups:
+            n = self.layout[g][1]
+            self.master[g] = aligned_zeros(n)
+            self.grad[g] = aligned_zeros(n)
+            self.m[g] = aligned_zeros(n)
+            self.v[g] = aligned_zeros(n)
+
+        self.device = torch.device(device)
+        r = self.req
+
+        def dev(nbytes):
+            return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=self.device)
+
+        self.wbuf = [dev(r.weight_buf) for _ in range(2)]
+        self.slabs = [dev(r.grad_slab) for _ in range(cfg.n_grad_slabs)]
+        self.window = dev(r.window)
+        self.ckpt = dev(r.checkpoints)
+        self.ws = dev(r.workspace)
+        self.streams = [torch.cuda.Stream(device=self.device) for _ in range(3)]
+        a = mt_device_arena()
+        a.weight_buf[0] = self.wbuf[0].data_ptr()
+        a.weight_buf[1] = self.wbuf[1].data_ptr()
+        for i, s in enumerate(self.slabs):
+            a.grad_slab[i] = s.data_ptr()
+        a.window = self.window.data_ptr()
+        a.checkpoints = self.ckpt.data_ptr()
+        a.workspace = self.ws.data_ptr()
+        a.stream_prefetch = self.streams[0].cuda_stream
+        a.stream_compute = self.streams[1].cuda_stream
+        a.stream_offload = self.streams[2].cuda_stream
+        a.weight_buf_bytes = self.wbuf[0].numel()
+        a.grad_slab_bytes = self.slabs[0].numel()
+        a.window_bytes = self.window.numel()
+        a.checkpoints_bytes = self.ckpt.numel()
+        a.workspace_bytes = self.ws.numel()
+        self.arena = a
+        with torch.cuda.device(self.device):
+            self.ctx = mt_create(self.c, a)
+        self.bound = False
+
+    # ------------------------------------------------------------ weights
+    def views(self, group: int, which: str = "master") -> Dict[str, np.ndarray]:
+        flat = getattr(self, which)[group]
+        return {name: flat[off:off + n].reshape(rows, cols) if rows > 1 else flat[off:off + n]
+                for name, off, n, rows, cols in self.layout[group][0]}
+
+    def load_weights(self, stream: Iterable) -> None:
+        """Copy (group, name, array) tuples into the fp32 masters, then bind."""
+        vs = {g: self.views(g) for g in self.groups}
+        for g, name, arr in stream:
+            vs[g][name][...] = np.asarray(arr, dtype=np.float32).reshape(vs[g][name].shape)
+        self.bind()
+
+    def bind(self) -> None:
+        with torch.cuda.device(self.device):
+            for g in self.groups:
+                mt_bind_layer(self.ctx, g, self.master[g], self.grad[g], self.m[g], self.v[g])
+        self.bound = True
+
+    # --------------------------------------------------------------- steps
+    def forward_backward(self, tokens: np.ndarray, labels: np.ndarray) -> float:
+        """All micro-batches of one step (tokens/labels [acc, b, s]); grads
+        land in self.grad.  Returns the mean micro-batch loss."""
+        acc = tokens.shape[0]
+        losses = np.zeros(acc, dtype=np.float32)
+        with torch.cuda.device(self.device):
+            for mb in range(acc):
+                out = losses[mb:mb + 1]
+                mt_forward(self.ctx, tokens[mb].reshape(-1), labels[mb].reshape(-1), 1.0 / acc, out)
+                mt_backward(self.ctx, 1 if mb > 0 else 0)
+            mt_flush_grads(self.ctx)
+        self._losses = losses  # keep the output buffer alive until flush wrote it
+        return float(losses.mean())
+
+    def step(self, tokens: np.ndarray, labels: np.ndarray, step: int, lr: Optional[float] = None,
+             weight_decay: float = 0.01) -> float:
+        loss = self.forward_backward(tokens, labels)
+        hp = mt_adamw_hparams(lr if lr is not None else self.cfg.lr, 0.9, 0.999, 1e-8, weight_decay)
+        mt_adamw_step(self.ctx, hp, step)
+        return loss
+
+    def stats(self) -> dict:
+        return mt_get_stats(self.ctx)
+
+    def close(self) -> None:
+        if getattr(self, "ctx", None):
+            mt_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,220 @@
+/*
+ * mt.h -- C ABI of libmt: host-memory-centric, layer-streamed training of a
+ * Llama-style decoder on one MI355X (gfx950).
+ *
+ * The method (MegaTrain, as described on the pages cited below):
+ *   - fp32 master weights, gradients and Adam m/v live in host memory; the GPU
+ *     is a transient compute engine (zhichai.net "MegaTrain：单卡训百亿大模型的突破与实践",
+ *     design point 1; m.lqnn.cn MegaTrain article, section 二 "ParameterState").
+ *   - layers are streamed in one at a time into a ping-pong pair of flat
+ *     device buffers from pinned, pre-flattened host copies (zhichai design
+ *     point 2; lqnn 三.1 "gpu_flat_buffers" / "layer_pinned_flats").
+ *   - prefetch, compute and gradient offload run on three streams ordered by
+ *     events ("no compute before the data is there, no write before the
+ *     buffer is free") (zhichai design point 4; lqnn 三.2).
+ *   - each layer's gradients land in one of a pool of flat gradient slabs
+ *     (default 12) and a CPU thread adds them into the fp32 host gradient
+ *     (lqnn 三.3).
+ *   - an activation checkpoint every K layers; backward recomputes each
+ *     K-layer segment (zhichai design point 3; lqnn 三.4, default K = 4).
+ *   - a stateless layer template: the kernels of one block bound at run
+ *     time to whatever flat buffer holds the layer (zhichai design point 4;
+ *     blog.travelaiplan.net "單卡也能練 100B+：MegaTrain 實戰", 核心功能 3).
+ *   - the optimizer step runs on the CPU over the host state (lqnn 二).
+ *
+ * Conventions
+ *   - Every call returns mt_status; no C++ exception crosses the ABI.
+ *   - Arguments are validated before anything is enqueued on the GPU.
+ *   - The first HIP error poisons the context: later calls return
+ *     MT_E_ABORTED; mt_last_error() holds the message.
+ *   - A context is used by one caller thread at a time.
+ *   - bf16 values are passed as uint16_t bit patterns.
+ */
+#ifndef MT_H
+#define MT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MT_OK = 0,
+  MT_E_ARG = -1,      /* invalid argument (null pointer, wrong size, bad value)      */
+  MT_E_STATE = -2,    /* call out of order (see the call order below)                */
+  MT_E_HIP = -3,      /* a HIP runtime call failed                                   */
+  MT_E_NOMEM = -4,    /* host or pinned allocation failed, or an arena is too small  */
+  MT_E_UNBOUND = -5,  /* forward called before every group was bound                 */
+  MT_E_ABORTED = -6   /* the context was poisoned by an earlier HIP error            */
+} mt_status;
+
+/* Parameter groups: 0..n_layers-1 are decoder blocks. */
+enum { MT_GROUP_EMBED = -1, MT_GROUP_HEAD = -2 };
+
+typedef struct mt_config {
+  int32_t n_layers;       /* decoder blocks                                     */
+  int32_t hidden;         /* h, multiple of 256                                 */
+  int32_t n_heads;        /* query heads                                        */
+  int32_t n_kv_heads;     /* key/value heads, divides n_heads                   */
+  int32_t head_dim;       /* d: 64 or 128                                       */
+  int32_t ffn;            /* SwiGLU width F, multiple of 16                     */
+  int32_t vocab;          /* V, multiple of 256                                 */
+  float rms_eps;          /* RMSNorm epsilon (inside the square root)           */
+  float rope_base;        /* RoPE base (10000)                                  */
+  int32_t micro_batch;    /* b sequences per micro-batch                        */
+  int32_t seq_len;        /* s tokens per sequence, multiple of 128             */
+  int32_t ckpt_interval;  /* K: checkpoint every K layers (>= 1)                */
+  int32_t n_grad_slabs;   /* gradient slab pool size (1..64), 12 by default     */
+  int32_t host_threads;   /* CPU threads for accumulate / AdamW (0 = automatic) */
+} mt_config;
+
+/* One tensor of a group's flat layout. */
+typedef struct mt_tensor_desc {
+  char name[16];
+  int64_t offset;         /* elements from the start of the group's flat array  */
+  int64_t numel;
+  int32_t rows, cols;     /* matrices are row-major [out, in]; gains are [1, h] */
+} mt_tensor_desc;
+
+/* Device and host memory the library needs for a configuration. */
+typedef struct mt_device_req {
+  size_t weight_buf;      /* bytes of EACH of the two bf16 ping-pong buffers    */
+  size_t grad_slab;       /* bytes of EACH fp32 gradient slab                   */
+  size_t window;          /* activations of one K-layer recompute window        */
+  size_t checkpoints;     /* ceil(L/K) fp32 [T, h] layer inputs                 */
+  size_t workspace;       /* head logits, gradients in flight, RoPE table, ...  */
+  size_t device_total;    /* 2*weight_buf + n_slabs*grad_slab + the rest        */
+  size_t pinned_host;     /* pinned host bytes the library allocates itself     */
+  size_t host_state;      /* caller-owned fp32 master+grad+m+v: 16 B/parameter  */
+  int64_t unit_elems;     /* elements of the largest streamed unit              */
+  int32_t head_chunks;    /* vocabulary chunks the LM head is streamed in       */
+  int32_t reserved;
+} mt_device_req;
+
+/* Device memory and streams, owned by the caller (PyTorch allocates them).
+ * Each pointer must be 256-byte aligned and at least the size given by
+ * mt_device_requirements.  Streams are hipStream_t handles at default
+ * priority; the three must be distinct. */
+typedef struct mt_device_arena {
+  void* weight_buf[2];
+  void* grad_slab[64];    /* first n_grad_slabs entries used                    */
+  void* window;
+  void* checkpoints;
+  void* workspace;
+  void* stream_prefetch;  /* host -> device weight copies                       */
+  void* stream_compute;   /* kernels                                            */
+  void* stream_offload;   /* device -> host gradient copies                     */
+  /* bytes actually allocated for each region (checked against the needs) */
+  size_t weight_buf_bytes, grad_slab_bytes, window_bytes, checkpoints_bytes, workspace_bytes;
+} mt_device_arena;
+
+/* AdamW hyper-parameters (double so that derived coefficients such as
+ * 1 - beta1^t are formed from the exact values the caller holds). */
+typedef struct mt_adamw_hparams {
+  double lr, beta1, beta2, eps, weight_decay;
+} mt_adamw_hparams;
+
+/* Per-context counters, cumulative since mt_create. */
+typedef struct mt_stats {
+  int64_t h2d_bytes;          /* weight bytes copied host -> device            */
+  int64_t d2h_bytes;          /* gradient bytes copied device -> host          */
+  int64_t weight_loads;       /* streamed units loaded                         */
+  int64_t layer_forwards;     /* block forwards incl. recompute                */
+  int64_t layer_backwards;
+  int64_t slab_waits;         /* times the enqueue thread waited for a slab    */
+  double slab_wait_s;         /* host seconds spent waiting for slabs          */
+  double accumulate_s;        /* worker seconds adding slabs into host grads   */
+  double adamw_s;             /* seconds in mt_adamw_step                      */
+  int64_t microbatches;
+} mt_stats;
+
+typedef struct mt_ctx mt_ctx;
+
+/* Flat layout of one group (pure, no GPU).  Tensors start at multiples of 256
+ * elements; order: attn_norm, wq, wk, wv, wo, mlp_norm, w_gate, w_up, w_down
+ * for blocks; final_norm, w_head for MT_GROUP_HEAD; emb for MT_GROUP_EMBED
+ * (lqnn 三.1: pre-flattened per-layer weights).  Writes up to cap descriptors
+ * into out (out may be NULL when cap == 0), the count into *n_out and the
+ * flat length in elements into *flat_numel.  MT_E_ARG for a bad config/group. */
+mt_status mt_layout(const mt_config* cfg, int32_t group, mt_tensor_desc* out, int32_t cap,
+                    int32_t* n_out, int64_t* flat_numel);
+
+/* Memory needed for cfg (pure, no GPU).  MT_E_ARG for an unsupported config. */
+mt_status mt_device_requirements(const mt_config* cfg, mt_device_req* out);
+
+/* Create a context on the current HIP device.  The arena must satisfy
+ * mt_device_requirements(cfg) (MT_E_NOMEM if a region is smaller); it is
+ * borrowed, not freed, by the library.  Allocates pinned host slabs and
+ * staging buffers, events and the worker threads.  The library allocates no
+ * device memory. */
+mt_status mt_create(const mt_config* cfg, const mt_device_arena* arena, mt_ctx** out);
+
+/* Bind the host state of one group: fp32 master, grad, adam_m, adam_v flat
+ * arrays of exactly mt_layout's flat_numel elements (64-byte aligned,
+ * pageable memory is fine).  The caller keeps ownership; the arrays must
+ * outlive the context.  For blocks and the head the library makes a pinned
+ * bf16 working copy (round-to-nearest-even of master) that is what streams
+ * to the GPU.  Rebinding a group replaces its pointers and refreshes the copy.
+ * The caller must not write master except through mt_adamw_step, and must not
+ * touch grad between mt_forward and the return of mt_flush_grads. */
+mt_status mt_bind_layer(mt_ctx* ctx, int32_t group, float* master, float* grad, float* adam_m,
+                        float* adam_v, int64_t numel);
+
+/* Enqueue the forward pass of one micro-batch: embedding gather on the host,
+ * streamed block forwards with a checkpoint every K layers, the LM head in
+ * vocabulary chunks, cross-entropy and its gradient scaled by
+ * grad_scale / (labelled tokens).  tokens and labels are host int32 arrays of
+ * micro_batch*seq_len entries (sequence-major); label -1 is ignored; tokens
+ * must be in [0, vocab).  The micro-batch mean loss is written to *loss_out
+ * when mt_flush_grads returns (loss_out may be NULL).  Returns without waiting
+ * for the GPU. */
+mt_status mt_forward(mt_ctx* ctx, const int32_t* tokens, const int32_t* labels, float grad_scale,
+                     float* loss_out);
+
+/* Enqueue the backward pass of the last forward: LM head gradients, then per
+ * segment (last to first) recompute from the checkpoint and block backwards.
+ * Each unit's fp32 gradient is written into a free slab, copied to pinned host
+ * memory on the offload stream and added by the worker into the host grad:
+ * accumulate = 0 sets grad = g, accumulate = 1 adds grad += g.  The embedding
+ * gradient is scattered into the embedding grad on the host.  May block while
+ * every slab is in flight. */
+mt_status mt_backward(mt_ctx* ctx, int32_t accumulate);
+
+/* Wait until every gradient of every enqueued backward is in the host grads
+ * and all streams are idle; writes pending losses. */
+mt_status mt_flush_grads(mt_ctx* ctx);
+
+/* AdamW on every bound group (decoupled weight decay, bias correction, step is
+ * 1-based), then refresh the pinned bf16 working copies.  Allowed only after
+ * mt_flush_grads. */
+mt_status mt_adamw_step(mt_ctx* ctx, const mt_adamw_hparams* hp, int64_t step);
+
+mt_status mt_get_stats(mt_ctx* ctx, mt_stats* out);
+const char* mt_last_error(const mt_ctx* ctx);
+void mt_destroy(mt_ctx* ctx);
+
+/* ---- host kernels, usable without a GPU (the same code the context runs) ---- */
+
+/* fp32 -> bf16 round-to-nearest-even (NaN stays NaN), n elements. */
+mt_status mt_host_cast_bf16(const float* src, uint16_t* dst, int64_t n, int32_t threads);
+
+/* One AdamW step over n elements in place; bf16_out (may be NULL) receives
+ * RNE(master) after the update. */
+mt_status mt_host_adamw(float* master, const float* grad, float* m, float* v, uint16_t* bf16_out,
+                        int64_t n, const mt_adamw_hparams* hp, int64_t step, int32_t threads);
+
+/* grad = src (accumulate = 0) or grad += src (accumulate = 1). */
+mt_status mt_host_accumulate(float* grad, const float* src, int64_t n, int32_t accumulate,
+                             int32_t threads);
+
+/* RoPE cos/sin tables [seq_len, head_dim/2] from float64 angles
+ * pos * base^(-2i/head_dim), rounded to fp32. */
+mt_status mt_host_rope_table(int32_t seq_len, int32_t head_dim, float base, float* cos_out,
+                             float* sin_out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MT_H */

@@ -1,0 +1,191 @@
+"""libmt on the CPU: exported symbols, layout and memory accounting, host
+kernels (bf16 cast, AdamW, accumulate, RoPE table) against the oracle and
+torch, and argument errors that are rejected before any HIP call."""
+import ctypes as C
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import host_memory_centric_stateless_amd as mt
+from oracle import layout as OL
+from oracle import model as OM
+from oracle.adamw import AdamWHparams, adamw_step
+from synth_inputs import PRESETS
+
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include")
+
+
+def _declared():
+    names = set()
+    for f in os.listdir(INCLUDE):
+        if f.endswith(".h"):
+            src = open(os.path.join(INCLUDE, f)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names |= set(re.findall(r"\b(mtk?_[a-z0-9_]+)\s*\(", src))
+    return names
+
+
+def test_every_declared_symbol_is_exported():
+    declared = _declared()
+    assert len(declared) >= 20
+    for name in declared:
+        assert hasattr(mt.lib(), name), name
+    assert declared == set(mt.EXPORTED)
+
+
+@pytest.mark.parametrize("name", ["C1", "C2", "C3", "C4", "C5"])
+def test_layout_matches_oracle(name):
+    cfg = PRESETS[name]
+    c = mt.make_config(cfg)
+    for g in [OL.EMBED, 0, cfg.n_layers - 1, OL.HEAD]:
+        descs, total = mt.mt_layout(c, g)
+        ent, ototal = OL.group_layout(cfg, g)
+        assert total == ototal
+        assert [(d[0], d[1], d[2]) for d in descs] == [(e[0], e[2], e[3]) for e in ent]
+
+
+def test_layout_rejects_bad_group_and_config():
+    c = mt.make_config(PRESETS["C1"])
+    with pytest.raises(mt.MtError):
+        mt.mt_layout(c, 2)
+    bad = mt.make_config(PRESETS["C1"].replace(hidden=100))
+    with pytest.raises(mt.MtError):
+        mt.mt_layout(bad, 0)
+    with pytest.raises(mt.MtError):
+        mt.mt_device_requirements(mt.make_config(PRESETS["C1"].replace(head_dim=96)))
+
+
+@pytest.mark.parametrize("name", ["C1", "C2", "C3", "C4", "C5"])
+def test_device_requirements(name):
+    cfg = PRESETS[name]
+    r = mt.mt_device_requirements(mt.make_config(cfg))
+    assert r.host_state == 16 * OL.param_count(cfg)
+    P = OL.group_layout(cfg, 0)[1]
+    assert r.unit_elems >= P
+    assert r.weight_buf == -(-r.unit_elems * 2 // 256) * 256
+    assert r.grad_slab == -(-r.unit_elems * 4 // 256) * 256
+    # the whole vocabulary is covered by head chunks that each fit one unit
+    H = OL.group_layout(cfg, OL.HEAD)[1]
+    assert r.head_chunks * r.unit_elems >= H
+    assert r.device_total == (2 * r.weight_buf + cfg.n_grad_slabs * r.grad_slab + r.window
+                              + r.checkpoints + r.workspace)
+    # device memory does not grow with depth (only the checkpoint list does)
+    r2 = mt.mt_device_requirements(mt.make_config(cfg.replace(n_layers=2 * cfg.n_layers)))
+    assert r2.window == r.window and r2.weight_buf == r.weight_buf
+    assert r2.workspace == r.workspace
+
+
+def test_requirements_published_shapes():
+    r3 = mt.mt_device_requirements(mt.make_config(PRESETS["C3"]))
+    r4 = mt.mt_device_requirements(mt.make_config(PRESETS["C4"]))
+    assert (r3.unit_elems, r3.head_chunks) == (202_383_360, 1)
+    assert (r4.unit_elems, r4.head_chunks) == (275_261_440, 3)
+    assert r4.device_total < 288e9 and r3.device_total < 288e9
+
+
+def test_cast_bf16_matches_torch_including_ties_and_specials():
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal(100_003).astype(np.float32) * 10
+    specials = np.array([0.0, -0.0, np.inf, -np.inf, 1e-40, -1e-42, 3.0e38, -3.3e38,
+                         np.finfo(np.float32).max, np.finfo(np.float32).tiny], np.float32)
+    ties = (np.arange(1, 2001, dtype=np.uint32) << 16 | 0x8000).view(np.float32)
+    x = np.concatenate([x, specials, ties, -ties])
+    out = np.empty(x.size, np.uint16)
+    mt.mt_host_cast_bf16(x, out, threads=3)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(out, ref)
+    nan = np.array([np.nan, -np.nan], np.float32)
+    o2 = np.empty(2, np.uint16)
+    mt.mt_host_cast_bf16(nan, o2)
+    assert np.all((o2 & 0x7F80) == 0x7F80) and np.all(o2 & 0x7F)
+
+
+def test_host_adamw_matches_oracle_fp32_bitwise_and_fp64():
+    rng = np.random.default_rng(1)
+    n = 300_001
+    p0 = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    grads = [(rng.standard_normal(n) * 1e-3).astype(np.float32) for _ in range(3)]
+    grads[1][::7] = 0.0
+    hp = mt.mt_adamw_hparams(1e-3, 0.9, 0.999, 1e-8, 0.01)
+    ohp = AdamWHparams(lr=1e-3)
+    p, m, v = p0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    bf = np.empty(n, np.uint16)
+    q, qm, qv = p0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    d, dm, dv = p0.astype(np.float64), np.zeros(n), np.zeros(n)
+    for t, g in enumerate(grads, start=1):
+        mt.mt_host_adamw(p, g, m, v, bf, hp, t, threads=4)
+        adamw_step(q, g, qm, qv, t, ohp)
+        adamw_step(d, g.astype(np.float64), dm, dv, t, ohp)
+    np.testing.assert_array_equal(p, q)          # same fp32 arithmetic, same order
+    np.testing.assert_array_equal(m, qm)
+    np.testing.assert_array_equal(v, qv)
+    assert np.max(np.abs(p - d) / np.maximum(np.abs(d), 1e-3)) < 1e-6
+    ref = torch.from_numpy(p).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(bf, ref)
+
+
+def test_host_accumulate():
+    rng = np.random.default_rng(2)
+    a = rng.standard_normal(1_000_003).astype(np.float32)
+    b = rng.standard_normal(a.size).astype(np.float32)
+    g = np.zeros_like(a)
+    mt.mt_host_accumulate(g, a, 0, threads=5)
+    np.testing.assert_array_equal(g, a)
+    mt.mt_host_accumulate(g, b, 1, threads=5)
+    np.testing.assert_array_equal(g, a + b)
+
+
+@pytest.mark.parametrize("s,d", [(128, 64), (4096, 128), (131072, 128)])
+def test_rope_table_matches_oracle(s, d):
+    c, sn = mt.mt_host_rope_table(s, d, 10000.0)
+    oc, osn = OM.rope_tables(s, d, 10000.0, np.float32)
+    # both form the angle in float64 and round once to fp32; libm pow and
+    # numpy power may differ by a few float64 ulps in theta, which positions up
+    # to 131072 amplify, so bound the absolute error by one fp32 ulp at 1.0
+    for a, b in ((c, oc), (sn, osn)):
+        assert np.max(np.abs(a - b)) <= 2.0 ** -23
+        assert np.mean(a == b) > 0.9999
+
+
+def test_create_rejects_bad_arena_before_any_gpu_call():
+    cfg = mt.make_config(PRESETS["C1"])
+    req = mt.mt_device_requirements(cfg)
+    a = mt.mt_device_arena()
+    with pytest.raises(mt.MtError) as e:       # null pointers
+        mt.mt_create(cfg, a)
+    assert e.value.status == mt.MT_E_ARG
+    base = 1 << 40
+    a.weight_buf[0], a.weight_buf[1] = base, base + 2 ** 30
+    for i in range(PRESETS["C1"].n_grad_slabs):
+        a.grad_slab[i] = base + (4 + i) * 2 ** 30
+    a.window, a.checkpoints, a.workspace = base + 2 ** 35, base + 2 ** 36, base + 2 ** 37
+    a.stream_prefetch, a.stream_compute, a.stream_offload = 1, 2, 2
+    with pytest.raises(mt.MtError) as e:       # two streams alias
+        mt.mt_create(cfg, a)
+    assert e.value.status == mt.MT_E_ARG
+    a.stream_offload = 3
+    a.weight_buf_bytes = req.weight_buf - 256  # arena too small
+    a.grad_slab_bytes, a.window_bytes = req.grad_slab, req.window
+    a.checkpoints_bytes, a.workspace_bytes = req.checkpoints, req.workspace
+    with pytest.raises(mt.MtError) as e:
+        mt.mt_create(cfg, a)
+    assert e.value.status == mt.MT_E_NOMEM
+
+
+def test_kernel_entry_points_reject_bad_shapes():
+    with pytest.raises(mt.MtError):
+        mt.mtk_gemm(mt.MT_GEMM_NT, mt.MT_EPI_F32, 12, 16, 16, 1 << 30, 16, 1 << 30, 16, 1 << 30,
+                    16, stream=0)              # M not a multiple of 8
+    with pytest.raises(mt.MtError):
+        mt.mtk_gemm(mt.MT_GEMM_NN, mt.MT_EPI_SWIGLU, 16, 16, 16, 1 << 30, 16, 1 << 30, 16,
+                    1 << 30, 32, gu=1 << 30, ldgu=32, ffn=16, stream=0)  # SWIGLU needs NT
+    with pytest.raises(mt.MtError):
+        mt.mtk_attention_fwd(1 << 30, 1 << 30, 1 << 30, 1, 100, 4, 4, 64, stream=0)
+    with pytest.raises(mt.MtError):
+        mt.mtk_attention_fwd(1 << 30, 1 << 30, 1 << 30, 1, 128, 4, 3, 64, stream=0)
+    with pytest.raises(mt.MtError):
+        mt.mtk_rmsnorm_fwd(1 << 30, 1 << 30, 1 << 30, 1 << 30, 4, 6, 1e-5, stream=0)
