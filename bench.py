@@ -1,0 +1,241 @@
+"""Throughput of host-streamed training steps on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 3] [--warmup 1] [--config C3] [--no-cpu-baseline]
+
+One step = every micro-batch's streamed forward and backward (weights copied
+layer by layer from pinned host memory, checkpoint recompute, gradient slabs
+drained into host fp32 grads), the flush, and the host AdamW -- the whole
+path.  Inputs are seeded synthetic token ids; weights are N(0, 0.02) from a
+seed.  Prints one JSON line.
+
+`roofline` reports the dominant kernel (the SwiGLU gate/up GEMM of the block)
+timed live with HIP events on the stream it runs on; `cpu_baseline` times the
+CPU oracle on one decoder layer of the same shape.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+KERNEL_COPY_WGS = (32, 128, 512)
+
+
+def model_flops_per_token(cfg) -> float:
+    """6 * (block matrices + LM head) + causal attention (fwd + bwd = 3x fwd);
+    recompute is not counted."""
+    h, F, V = cfg.hidden, cfg.ffn, cfg.vocab
+    qd, kvd = cfg.n_heads * cfg.head_dim, cfg.n_kv_heads * cfg.head_dim
+    p_mm = h * qd + 2 * h * kvd + qd * h + 3 * h * F
+    return 6.0 * (cfg.n_layers * p_mm + h * V) + 6.0 * cfg.n_layers * cfg.seq_len * qd
+
+
+def hardware_flops_per_token(cfg) -> float:
+    """Adds the recompute forwards (every layer outside the last segment) and
+    the flash-backward recompute of the scores (2.5x the forward attention)."""
+    h, F = cfg.hidden, cfg.ffn
+    qd, kvd = cfg.n_heads * cfg.head_dim, cfg.n_kv_heads * cfg.head_dim
+    p_mm = h * qd + 2 * h * kvd + qd * h + 3 * h * F
+    K = cfg.ckpt_interval
+    nseg = -(-cfg.n_layers // K)
+    recomputed = cfg.n_layers - (cfg.n_layers - (nseg - 1) * K)
+    attn_fwd = 2.0 * cfg.seq_len * qd
+    return model_flops_per_token(cfg) + recomputed * (2.0 * p_mm + attn_fwd) + \
+        cfg.n_layers * 0.5 * attn_fwd
+
+
+def time_dominant_gemm(sess, reps: int = 20):
+    """SwiGLU gate/up GEMM of one block (T x 2F x h, bf16 MFMA), timed with
+    HIP events on the library's compute stream."""
+    import torch
+    import host_memory_centric_stateless_amd as mt
+    cfg = sess.cfg
+    T, h, F = cfg.micro_batch * cfg.seq_len, cfg.hidden, cfg.ffn
+    dev = sess.device
+    stream = sess.streams[1]
+    g = torch.Generator(device="cpu").manual_seed(5)
+    A = torch.randn(T, h, generator=g).to(torch.bfloat16).to(dev)
+    B = (torch.randn(2 * F, h, generator=g) * 0.02).to(torch.bfloat16).to(dev)
+    m = torch.empty(T, F, dtype=torch.bfloat16, device=dev)
+    gu = torch.empty(T, 2 * F, dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    args = (mt.MT_GEMM_NT, mt.MT_EPI_SWIGLU, T, F, h, A, h, B, h, m, F)
+    kw = dict(gu=gu, ldgu=2 * F, ffn=F, stream=stream)
+    for _ in range(3):
+        mt.mtk_gemm(*args, **kw)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        mt.mtk_gemm(*args, **kw)
+    e1.record(stream)
+    e1.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flops = 2.0 * T * (2 * F) * h
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {"kernel": "gemm_kernel<NT,SWIGLU> gate/up", "shape": [T, 2 * F, h],
+            "ms": ms, "tflops": tflops, "flops": flops}
+
+
+def link_roofline(nbytes: int, reps: int = 4):
+    """Pinned host <-> device copy rates at layer-sized transfers: H2D alone,
+    D2H alone, and both directions at once on two streams (GB/s)."""
+    import torch
+    dev = torch.device("cuda:0")
+    h1 = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    h2 = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    d1 = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    d2 = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+
+    def timed(fn_list):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True), s)
+              for _, s in fn_list]
+        torch.cuda.synchronize()
+        for (e0, e1, s), (fn, _) in zip(ev, fn_list):
+            with torch.cuda.stream(s):
+                e0.record(s)
+                for _ in range(reps):
+                    fn()
+                e1.record(s)
+        torch.cuda.synchronize()
+        return [nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9 for e0, e1, _ in ev]
+
+    h2d = lambda: d1.copy_(h1, non_blocking=True)
+    d2h = lambda: h2.copy_(d2, non_blocking=True)
+    timed([(h2d, sa)])
+    out = {"bytes_per_copy": nbytes, "h2d_GBps": timed([(h2d, sa)])[0],
+           "d2h_GBps": timed([(d2h, sb)])[0]}
+    a, b = timed([(h2d, sa), (d2h, sb)])
+    out["duplex_h2d_GBps"], out["duplex_d2h_GBps"] = a, b
+    # device -> host by a copy kernel writing host-mapped memory, alone and
+    # while the copy engine runs host -> device
+    import host_memory_centric_stateless_amd as mt
+    for wgs in KERNEL_COPY_WGS:
+        kd2h = lambda: mt.mtk_copy(h2, d2, nbytes, wgs, stream=sb)
+        out[f"kernel{wgs}_d2h_GBps"] = timed([(kd2h, sb)])[0]
+        a, b = timed([(h2d, sa), (kd2h, sb)])
+        out[f"kernel{wgs}_duplex_h2d_GBps"], out[f"kernel{wgs}_duplex_d2h_GBps"] = a, b
+    return out
+
+
+def cpu_baseline(cfg, budget_s: float = 30.0):
+    """The oracle (fp32 NumPy) on one decoder layer at the same shape:
+    forward + recompute forward + backward, on this host's cores."""
+    from oracle import model as OM
+    from synth_inputs import make_batch, tensor_specs
+    rng = np.random.default_rng(0)
+    T = cfg.micro_batch * cfg.seq_len
+    W = {}
+    for name, shape, kind in tensor_specs(cfg, 0):
+        W[name] = (np.ones(shape, np.float32) if kind == "gain"
+                   else (rng.standard_normal(shape, dtype=np.float32) * np.float32(0.02)))
+    x = rng.standard_normal((T, cfg.hidden), dtype=np.float32)
+    cos, sin = OM.rope_tables(cfg.seq_len, cfg.head_dim, cfg.rope_base, np.float32)
+    t0 = time.perf_counter()
+    y, _ = OM.block_forward(W, x, cfg, cos, sin, cfg.micro_batch)
+    _, cache = OM.block_forward(W, x, cfg, cos, sin, cfg.micro_batch)
+    OM.block_backward(W, cache, np.ones_like(y) * np.float32(1e-3), cfg, cos, sin, cfg.micro_batch)
+    dt = time.perf_counter() - t0
+    per_layer_model = (model_flops_per_token(cfg.replace(n_layers=1, vocab=0)))
+    tflops = per_layer_model * T / dt / 1e12
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": tflops, "unit": "model TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"1 decoder layer ({cfg.name}) forward + recompute + backward on "
+                      f"{T} tokens, fp32 NumPy, {dt:.1f} s; tokens/s equivalent "
+                      f"{T / dt / cfg.n_layers:.1f}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--config", default="C3")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--host-threads", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the method's multi-GPU "
+              "data parallelism is not part of this build", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from host_memory_centric_stateless_amd import Session
+    from synth_inputs import PRESETS, make_batch, weight_stream
+
+    cfg = PRESETS[args.config]
+    t0 = time.perf_counter()
+    sess = Session(cfg, host_threads=args.host_threads)
+    sess.load_weights(weight_stream(cfg, 0))
+    print(f"[bench] {cfg.name}: init {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+
+    tokens_per_step = cfg.grad_accum * cfg.micro_batch * cfg.seq_len
+    losses = []
+    for w in range(args.warmup):
+        tok, lab = make_batch(cfg, 1 + w)
+        losses.append(sess.step(tok, lab, 1 + w))
+        print(f"[bench] warmup {w} loss {losses[-1]:.4f}", file=sys.stderr, flush=True)
+    batches = [make_batch(cfg, 1 + args.warmup + k) for k in range(args.steps)]
+    s0 = sess.stats()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(args.steps):
+        tok, lab = batches[k]
+        losses.append(sess.step(tok, lab, 1 + args.warmup + k))
+        print(f"[bench] step {k} loss {losses[-1]:.4f} t={time.perf_counter() - t_start:.2f}s",
+              file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    s1 = sess.stats()
+
+    ms_per_step = 1e3 * elapsed / args.steps
+    tok_s = tokens_per_step * args.steps / elapsed
+    model_tflops = model_flops_per_token(cfg) * tok_s / 1e12
+    hw_tflops = hardware_flops_per_token(cfg) * tok_s / 1e12
+    h2d = (s1["h2d_bytes"] - s0["h2d_bytes"]) / elapsed / 1e9
+    d2h = (s1["d2h_bytes"] - s0["d2h_bytes"]) / elapsed / 1e9
+    adamw_s = (s1["adamw_s"] - s0["adamw_s"]) / args.steps
+
+    gemm = time_dominant_gemm(sess)
+    link = link_roofline(sess.req.weight_buf)
+    roofline = {"bound": "mfma", "achieved": gemm["tflops"], "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": gemm["tflops"] / MFMA_BF16_PEAK_TFLOPS,
+                "traffic": None, "kernel": gemm["kernel"], "shape_MNK": gemm["shape"],
+                "avg_launch_ms": gemm["ms"]}
+    sess.close()
+    base = None if args.no_cpu_baseline else cpu_baseline(cfg)
+
+    out = {
+        "metric": "model TFLOPS & tokens/s per GPU, host-streamed layer fwd+bwd (7B/14B shapes)",
+        "value": model_tflops, "unit": "model TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name, "layers": cfg.n_layers, "hidden": cfg.hidden,
+                   "heads": cfg.n_heads, "kv_heads": cfg.n_kv_heads, "ffn": cfg.ffn,
+                   "vocab": cfg.vocab, "micro_batch": cfg.micro_batch, "seq_len": cfg.seq_len,
+                   "grad_accum": cfg.grad_accum, "ckpt_interval": cfg.ckpt_interval,
+                   "grad_slabs": cfg.n_grad_slabs, "global_batch_tokens": tokens_per_step},
+        "tokens_per_s": tok_s, "hardware_tflops": hw_tflops,
+        "mfma_frac_end_to_end": model_tflops / MFMA_BF16_PEAK_TFLOPS,
+        "h2d_GBps": h2d, "d2h_GBps": d2h, "adamw_s_per_step": adamw_s,
+        "loss_last": losses[-1],
+        "link_roofline": link,
+        "h2d_frac_of_link": h2d / link["h2d_GBps"],
+        "pipeline": {k: (s1[k] - s0[k]) / args.steps for k in
+                     ("slab_waits", "slab_wait_s", "accumulate_s", "weight_loads", "layer_forwards",
+                      "layer_backwards")},
+        "roofline": roofline, "cpu_baseline": base,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libmt.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with "
-                      "`python -m host_memory_centric_stateless_amd.build`")
+                      "`python host_memory_centric_stateless_amd/build.py`")
 _lib = C.CDLL(LIB_PATH)
 
 
@@ -113,6 +113,7 @@ _SIGS = {
     "mt_bind_layer": ([_P, _I32, _P, _P, _P, _P, _I64], C.c_int),
     "mt_forward": ([_P, _P, _P, _F, _P], C.c_int),
     "mt_backward": ([_P, _I32], C.c_int),
+    "mt_backward_step": ([_P, _I32, C.POINTER(mt_adamw_hparams), _I64], C.c_int),
     "mt_flush_grads": ([_P], C.c_int),
     "mt_adamw_step": ([_P, C.POINTER(mt_adamw_hparams), _I64], C.c_int),
     "mt_get_stats": ([_P, C.POINTER(mt_stats)], C.c_int),
@@ -130,6 +131,7 @@ _SIGS = {
     "mtk_attention_fwd": ([_P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P], C.c_int),
     "mtk_attention_bwd": ([_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P], C.c_int),
     "mtk_cross_entropy": ([_P, _I64, _P, _I64, _I32, _F, _I64, _P, _I64, _P, _P, _P], C.c_int),
+    "mtk_copy": ([_P, _P, C.c_size_t, _I32, _P], C.c_int),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -210,6 +212,10 @@ def mt_forward(ctx, tokens: np.ndarray, labels: np.ndarray, grad_scale: float, l
 
 def mt_backward(ctx, accumulate: int):
     _check(_lib.mt_backward(ctx, int(accumulate)), "mt_backward", ctx)
+
+
+def mt_backward_step(ctx, accumulate: int, hp: mt_adamw_hparams, step: int):
+    _check(_lib.mt_backward_step(ctx, int(accumulate), C.byref(hp), step), "mt_backward_step", ctx)
 
 
 def mt_flush_grads(ctx):
@@ -300,6 +306,10 @@ def mtk_cross_entropy(logits, ld, labels, T, V, grad_scale, n_valid, dlogits, ld
     _check(_lib.mtk_cross_entropy(_ptr(logits), ld, _ptr(labels), T, V, grad_scale, n_valid,
                                   _ptr(dlogits), ld_d, _ptr(loss_rows), _ptr(loss_out),
                                   _stream(stream)), "mtk_cross_entropy")
+
+
+def mtk_copy(dst, src, nbytes, workgroups, stream=None):
+    _check(_lib.mtk_copy(_ptr(dst), _ptr(src), nbytes, workgroups, _stream(stream)), "mtk_copy")
 
 
 from .session import Session, aligned_zeros  # noqa: E402,F401

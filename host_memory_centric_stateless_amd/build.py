@@ -1,6 +1,6 @@
 """Build libmt.so in-tree with hipcc for gfx950.
 
-    python -m host_memory_centric_stateless_amd.build [-v]
+    python host_memory_centric_stateless_amd/build.py [-v]
 
 Every .hip / .cpp file under csrc/ is compiled to an object (in parallel) and
 linked into host_memory_centric_stateless_amd/libmt.so.  Objects go to

@@ -60,6 +60,10 @@ hipError_t launch_cross_entropy(const float* logits, int64_t ld, const int32_t* 
                                 int V, float grad_scale, int64_t n_valid, uint16_t* dlogits,
                                 int64_t ld_d, float* loss_rows, float* loss_out, hipStream_t s);
 
+// 16-byte-vector copy by `wgs` workgroups (bytes multiple of 16; either side
+// may be host-mapped pinned memory).
+hipError_t launch_copy(void* dst, const void* src, size_t bytes, int wgs, hipStream_t s);
+
 // Shape checks shared by the C-ABI wrappers and the engine.
 bool gemm_shape_ok(const mt_gemm_args& a, const char** why);
 

@@ -251,7 +251,25 @@ __global__ __launch_bounds__(NT) void loss_reduce_kernel(const float* __restrict
   if (threadIdx.x == 0) *out = s * inv_n;
 }
 
+// ------------------------------------------------------------- host copy
+// Streams 16-byte vectors from device memory into host-mapped pinned memory
+// (or back): the GPU's own stores cross the host link, so a gradient slab can
+// drain while the copy engine is busy bringing the next layer in.
+__global__ void copy16_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst, int64_t n16) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+    dst[i] = src[i];
+}
+
 }  // namespace
+
+hipError_t launch_copy(void* dst, const void* src, size_t bytes, int wgs, hipStream_t s) {
+  const int64_t n16 = (int64_t)(bytes / 16);
+  if (n16 > 0)
+    hipLaunchKernelGGL(copy16_kernel, dim3(wgs), dim3(NT), 0, s,
+                       static_cast<const uint4*>(src), static_cast<uint4*>(dst), n16);
+  return hipGetLastError();
+}
 
 hipError_t launch_rmsnorm_fwd(const float* x, const uint16_t* g, uint16_t* out, float* rstd,
                               int64_t T, int h, float eps, hipStream_t s) {

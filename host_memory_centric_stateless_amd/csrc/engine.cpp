@@ -69,10 +69,19 @@ struct Job {
   int slab = -1, group = 0, parity = 0;
   int64_t e0 = 0, n = 0;
   bool add = false;
+  bool adamw = false;  // run the optimizer on this range once it is accumulated
+  int unit = -1;       // streamed unit whose working copy the update refreshes
   std::vector<int32_t> tok;
 };
 
 enum State { ST_UNBOUND, ST_IDLE, ST_FWD, ST_BWD, ST_FLUSHED };
+
+// Gradients drain to pinned host memory through a small copy kernel rather
+// than the copy engine: on the MI355X host link a kernel's stores keep ~50
+// GB/s device->host while the engine streams the next layer host->device at
+// ~45 GB/s, whereas two engine copies in opposite directions leave the
+// device->host one at ~28 GB/s.  32 workgroups are enough to fill the link.
+constexpr int kDrainWorkgroups = 32;
 
 double now_s() {
   return std::chrono::duration<double>(std::chrono::steady_clock::now().time_since_epoch())
@@ -133,6 +142,12 @@ struct mt_ctx {
   std::vector<int> free_slabs;
   int embed_busy[2] = {0, 0};
   int delay_us = 0;
+  // overlapped optimizer (mt_backward_step)
+  bool fused = false;
+  mt_adamw_hparams hp{};
+  int64_t opt_step = 0;
+  std::vector<char> upd_pending;  // per streamed unit: update not applied yet
+  bool embed_upd_pending = false;
 
   std::mutex err_mu;
   std::string err;
@@ -402,6 +417,11 @@ mt_status issue_load(mt_ctx* c, const Load& ld) {
   const uint16_t* src;
   int64_t n;
   c->unit_src(ld.unit, &src, &n);
+  {  // an overlapped optimizer step may still be refreshing this unit's copy
+    std::unique_lock<std::mutex> lk(c->mu);
+    c->idle_cv.wait(lk, [&] { return !c->upd_pending[ld.unit] || c->poisoned.load(); });
+    if (c->poisoned) return MT_E_ABORTED;
+  }
   MT_HIP(c, hipStreamWaitEvent(c->sp, c->ev_free[ld.buf], 0));
   MT_HIP(c, hipMemcpyAsync(c->wbuf[ld.buf], src, (size_t)n * 2, hipMemcpyHostToDevice, c->sp));
   MT_HIP(c, hipEventRecord(c->ev_ready[ld.buf], c->sp));
@@ -436,10 +456,10 @@ int acquire_slab(mt_ctx* c) {
 
 // Gradient of a unit is complete in device slab s: copy it out and hand it to
 // the worker.
-mt_status offload_slab(mt_ctx* c, int s, int group, int64_t e0, int64_t n) {
+mt_status offload_slab(mt_ctx* c, int s, int group, int64_t e0, int64_t n, int unit) {
   MT_HIP(c, hipEventRecord(c->ev_written[s], c->sc));
   MT_HIP(c, hipStreamWaitEvent(c->so, c->ev_written[s], 0));
-  MT_HIP(c, hipMemcpyAsync(c->hslab[s], c->dslab[s], (size_t)n * 4, hipMemcpyDeviceToHost, c->so));
+  MT_HIP(c, launch_copy(c->hslab[s], c->dslab[s], (size_t)n * 4, kDrainWorkgroups, c->so));
   MT_HIP(c, hipEventRecord(c->ev_copied[s], c->so));
   c->st.d2h_bytes += n * 4;
   Job j;
@@ -449,6 +469,8 @@ mt_status offload_slab(mt_ctx* c, int s, int group, int64_t e0, int64_t n) {
   j.e0 = e0;
   j.n = n;
   j.add = c->accumulate != 0;
+  j.adamw = c->fused;
+  j.unit = unit;
   {
     std::lock_guard<std::mutex> g(c->mu);
     c->jobs.push_back(std::move(j));
@@ -477,8 +499,8 @@ void worker_main(mt_ctx* c) {
     } else {
       if (c->delay_us > 0) std::this_thread::sleep_for(std::chrono::microseconds(c->delay_us));
       const double t0 = now_s();
+      const mt_ctx::Bind& b = c->bind_of(j.kind == Job::SLAB ? j.group : MT_GROUP_EMBED);
       if (j.kind == Job::SLAB) {
-        const mt_ctx::Bind& b = c->bind_of(j.group);
         accumulate(*c->pool, b.grad + j.e0, c->hslab[j.slab], j.n, j.add);
       } else {
         const int64_t h = c->p.c.hidden;
@@ -486,8 +508,22 @@ void worker_main(mt_ctx* c) {
         embed_scatter(*c->pool, c->embed.grad, j.tok.data(), (int64_t)j.tok.size(), h,
                       c->dx0_stage[j.parity]);
       }
+      const double t1 = now_s();
+      if (j.adamw) {
+        const int64_t e0 = j.kind == Job::SLAB ? j.e0 : 0;
+        const int64_t n = j.kind == Job::SLAB ? j.n : b.n;
+        adamw(*c->pool, b.master + e0, b.grad + e0, b.m + e0, b.v + e0,
+              b.pinned ? b.pinned + e0 : nullptr, n, c->hp, c->opt_step);
+      }
       std::lock_guard<std::mutex> g(c->mu);
-      c->st.accumulate_s += now_s() - t0;
+      c->st.accumulate_s += t1 - t0;
+      if (j.adamw) {
+        c->st.adamw_s += now_s() - t1;
+        if (j.kind == Job::SLAB)
+          c->upd_pending[j.unit] = 0;
+        else
+          c->embed_upd_pending = false;
+      }
     }
     {
       std::lock_guard<std::mutex> g(c->mu);
@@ -572,7 +608,7 @@ mt_status run_step(mt_ctx* c, const Step& s) {
                                      c->wsp<float>(p.ws.dy0), c->wsp<uint16_t>(p.ws.dyb), slab,
                                      c->wsp<float>(p.ws.partial), T, (int)h, cs));
       }
-      mt_status r = offload_slab(c, sl, MT_GROUP_HEAD, e0, ne);
+      mt_status r = offload_slab(c, sl, MT_GROUP_HEAD, e0, ne, p.c.n_layers + ch);
       if (r != MT_OK) return r;
       break;
     }
@@ -591,7 +627,7 @@ mt_status run_step(mt_ctx* c, const Step& s) {
       MT_HIP(c, block_backward(c, W, acts_of(c, w, x), dy, c->wsp<uint16_t>(p.ws.dyb), dx, slab));
       c->dy_idx ^= 1;
       c->st.layer_backwards += 1;
-      mt_status r = offload_slab(c, sl, l, 0, p.layer_elems);
+      mt_status r = offload_slab(c, sl, l, 0, p.layer_elems, l);
       if (r != MT_OK) return r;
       break;
     }
@@ -606,14 +642,14 @@ mt_status run_step(mt_ctx* c, const Step& s) {
       float* dx0 = c->wsp<float>(c->dy_idx ? p.ws.dy1 : p.ws.dy0);
       MT_HIP(c, hipEventRecord(c->ev_dx0[par], cs));
       MT_HIP(c, hipStreamWaitEvent(c->so, c->ev_dx0[par], 0));
-      MT_HIP(c, hipMemcpyAsync(c->dx0_stage[par], dx0, (size_t)T * h * 4, hipMemcpyDeviceToHost,
-                               c->so));
+      MT_HIP(c, launch_copy(c->dx0_stage[par], dx0, (size_t)T * h * 4, kDrainWorkgroups, c->so));
       MT_HIP(c, hipEventRecord(c->ev_dx0_copied[par], c->so));
       c->st.d2h_bytes += T * h * 4;
       Job j;
       j.kind = Job::EMBED;
       j.parity = par;
       j.add = c->accumulate != 0;
+      j.adamw = c->fused;
       j.tok = c->tok_cur;
       {
         std::lock_guard<std::mutex> gd(c->mu);
@@ -703,6 +739,7 @@ extern "C" mt_status mt_create(const mt_config* cfg, const mt_device_arena* a, m
   c->ckpt = (uint8_t*)a->checkpoints;
   c->ws = (uint8_t*)a->workspace;
   c->layers.resize(cfg->n_layers);
+  c->upd_pending.assign(cfg->n_layers + p.n_chunks, 0);
 
   auto ev = [&](hipEvent_t* x) { return hipEventCreateWithFlags(x, hipEventDisableTiming); };
   for (int i = 0; i < 2; ++i) {
@@ -845,6 +882,11 @@ extern "C" mt_status mt_forward(mt_ctx* c, const int32_t* tokens, const int32_t*
     if (labels[t] >= p.c.vocab || labels[t] < -1) return MT_E_ARG;
     n_valid += labels[t] >= 0;
   }
+  {  // an overlapped optimizer step may still be updating the embedding
+    std::unique_lock<std::mutex> lk(c->mu);
+    c->idle_cv.wait(lk, [&] { return !c->embed_upd_pending || c->poisoned.load(); });
+    if (c->poisoned) return MT_E_ABORTED;
+  }
   c->parity = (int)(c->mb & 1);
   const int par = c->parity;
   // staging of two micro-batches ago must have reached the device
@@ -877,18 +919,39 @@ extern "C" mt_status mt_forward(mt_ctx* c, const int32_t* tokens, const int32_t*
   return MT_OK;
 }
 
-extern "C" mt_status mt_backward(mt_ctx* c, int32_t accumulate_flag) {
+static mt_status backward_impl(mt_ctx* c, int32_t accumulate_flag, const mt_adamw_hparams* hp,
+                               int64_t step) {
   mt_status r = check_live(c);
   if (r != MT_OK) return r;
   if (c->state != ST_FWD) return MT_E_STATE;
   if (accumulate_flag != 0 && accumulate_flag != 1) return MT_E_ARG;
   c->accumulate = accumulate_flag;
+  c->fused = hp != nullptr;
+  if (c->fused) {
+    std::lock_guard<std::mutex> g(c->mu);
+    c->hp = *hp;
+    c->opt_step = step;
+    std::fill(c->upd_pending.begin(), c->upd_pending.end(), 1);
+    c->embed_upd_pending = true;
+  }
   r = run_until(c, c->steps.size(), 0, 0.0f);
+  c->fused = false;
   if (r != MT_OK) return r;
+  if (hp) c->buf_unit[0] = c->buf_unit[1] = -1;  // working copies are being rewritten
   c->mb += 1;
   c->st.microbatches += 1;
-  c->state = ST_BWD;
+  c->state = hp ? ST_IDLE : ST_BWD;
   return MT_OK;
+}
+
+extern "C" mt_status mt_backward(mt_ctx* c, int32_t accumulate_flag) {
+  return backward_impl(c, accumulate_flag, nullptr, 0);
+}
+
+extern "C" mt_status mt_backward_step(mt_ctx* c, int32_t accumulate_flag,
+                                      const mt_adamw_hparams* hp, int64_t step) {
+  if (!c || !hp || step < 1) return MT_E_ARG;
+  return backward_impl(c, accumulate_flag, hp, step);
 }
 
 extern "C" mt_status mt_flush_grads(mt_ctx* c) {

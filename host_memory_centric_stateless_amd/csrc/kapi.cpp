@@ -81,3 +81,11 @@ extern "C" mt_status mtk_cross_entropy(const float* logits, int64_t ld, const in
   return hip_status(launch_cross_entropy(logits, ld, labels, T, V, grad_scale, n_valid, dlogits,
                                          ld_d, loss_rows, loss_out, (hipStream_t)stream));
 }
+
+extern "C" mt_status mtk_copy(void* dst, const void* src, size_t bytes, int32_t workgroups,
+                              void* stream) {
+  if (!dst || !src || bytes % 16 || workgroups < 1 || workgroups > 65535 ||
+      ((uintptr_t)dst % 16) || ((uintptr_t)src % 16))
+    return MT_E_ARG;
+  return hip_status(launch_copy(dst, src, bytes, workgroups, (hipStream_t)stream));
+}

@@ -13,7 +13,7 @@ import numpy as np
 import torch
 
 from . import (MT_GROUP_EMBED, MT_GROUP_HEAD, make_config, mt_adamw_hparams, mt_adamw_step,
-               mt_backward, mt_bind_layer, mt_create, mt_destroy, mt_device_arena,
+               mt_backward, mt_backward_step, mt_bind_layer, mt_create, mt_destroy, mt_device_arena,
                mt_device_requirements, mt_flush_grads, mt_forward, mt_get_stats, mt_layout)
 
 
@@ -112,11 +112,28 @@ class Session:
         return float(losses.mean())
 
     def step(self, tokens: np.ndarray, labels: np.ndarray, step: int, lr: Optional[float] = None,
-             weight_decay: float = 0.01) -> float:
-        loss = self.forward_backward(tokens, labels)
+             weight_decay: float = 0.01, overlap_optimizer: bool = True) -> float:
+        """One optimizer step.  overlap_optimizer: run each group's AdamW on
+        the CPU worker as soon as its gradient of the last micro-batch is in
+        (mt_backward_step) instead of after the flush (mt_adamw_step)."""
         hp = mt_adamw_hparams(lr if lr is not None else self.cfg.lr, 0.9, 0.999, 1e-8, weight_decay)
-        mt_adamw_step(self.ctx, hp, step)
-        return loss
+        if not overlap_optimizer:
+            loss = self.forward_backward(tokens, labels)
+            mt_adamw_step(self.ctx, hp, step)
+            return loss
+        acc = tokens.shape[0]
+        losses = np.zeros(acc, dtype=np.float32)
+        with torch.cuda.device(self.device):
+            for mb in range(acc):
+                mt_forward(self.ctx, tokens[mb].reshape(-1), labels[mb].reshape(-1), 1.0 / acc,
+                           losses[mb:mb + 1])
+                if mb + 1 < acc:
+                    mt_backward(self.ctx, 1 if mb > 0 else 0)
+                else:
+                    mt_backward_step(self.ctx, 1 if mb > 0 else 0, hp, step)
+            mt_flush_grads(self.ctx)
+        self._losses = losses
+        return float(losses.mean())
 
     def stats(self) -> dict:
         return mt_get_stats(self.ctx)

@@ -1,0 +1,125 @@
+"""Summarise a rocprofv3 kernel + memory-copy trace of a streamed training run.
+
+    python -m host_memory_centric_stateless_amd.trace_summary <dir>/<prefix> [--window last]
+
+Reads <prefix>_kernel_trace.csv and <prefix>_memory_copy_trace.csv (rocprofv3
+--kernel-trace --memory-copy-trace --output-format csv) and prints:
+
+* per-kernel total / average duration and share of kernel time;
+* busy time (union of intervals) of kernels, host->device copies and
+  device->host copies;
+* copy/compute overlap = |copies AND kernels| / min(|copies|, |kernels|)
+  (union measure), for H2D, D2H and both;
+* large-copy durations (copies longer than 1 ms).
+
+--window last restricts everything to the span of the last `--last-frac` of
+the run's copy activity (default: whole trace).
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+from collections import defaultdict
+from typing import List, Tuple
+
+Interval = Tuple[int, int]
+
+
+def _read(path):
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def union(iv: List[Interval]) -> List[Interval]:
+    out: List[Interval] = []
+    for a, b in sorted(iv):
+        if out and a <= out[-1][1]:
+            if b > out[-1][1]:
+                out[-1] = (out[-1][0], b)
+        else:
+            out.append((a, b))
+    return out
+
+
+def measure(iv: List[Interval]) -> int:
+    return sum(b - a for a, b in iv)
+
+
+def intersect(x: List[Interval], y: List[Interval]) -> List[Interval]:
+    i = j = 0
+    out = []
+    while i < len(x) and j < len(y):
+        a, b = max(x[i][0], y[j][0]), min(x[i][1], y[j][1])
+        if a < b:
+            out.append((a, b))
+        if x[i][1] < y[j][1]:
+            i += 1
+        else:
+            j += 1
+    return out
+
+
+def clip(iv, lo, hi):
+    return [(max(a, lo), min(b, hi)) for a, b in iv if b > lo and a < hi]
+
+
+def summarize(prefix: str, t0: int = None, t1: int = None) -> str:
+    kt = _read(prefix + "_kernel_trace.csv")
+    mc = _read(prefix + "_memory_copy_trace.csv")
+    kern = [(int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]) for r in kt]
+    h2d = [(int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in mc
+           if r["Direction"].endswith("HOST_TO_DEVICE")]
+    d2h = [(int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in mc
+           if r["Direction"].endswith("DEVICE_TO_HOST")]
+    lo = t0 if t0 is not None else min([k[0] for k in kern] + [c[0] for c in h2d + d2h])
+    hi = t1 if t1 is not None else max([k[1] for k in kern] + [c[1] for c in h2d + d2h])
+    kern = [(max(a, lo), min(b, hi), n) for a, b, n in kern if b > lo and a < hi]
+    h2d, d2h = clip(h2d, lo, hi), clip(d2h, lo, hi)
+
+    per = defaultdict(lambda: [0, 0])
+    for a, b, n in kern:
+        per[n][0] += 1
+        per[n][1] += b - a
+    ktot = sum(v[1] for v in per.values())
+    K = union([(a, b) for a, b, _ in kern])
+    H, D = union(h2d), union(d2h)
+    C = union(h2d + d2h)
+    lines = [f"window: {(hi - lo) / 1e9:.3f} s",
+             f"kernel busy (union): {measure(K) / 1e9:.3f} s  ({100 * measure(K) / (hi - lo):.1f}% of window)",
+             f"H2D busy (union):    {measure(H) / 1e9:.3f} s  ({len(h2d)} copies)",
+             f"D2H busy (union):    {measure(D) / 1e9:.3f} s  ({len(d2h)} copies)",
+             f"any copy busy:       {measure(C) / 1e9:.3f} s"]
+    for name, X in (("H2D", H), ("D2H", D), ("any copy", C)):
+        if measure(X) and measure(K):
+            ov = measure(intersect(X, K)) / min(measure(X), measure(K))
+            lines.append(f"overlap {name:8s} with kernels: {ov:.3f}")
+    for name, X in (("H2D", h2d), ("D2H", d2h)):
+        big = [b - a for a, b in X if b - a > 1_000_000]
+        if big:
+            lines.append(f"{name} copies > 1 ms: n={len(big)} mean {sum(big) / len(big) / 1e6:.2f} ms "
+                         f"min {min(big) / 1e6:.2f} max {max(big) / 1e6:.2f}")
+    lines.append("")
+    lines.append(f"{'kernel':70s} {'calls':>6s} {'total ms':>10s} {'avg us':>10s} {'share':>6s}")
+    for n, (c, t) in sorted(per.items(), key=lambda kv: -kv[1][1]):
+        short = n.replace("mt::(anonymous namespace)::", "").split("(")[0][:70]
+        lines.append(f"{short:70s} {c:6d} {t / 1e6:10.1f} {t / c / 1e3:10.1f} {100 * t / ktot:5.1f}%")
+    return "\n".join(lines)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("prefix")
+    ap.add_argument("--start-frac", type=float, default=0.0,
+                    help="start the window this fraction into the trace")
+    a = ap.parse_args()
+    t0 = None
+    if a.start_frac > 0:
+        kt = _read(a.prefix + "_kernel_trace.csv")
+        lo = min(int(r["Start_Timestamp"]) for r in kt)
+        hi = max(int(r["End_Timestamp"]) for r in kt)
+        t0 = int(lo + a.start_frac * (hi - lo))
+    print(summarize(a.prefix, t0=t0))
+
+
+if __name__ == "__main__":
+    main()

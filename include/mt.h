@@ -182,8 +182,21 @@ mt_status mt_forward(mt_ctx* ctx, const int32_t* tokens, const int32_t* labels, 
  * every slab is in flight. */
 mt_status mt_backward(mt_ctx* ctx, int32_t accumulate);
 
+/* mt_backward for the LAST micro-batch of an optimizer step, with the
+ * optimizer overlapped: as soon as a group's (or LM-head chunk's) gradient is
+ * complete in host memory the CPU worker runs AdamW on it (same arithmetic as
+ * mt_adamw_step) and refreshes its pinned bf16 working copy, while the GPU
+ * keeps working on the remaining layers.  A later mt_forward waits, per
+ * streamed unit, for that unit's update before copying it; mt_flush_grads
+ * waits for all of them.  mt_adamw_step must not be called for this step.
+ * Built from the optimizer running where the state lives (m.lqnn.cn MegaTrain
+ * article, 二) and the pipelined slab worker (三.3). */
+mt_status mt_backward_step(mt_ctx* ctx, int32_t accumulate, const mt_adamw_hparams* hp,
+                           int64_t step);
+
 /* Wait until every gradient of every enqueued backward is in the host grads
- * and all streams are idle; writes pending losses. */
+ * (and, after mt_backward_step, every group is updated) and all streams are
+ * idle; writes pending losses. */
 mt_status mt_flush_grads(mt_ctx* ctx);
 
 /* AdamW on every bound group (decoupled weight decay, bias correction, step is

@@ -103,6 +103,14 @@ mt_status mtk_cross_entropy(const float* logits, int64_t ld, const int32_t* labe
                             int32_t V, float grad_scale, int64_t n_valid, uint16_t* dlogits,
                             int64_t ld_d, float* loss_rows, float* loss_out, void* stream);
 
+/* Copy `bytes` (multiple of 16, both pointers 16-byte aligned) with a copy
+ * kernel of `workgroups` 256-thread workgroups instead of the copy engine.
+ * Either side may be pinned host memory (hipHostMalloc), which the kernel
+ * reads or writes across the host link.  Used to drain gradient slabs to the
+ * host while the copy engine streams the next layer in (the pages' three
+ * overlapped stages, m.lqnn.cn MegaTrain article 三.2-三.3). */
+mt_status mtk_copy(void* dst, const void* src, size_t bytes, int32_t workgroups, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
