@@ -26,7 +26,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
-KERNEL_COPY_WGS = (32, 128, 512)
+KERNEL_COPY_WGS = (8, 32)
 
 
 def model_flops_per_token(cfg) -> float:

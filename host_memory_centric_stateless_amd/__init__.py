@@ -54,7 +54,8 @@ class mt_config(C.Structure):
                 ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("ffn", C.c_int32),
                 ("vocab", C.c_int32), ("rms_eps", C.c_float), ("rope_base", C.c_float),
                 ("micro_batch", C.c_int32), ("seq_len", C.c_int32), ("ckpt_interval", C.c_int32),
-                ("n_grad_slabs", C.c_int32), ("host_threads", C.c_int32)]
+                ("n_grad_slabs", C.c_int32), ("host_threads", C.c_int32),
+                ("slab_bf16", C.c_int32)]
 
 
 class mt_tensor_desc(C.Structure):
@@ -168,11 +169,11 @@ def _stream(s):
 
 
 # ------------------------------------------------------------ config helpers
-def make_config(cfg, host_threads: int = 0) -> mt_config:
+def make_config(cfg, host_threads: int = 0, slab_bf16: bool = True) -> mt_config:
     """mt_config from any object with the ModelConfig attribute names."""
     return mt_config(cfg.n_layers, cfg.hidden, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ffn,
                      cfg.vocab, cfg.rms_eps, cfg.rope_base, cfg.micro_batch, cfg.seq_len,
-                     cfg.ckpt_interval, cfg.n_grad_slabs, host_threads)
+                     cfg.ckpt_interval, cfg.n_grad_slabs, host_threads, int(bool(slab_bf16)))
 
 
 # ------------------------------------------------------------- C-ABI calls

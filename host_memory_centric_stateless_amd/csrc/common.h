@@ -44,10 +44,11 @@ __host__ __device__ inline uint32_t pack_bf2(float lo, float hi) {
 hipError_t launch_gemm(const mt_gemm_args& a, hipStream_t s);
 hipError_t launch_rmsnorm_fwd(const float* x, const uint16_t* g, uint16_t* out, float* rstd,
                               int64_t T, int h, float eps, hipStream_t s);
+// dg receives the gain gradient in fp32, or in bf16 via dg_bf16 when dg is null.
 hipError_t launch_rmsnorm_bwd(const float* dn, const float* x, const float* rstd,
                               const uint16_t* g, const float* resid, float* dx,
-                              uint16_t* dx_bf16, float* dg, float* partial, int64_t T, int h,
-                              hipStream_t s);
+                              uint16_t* dx_bf16, float* dg, uint16_t* dg_bf16, float* partial,
+                              int64_t T, int h, hipStream_t s);
 size_t rmsnorm_bwd_partial_bytes(int64_t T, int h);
 hipError_t launch_rope(uint16_t* qkv, int64_t T, int seq, int nq, int nkv, int d,
                        const float* cos_t, const float* sin_t, int inverse, hipStream_t s);

@@ -144,13 +144,16 @@ __global__ __launch_bounds__(NT) void rmsnorm_bwd_kernel(
   }
 }
 
-__global__ void colsum_kernel(const float* __restrict__ partial, float* __restrict__ out, int nblk,
-                              int h) {
+__global__ void colsum_kernel(const float* __restrict__ partial, float* __restrict__ out,
+                              uint16_t* __restrict__ out16, int nblk, int h) {
   const int c = blockIdx.x * blockDim.x + threadIdx.x;
   if (c >= h) return;
   float s = 0.0f;
   for (int b = 0; b < nblk; ++b) s += partial[(int64_t)b * h + c];
-  out[c] = s;
+  if (out16)
+    out16[c] = f2bf(s);
+  else
+    out[c] = s;
 }
 
 int64_t bwd_blocks(int64_t T) {
@@ -291,8 +294,8 @@ size_t rmsnorm_bwd_partial_bytes(int64_t T, int h) {
 
 hipError_t launch_rmsnorm_bwd(const float* dn, const float* x, const float* rstd,
                               const uint16_t* g, const float* resid, float* dx,
-                              uint16_t* dx_bf16, float* dg, float* partial, int64_t T, int h,
-                              hipStream_t s) {
+                              uint16_t* dx_bf16, float* dg, uint16_t* dg_bf16, float* partial,
+                              int64_t T, int h, hipStream_t s) {
   const int64_t nb = bwd_blocks(T);
   const int64_t rpb = (T + nb - 1) / nb;
   const int64_t nblk = (T + rpb - 1) / rpb;
@@ -307,7 +310,7 @@ hipError_t launch_rmsnorm_bwd(const float* dn, const float* x, const float* rstd
   MT_BWD(1) MT_BWD(2) MT_BWD(4) MT_BWD(5) MT_BWD(8) MT_BWD(16)
 #undef MT_BWD
   if (!done) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(colsum_kernel, dim3((h + NT - 1) / NT), dim3(NT), 0, s, partial, dg,
+  hipLaunchKernelGGL(colsum_kernel, dim3((h + NT - 1) / NT), dim3(NT), 0, s, partial, dg, dg_bf16,
                      (int)nblk, h);
   return hipGetLastError();
 }

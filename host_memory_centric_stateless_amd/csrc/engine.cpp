@@ -77,11 +77,12 @@ struct Job {
 enum State { ST_UNBOUND, ST_IDLE, ST_FWD, ST_BWD, ST_FLUSHED };
 
 // Gradients drain to pinned host memory through a small copy kernel rather
-// than the copy engine: on the MI355X host link a kernel's stores keep ~50
-// GB/s device->host while the engine streams the next layer host->device at
-// ~45 GB/s, whereas two engine copies in opposite directions leave the
-// device->host one at ~28 GB/s.  32 workgroups are enough to fill the link.
-constexpr int kDrainWorkgroups = 32;
+// than the copy engine.  Measured on the MI355X host link (810 MB slabs): two
+// engine copies in opposite directions leave device->host at ~28 GB/s
+// (~13 GB/s under the streaming load), while 8 copy workgroups keep ~41 GB/s
+// device->host next to ~52 GB/s host->device.  With 12 or more workgroups the
+// first GEMM launched beside the copy stalls for 4-10 ms, with 8 it does not.
+constexpr int kDrainWorkgroups = 8;
 
 double now_s() {
   return std::chrono::duration<double>(std::chrono::steady_clock::now().time_since_epoch())
@@ -281,7 +282,7 @@ hipError_t block_forward(mt_ctx* c, const uint16_t* W, const Acts& a, float* y) 
 // bf16); writes dx/dxb (gradient of the block input) and every weight
 // gradient into `slab` at the layer's flat offsets.
 hipError_t block_backward(mt_ctx* c, const uint16_t* W, const Acts& a, const float* dy,
-                          uint16_t* dyb, float* dx, float* slab) {
+                          uint16_t* dyb, float* dx, void* slab_base) {
   const Plan& p = c->p;
   const mt_config& g = p.c;
   const int64_t T = p.T, h = g.hidden, F = g.ffn;
@@ -294,25 +295,33 @@ hipError_t block_backward(mt_ctx* c, const uint16_t* W, const Acts& a, const flo
   uint16_t* dout = c->wsp<uint16_t>(p.ws.dout);
   uint16_t* dqkv = c->wsp<uint16_t>(p.ws.dqkv);
   float* partial = c->wsp<float>(p.ws.partial);
+  // weight gradients land in the slab at the layer's flat offsets, fp32 or bf16
+  const bool sb = p.slab_bf16;
+  const int wepi = sb ? MT_EPI_BF16 : MT_EPI_F32;
+  auto slab = [&](int t) -> void* {
+    return static_cast<uint8_t*>(slab_base) + (size_t)L[t].off * (sb ? 2 : 4);
+  };
+  auto dg32 = [&](int t) { return sb ? nullptr : static_cast<float*>(slab(t)); };
+  auto dg16 = [&](int t) { return sb ? static_cast<uint16_t*>(slab(t)) : nullptr; };
   // MLP: dm = dy Wd, fused SwiGLU backward -> dgu = [da | du]
   CK(gemm(s, MT_GEMM_NN, MT_EPI_SWIGLU_BWD, T, F, h, dyb, h, W + L[T_WDOWN].off, F, dgu, 2 * F,
           nullptr, 0, a.gu, 2 * F, F));
-  CK(gemm(s, MT_GEMM_TN, MT_EPI_F32, h, F, T, dyb, h, a.m, F, slab + L[T_WDOWN].off, F));
-  CK(gemm(s, MT_GEMM_TN, MT_EPI_F32, 2 * F, h, T, dgu, 2 * F, a.n2, h, slab + L[T_WGATE].off, h));
+  CK(gemm(s, MT_GEMM_TN, wepi, h, F, T, dyb, h, a.m, F, slab(T_WDOWN), F));
+  CK(gemm(s, MT_GEMM_TN, wepi, 2 * F, h, T, dgu, 2 * F, a.n2, h, slab(T_WGATE), h));
   CK(gemm(s, MT_GEMM_NN, MT_EPI_F32, T, h, 2 * F, dgu, 2 * F, W + L[T_WGATE].off, h, dn, h));
   CK(launch_rmsnorm_bwd(dn, a.h1, a.rstd2, W + L[T_MLP_NORM].off, dy, dh1, dh1b,
-                        slab + L[T_MLP_NORM].off, partial, T, (int)h, s));
+                        dg32(T_MLP_NORM), dg16(T_MLP_NORM), partial, T, (int)h, s));
   // attention
   CK(gemm(s, MT_GEMM_NN, MT_EPI_BF16, T, p.qd, h, dh1b, h, W + L[T_WO].off, p.qd, dout, p.qd));
-  CK(gemm(s, MT_GEMM_TN, MT_EPI_F32, h, p.qd, T, dh1b, h, a.o, p.qd, slab + L[T_WO].off, p.qd));
+  CK(gemm(s, MT_GEMM_TN, wepi, h, p.qd, T, dh1b, h, a.o, p.qd, slab(T_WO), p.qd));
   CK(launch_attn_bwd(a.qkv, a.o, dout, a.lse, c->wsp<float>(p.ws.dsum), dqkv, g.micro_batch,
                      g.seq_len, g.n_heads, g.n_kv_heads, g.head_dim, s));
   CK(launch_rope(dqkv, T, g.seq_len, g.n_heads, g.n_kv_heads, g.head_dim,
                  c->wsp<float>(p.ws.cos_t), c->wsp<float>(p.ws.sin_t), 1, s));
-  CK(gemm(s, MT_GEMM_TN, MT_EPI_F32, p.ldq, h, T, dqkv, p.ldq, a.n1, h, slab + L[T_WQ].off, h));
+  CK(gemm(s, MT_GEMM_TN, wepi, p.ldq, h, T, dqkv, p.ldq, a.n1, h, slab(T_WQ), h));
   CK(gemm(s, MT_GEMM_NN, MT_EPI_F32, T, h, p.ldq, dqkv, p.ldq, W + L[T_WQ].off, h, dn, h));
   CK(launch_rmsnorm_bwd(dn, a.x, a.rstd1, W + L[T_ATTN_NORM].off, dh1, dx, dyb,
-                        slab + L[T_ATTN_NORM].off, partial, T, (int)h, s));
+                        dg32(T_ATTN_NORM), dg16(T_ATTN_NORM), partial, T, (int)h, s));
   return hipSuccess;
 }
 
@@ -459,9 +468,10 @@ int acquire_slab(mt_ctx* c) {
 mt_status offload_slab(mt_ctx* c, int s, int group, int64_t e0, int64_t n, int unit) {
   MT_HIP(c, hipEventRecord(c->ev_written[s], c->sc));
   MT_HIP(c, hipStreamWaitEvent(c->so, c->ev_written[s], 0));
-  MT_HIP(c, launch_copy(c->hslab[s], c->dslab[s], (size_t)n * 4, kDrainWorkgroups, c->so));
+  const size_t bytes = (size_t)n * (c->p.slab_bf16 ? 2 : 4);
+  MT_HIP(c, launch_copy(c->hslab[s], c->dslab[s], bytes, kDrainWorkgroups, c->so));
   MT_HIP(c, hipEventRecord(c->ev_copied[s], c->so));
-  c->st.d2h_bytes += n * 4;
+  c->st.d2h_bytes += (int64_t)bytes;
   Job j;
   j.kind = Job::SLAB;
   j.slab = s;
@@ -473,6 +483,7 @@ mt_status offload_slab(mt_ctx* c, int s, int group, int64_t e0, int64_t n, int u
   j.unit = unit;
   {
     std::lock_guard<std::mutex> g(c->mu);
+    if (j.adamw) c->upd_pending[unit] = 1;
     c->jobs.push_back(std::move(j));
     c->outstanding += 1;
   }
@@ -501,7 +512,11 @@ void worker_main(mt_ctx* c) {
       const double t0 = now_s();
       const mt_ctx::Bind& b = c->bind_of(j.kind == Job::SLAB ? j.group : MT_GROUP_EMBED);
       if (j.kind == Job::SLAB) {
-        accumulate(*c->pool, b.grad + j.e0, c->hslab[j.slab], j.n, j.add);
+        if (c->p.slab_bf16)
+          accumulate_bf16(*c->pool, b.grad + j.e0, reinterpret_cast<const uint16_t*>(c->hslab[j.slab]),
+                          j.n, j.add);
+        else
+          accumulate(*c->pool, b.grad + j.e0, c->hslab[j.slab], j.n, j.add);
       } else {
         const int64_t h = c->p.c.hidden;
         if (!j.add) memset(c->embed.grad, 0, (size_t)c->embed.n * sizeof(float));
@@ -509,15 +524,22 @@ void worker_main(mt_ctx* c) {
                       c->dx0_stage[j.parity]);
       }
       const double t1 = now_s();
+      {  // the staging memory is consumed: hand it back before the optimizer runs
+        std::lock_guard<std::mutex> g(c->mu);
+        c->st.accumulate_s += t1 - t0;
+        if (j.kind == Job::SLAB)
+          c->free_slabs.push_back(j.slab);
+        else
+          c->embed_busy[j.parity] = 0;
+      }
+      c->slab_cv.notify_all();
+      c->idle_cv.notify_all();
       if (j.adamw) {
         const int64_t e0 = j.kind == Job::SLAB ? j.e0 : 0;
         const int64_t n = j.kind == Job::SLAB ? j.n : b.n;
         adamw(*c->pool, b.master + e0, b.grad + e0, b.m + e0, b.v + e0,
               b.pinned ? b.pinned + e0 : nullptr, n, c->hp, c->opt_step);
-      }
-      std::lock_guard<std::mutex> g(c->mu);
-      c->st.accumulate_s += t1 - t0;
-      if (j.adamw) {
+        std::lock_guard<std::mutex> g(c->mu);
         c->st.adamw_s += now_s() - t1;
         if (j.kind == Job::SLAB)
           c->upd_pending[j.unit] = 0;
@@ -527,10 +549,12 @@ void worker_main(mt_ctx* c) {
     }
     {
       std::lock_guard<std::mutex> g(c->mu);
-      if (j.kind == Job::SLAB)
-        c->free_slabs.push_back(j.slab);
-      else
-        c->embed_busy[j.parity] = 0;
+      if (e != hipSuccess) {
+        if (j.kind == Job::SLAB)
+          c->free_slabs.push_back(j.slab);
+        else
+          c->embed_busy[j.parity] = 0;
+      }
       c->outstanding -= 1;
     }
     c->slab_cv.notify_all();
@@ -588,24 +612,28 @@ mt_status run_step(mt_ctx* c, const Step& s) {
       const int ch = s.chunk;
       const int sl = acquire_slab(c);
       if (sl < 0) return MT_E_ABORTED;
-      float* slab = c->dslab[sl];
+      const bool sb = p.slab_bf16;
+      const size_t es = sb ? 2 : 4;
+      uint8_t* slab = reinterpret_cast<uint8_t*>(c->dslab[sl]);
       const int64_t e0 = p.chunk_e0[ch], ne = p.chunk_e0[ch + 1] - e0;
       const uint16_t* Wr = W + (ch == 0 ? p.head[1].off : 0);
-      float* dWr = slab + (ch == 0 ? p.head[1].off : 0);
+      void* dWr = slab + (ch == 0 ? p.head[1].off : 0) * es;
       const int64_t r0 = p.chunk_row0[ch], nr = p.chunk_row0[ch + 1] - r0;
       if (ch == 0 && p.head[1].off > p.head[0].numel)
-        MT_HIP(c, hipMemsetAsync(slab, 0, (size_t)p.head[1].off * 4, cs));
+        MT_HIP(c, hipMemsetAsync(slab, 0, (size_t)p.head[1].off * es, cs));
       const uint16_t* dl = c->wsp<uint16_t>(p.ws.dlogits) + r0;
       MT_HIP(c, gemm(cs, MT_GEMM_NN, c->head_grad_first ? MT_EPI_F32 : MT_EPI_F32_ACCUM, T, h, nr,
                      dl, V, Wr, h, c->wsp<float>(p.ws.dxf), h));
       c->head_grad_first = false;
-      MT_HIP(c, gemm(cs, MT_GEMM_TN, MT_EPI_F32, nr, h, T, dl, V, c->wsp<uint16_t>(p.ws.xf), h,
-                     dWr, h));
+      MT_HIP(c, gemm(cs, MT_GEMM_TN, sb ? MT_EPI_BF16 : MT_EPI_F32, nr, h, T, dl, V,
+                     c->wsp<uint16_t>(p.ws.xf), h, dWr, h));
       if (ch == 0) {
         c->dy_idx = 0;
         MT_HIP(c, launch_rmsnorm_bwd(c->wsp<float>(p.ws.dxf), c->wsp<float>(p.ws.xL),
                                      c->wsp<float>(p.ws.rstd_f), W + p.head[0].off, nullptr,
-                                     c->wsp<float>(p.ws.dy0), c->wsp<uint16_t>(p.ws.dyb), slab,
+                                     c->wsp<float>(p.ws.dy0), c->wsp<uint16_t>(p.ws.dyb),
+                                     sb ? nullptr : reinterpret_cast<float*>(slab),
+                                     sb ? reinterpret_cast<uint16_t*>(slab) : nullptr,
                                      c->wsp<float>(p.ws.partial), T, (int)h, cs));
       }
       mt_status r = offload_slab(c, sl, MT_GROUP_HEAD, e0, ne, p.c.n_layers + ch);
@@ -616,11 +644,11 @@ mt_status run_step(mt_ctx* c, const Step& s) {
       const int l = s.layer, w = s.slot;
       const int sl = acquire_slab(c);
       if (sl < 0) return MT_E_ABORTED;
-      float* slab = c->dslab[sl];
+      void* slab = c->dslab[sl];
       if (p.layer_elems != p.layer[T_WDOWN].off + p.layer[T_WDOWN].numel ||
           p.layer[T_WQ].off != p.layer[T_ATTN_NORM].numel ||
           p.layer[T_MLP_NORM].numel + p.layer[T_MLP_NORM].off != p.layer[T_WGATE].off)
-        MT_HIP(c, hipMemsetAsync(slab, 0, (size_t)p.layer_elems * 4, cs));
+        MT_HIP(c, hipMemsetAsync(slab, 0, (size_t)p.layer_elems * (p.slab_bf16 ? 2 : 4), cs));
       float* x = (l % K == 0) ? c->ckpt_ptr(l / K) : c->slot_x(w);
       float* dy = c->wsp<float>(c->dy_idx ? p.ws.dy1 : p.ws.dy0);
       float* dx = c->wsp<float>(c->dy_idx ? p.ws.dy0 : p.ws.dy1);
@@ -653,6 +681,7 @@ mt_status run_step(mt_ctx* c, const Step& s) {
       j.tok = c->tok_cur;
       {
         std::lock_guard<std::mutex> gd(c->mu);
+        if (j.adamw) c->embed_upd_pending = true;
         c->jobs.push_back(std::move(j));
         c->outstanding += 1;
       }
@@ -928,11 +957,12 @@ static mt_status backward_impl(mt_ctx* c, int32_t accumulate_flag, const mt_adam
   c->accumulate = accumulate_flag;
   c->fused = hp != nullptr;
   if (c->fused) {
+    // A unit is marked "update pending" only when its gradient job is queued
+    // (offload_slab / the embedding job): that is its last use in this step,
+    // so no copy of it issued by this backward can wait on its own update.
     std::lock_guard<std::mutex> g(c->mu);
     c->hp = *hp;
     c->opt_step = step;
-    std::fill(c->upd_pending.begin(), c->upd_pending.end(), 1);
-    c->embed_upd_pending = true;
   }
   r = run_until(c, c->steps.size(), 0, 0.0f);
   c->fused = false;

@@ -141,6 +141,23 @@ void accumulate(ThreadPool& pool, float* grad, const float* src, int64_t n, bool
   });
 }
 
+static inline float bf16_to_f32(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+void accumulate_bf16(ThreadPool& pool, float* grad, const uint16_t* src, int64_t n, bool add) {
+  chunked(pool, n, [&](int64_t b, int64_t e) {
+    if (add) {
+      for (int64_t i = b; i < e; ++i) grad[i] += bf16_to_f32(src[i]);
+    } else {
+      for (int64_t i = b; i < e; ++i) grad[i] = bf16_to_f32(src[i]);
+    }
+  });
+}
+
 void embed_gather(ThreadPool& pool, const float* emb, const int32_t* tok, int64_t T, int64_t h,
                   float* x0) {
   const int64_t per = 64;

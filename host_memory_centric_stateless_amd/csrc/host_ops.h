@@ -41,6 +41,8 @@ void cast_bf16(ThreadPool& pool, const float* src, uint16_t* dst, int64_t n);
 void adamw(ThreadPool& pool, float* p, const float* g, float* m, float* v, uint16_t* bf, int64_t n,
            const mt_adamw_hparams& hp, int64_t step);
 void accumulate(ThreadPool& pool, float* grad, const float* src, int64_t n, bool add);
+// grad = float(src) or grad += float(src) for bf16 src.
+void accumulate_bf16(ThreadPool& pool, float* grad, const uint16_t* src, int64_t n, bool add);
 // x0[t, :] = emb[tok[t], :]
 void embed_gather(ThreadPool& pool, const float* emb, const int32_t* tok, int64_t T, int64_t h,
                   float* x0);

@@ -30,7 +30,7 @@ extern "C" mt_status mtk_rmsnorm_bwd(const float* dn, const float* x, const floa
   if (!dn || !x || !rstd || !g || !dx || !dg || !workspace || T < 1 || h < 4 || h % 4 ||
       h > 16384)
     return MT_E_ARG;
-  return hip_status(launch_rmsnorm_bwd(dn, x, rstd, g, resid, dx, dx_bf16, dg,
+  return hip_status(launch_rmsnorm_bwd(dn, x, rstd, g, resid, dx, dx_bf16, dg, nullptr,
                                        static_cast<float*>(workspace), T, h,
                                        (hipStream_t)stream));
 }

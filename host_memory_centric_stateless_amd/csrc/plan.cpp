@@ -43,6 +43,7 @@ std::string make_plan(const mt_config& c, Plan* p) {
   if (c.n_grad_slabs < 1 || c.n_grad_slabs > 64) return "n_grad_slabs must be in 1..64";
   if (!(c.rms_eps >= 0.0f) || !(c.rope_base > 1.0f)) return "rms_eps / rope_base";
   if (c.host_threads < 0) return "host_threads must be >= 0";
+  if (c.slab_bf16 != 0 && c.slab_bf16 != 1) return "slab_bf16 must be 0 or 1";
 
   p->c = c;
   const int64_t h = c.hidden, F = c.ffn, V = c.vocab;
@@ -141,7 +142,8 @@ std::string make_plan(const mt_config& c, Plan* p) {
   w.bytes = o;
 
   p->weight_buf_bytes = round_bytes((size_t)p->unit_elems * 2);
-  p->slab_bytes = round_bytes((size_t)p->unit_elems * 4);
+  p->slab_bf16 = c.slab_bf16 != 0;
+  p->slab_bytes = round_bytes((size_t)p->unit_elems * (p->slab_bf16 ? 2 : 4));
   p->window_bytes = (size_t)std::min(c.ckpt_interval, c.n_layers) * s.bytes;
   p->ckpt_bytes = (size_t)std::max(1, p->n_segments - 1) * round_bytes(T * h * 4);
   return "";

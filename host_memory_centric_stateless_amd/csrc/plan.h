@@ -51,6 +51,7 @@ struct Plan {
   int n_chunks;
   std::vector<int64_t> chunk_row0, chunk_e0;
   int64_t unit_elems;
+  bool slab_bf16;       // gradient slabs hold bf16 (else fp32)
   int n_segments;
   SlotLayout slot;
   WorkLayout ws;

@@ -26,13 +26,14 @@ def aligned_zeros(n: int, align: int = 64) -> np.ndarray:
 
 class Session:
     def __init__(self, cfg, host_threads: int = 0, device: str = "cuda:0",
-                 ckpt_interval: Optional[int] = None, n_grad_slabs: Optional[int] = None):
+                 ckpt_interval: Optional[int] = None, n_grad_slabs: Optional[int] = None,
+                 slab_bf16: bool = True):
         if ckpt_interval is not None:
             cfg = cfg.replace(ckpt_interval=ckpt_interval)
         if n_grad_slabs is not None:
             cfg = cfg.replace(n_grad_slabs=n_grad_slabs)
         self.cfg = cfg
-        self.c = make_config(cfg, host_threads)
+        self.c = make_config(cfg, host_threads, slab_bf16)
         self.req = mt_device_requirements(self.c)
         self.groups = [MT_GROUP_EMBED] + list(range(cfg.n_layers)) + [MT_GROUP_HEAD]
         self.layout: Dict[int, Tuple[list, int]] = {g: mt_layout(self.c, g) for g in self.groups}

@@ -68,6 +68,9 @@ typedef struct mt_config {
   int32_t ckpt_interval;  /* K: checkpoint every K layers (>= 1)                */
   int32_t n_grad_slabs;   /* gradient slab pool size (1..64), 12 by default     */
   int32_t host_threads;   /* CPU threads for accumulate / AdamW (0 = automatic) */
+  int32_t slab_bf16;      /* 1: gradient slabs carry bf16 (half the device->host
+                             bytes; rounded once per micro-batch, accumulated in
+                             fp32 on the host); 0: fp32 slabs                   */
 } mt_config;
 
 /* One tensor of a group's flat layout. */

@@ -67,7 +67,9 @@ def test_device_requirements(name):
     P = OL.group_layout(cfg, 0)[1]
     assert r.unit_elems >= P
     assert r.weight_buf == -(-r.unit_elems * 2 // 256) * 256
-    assert r.grad_slab == -(-r.unit_elems * 4 // 256) * 256
+    assert r.grad_slab == -(-r.unit_elems * 2 // 256) * 256          # bf16 slabs (default)
+    r32 = mt.mt_device_requirements(mt.make_config(cfg, slab_bf16=False))
+    assert r32.grad_slab == -(-r.unit_elems * 4 // 256) * 256        # fp32 slabs
     # the whole vocabulary is covered by head chunks that each fit one unit
     H = OL.group_layout(cfg, OL.HEAD)[1]
     assert r.head_chunks * r.unit_elems >= H

@@ -45,10 +45,10 @@ def _sync_state(sess, st):
     sess.bind()
 
 
-def gradients_at_matched_weights(cfg, steps, report):
+def gradients_at_matched_weights(cfg, steps, report, **kw):
     """Each step starts the GPU from the oracle's state, so the gradient
     comparison measures the kernels, not the divergence of two trajectories."""
-    sess = _session(cfg)
+    sess = _session(cfg, **kw)
     st = HostState(cfg, np.float32)
     st.load_weights(weight_stream(cfg, 0))
     worst = {"loss": 0.0, "grad": 0.0}
@@ -97,10 +97,11 @@ def independent_trajectories(cfg, steps):
     return losses, weights
 
 
-def test_c1_gradients_match_oracle_each_step():
+@pytest.mark.parametrize("slab_bf16", [True, False])
+def test_c1_gradients_match_oracle_each_step(slab_bf16):
     cfg = PRESETS["C1"]
     report = {}
-    worst, stats = gradients_at_matched_weights(cfg, 3, report)
+    worst, stats = gradients_at_matched_weights(cfg, 3, report, slab_bf16=slab_bf16)
     for k, v in sorted(report.items()):
         print(k, " ".join(f"{e:.2e}/{sg:.1e}" for e, sg in v))
     print("stats", stats)
@@ -148,7 +149,8 @@ def _grads_after_one_step(cfg, **kw):
 def test_pipeline_invariants_bit_exact():
     cfg = PRESETS["C1"].replace(grad_accum=2)
     base_loss, base, _ = _grads_after_one_step(cfg, ckpt_interval=1)
-    for kw in ({"ckpt_interval": 2}, {"n_grad_slabs": 1}, {"n_grad_slabs": 2}):
+    for kw in ({"ckpt_interval": 2}, {"n_grad_slabs": 1}, {"n_grad_slabs": 2},
+               {"host_threads": 3}):
         print("variant", kw, flush=True)
         loss, g, stats = _grads_after_one_step(cfg, **kw)
         assert loss == base_loss, kw
