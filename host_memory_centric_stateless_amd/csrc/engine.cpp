@@ -134,6 +134,10 @@ struct mt_ctx {
   int accumulate = 0;
 
   std::unique_ptr<ThreadPool> pool;
+  std::unique_ptr<ThreadPool> opt_pool;  // optimizer work, separate from slab draining
+  std::thread opt_worker;
+  std::deque<Job> opt_jobs;
+  std::condition_variable opt_cv;
   std::thread worker;
   std::mutex mu;
   std::condition_variable cv, slab_cv, idle_cv;
@@ -534,17 +538,17 @@ void worker_main(mt_ctx* c) {
       }
       c->slab_cv.notify_all();
       c->idle_cv.notify_all();
-      if (j.adamw) {
-        const int64_t e0 = j.kind == Job::SLAB ? j.e0 : 0;
-        const int64_t n = j.kind == Job::SLAB ? j.n : b.n;
-        adamw(*c->pool, b.master + e0, b.grad + e0, b.m + e0, b.v + e0,
-              b.pinned ? b.pinned + e0 : nullptr, n, c->hp, c->opt_step);
+      if (j.adamw) {  // the optimizer thread takes it from here
         std::lock_guard<std::mutex> g(c->mu);
-        c->st.adamw_s += now_s() - t1;
-        if (j.kind == Job::SLAB)
-          c->upd_pending[j.unit] = 0;
-        else
-          c->embed_upd_pending = false;
+        Job o;
+        o.kind = j.kind;
+        o.group = j.kind == Job::SLAB ? j.group : MT_GROUP_EMBED;
+        o.e0 = j.kind == Job::SLAB ? j.e0 : 0;
+        o.n = j.kind == Job::SLAB ? j.n : b.n;
+        o.unit = j.unit;
+        c->opt_jobs.push_back(std::move(o));
+        c->outstanding += 1;
+        c->opt_cv.notify_all();
       }
     }
     {
@@ -558,6 +562,35 @@ void worker_main(mt_ctx* c) {
       c->outstanding -= 1;
     }
     c->slab_cv.notify_all();
+    c->idle_cv.notify_all();
+  }
+}
+
+// AdamW on groups (or head chunks) whose last-micro-batch gradient is complete,
+// on its own thread and pool so that slab draining never waits behind it.
+void opt_main(mt_ctx* c) {
+  for (;;) {
+    Job j;
+    {
+      std::unique_lock<std::mutex> lk(c->mu);
+      c->opt_cv.wait(lk, [&] { return c->stop || !c->opt_jobs.empty(); });
+      if (c->opt_jobs.empty()) return;
+      j = std::move(c->opt_jobs.front());
+      c->opt_jobs.pop_front();
+    }
+    const double t0 = now_s();
+    const mt_ctx::Bind& b = c->bind_of(j.group);
+    adamw(*c->opt_pool, b.master + j.e0, b.grad + j.e0, b.m + j.e0, b.v + j.e0,
+          b.pinned ? b.pinned + j.e0 : nullptr, j.n, c->hp, c->opt_step);
+    {
+      std::lock_guard<std::mutex> g(c->mu);
+      c->st.adamw_s += now_s() - t0;
+      if (j.kind == Job::SLAB)
+        c->upd_pending[j.unit] = 0;
+      else
+        c->embed_upd_pending = false;
+      c->outstanding -= 1;
+    }
     c->idle_cv.notify_all();
   }
 }
@@ -804,9 +837,11 @@ extern "C" mt_status mt_create(const mt_config* cfg, const mt_device_arena* a, m
   }
 
   c->pool.reset(new ThreadPool(cfg->host_threads > 0 ? cfg->host_threads : default_threads()));
+  c->opt_pool.reset(new ThreadPool(cfg->host_threads > 0 ? cfg->host_threads : default_threads()));
   if (const char* d = getenv("MT_TEST_WORKER_DELAY_US")) c->delay_us = atoi(d);
   for (int i = c->nslab - 1; i >= 0; --i) c->free_slabs.push_back(i);
   c->worker = std::thread(worker_main, c.get());
+  c->opt_worker = std::thread(opt_main, c.get());
   *out = c.release();
   return MT_OK;
 }
@@ -821,7 +856,9 @@ extern "C" void mt_destroy(mt_ctx* c) {
     c->stop = true;
   }
   c->cv.notify_all();
+  c->opt_cv.notify_all();
   if (c->worker.joinable()) c->worker.join();
+  if (c->opt_worker.joinable()) c->opt_worker.join();
   for (auto& b : c->layers)
     if (b.pinned) (void)hipHostFree(b.pinned);
   if (c->head.pinned) (void)hipHostFree(c->head.pinned);
