@@ -96,6 +96,11 @@ class mt_stats(C.Structure):
         return {k: getattr(self, k) for k, _ in self._fields_}
 
 
+class mt_kernel_time(C.Structure):
+    _fields_ = [("name", C.c_char * 32), ("launches", C.c_int64), ("ms", C.c_double),
+                ("flop", C.c_double), ("bytes", C.c_double)]
+
+
 class mt_gemm_args(C.Structure):
     _fields_ = [("layout", C.c_int32), ("epilogue", C.c_int32), ("M", C.c_int64),
                 ("N", C.c_int64), ("K", C.c_int64), ("A", C.c_void_p), ("lda", C.c_int64),
@@ -119,6 +124,8 @@ _SIGS = {
     "mt_adamw_step": ([_P, C.POINTER(mt_adamw_hparams), _I64], C.c_int),
     "mt_get_stats": ([_P, C.POINTER(mt_stats)], C.c_int),
     "mt_last_error": ([_P], C.c_char_p),
+    "mt_kernel_timing": ([_P, _I32], C.c_int),
+    "mt_get_kernel_times": ([_P, C.POINTER(mt_kernel_time), _I32, C.POINTER(_I32)], C.c_int),
     "mt_destroy": ([_P], None),
     "mt_host_cast_bf16": ([_P, _P, _I64, _I32], C.c_int),
     "mt_host_adamw": ([_P, _P, _P, _P, _P, _I64, C.POINTER(mt_adamw_hparams), _I64, _I32], C.c_int),
@@ -231,6 +238,19 @@ def mt_get_stats(ctx) -> dict:
     s = mt_stats()
     _check(_lib.mt_get_stats(ctx, C.byref(s)), "mt_get_stats", ctx)
     return s.as_dict()
+
+
+def mt_kernel_timing(ctx, enable: bool):
+    _check(_lib.mt_kernel_timing(ctx, int(bool(enable))), "mt_kernel_timing", ctx)
+
+
+def mt_get_kernel_times(ctx) -> list:
+    """[{name, launches, ms, flop, bytes}] by descending device time."""
+    n = _I32()
+    buf = (mt_kernel_time * 64)()
+    _check(_lib.mt_get_kernel_times(ctx, buf, 64, C.byref(n)), "mt_get_kernel_times", ctx)
+    return [{"name": k.name.decode(), "launches": k.launches, "ms": k.ms, "flop": k.flop,
+             "bytes": k.bytes} for k in buf[:min(n.value, 64)]]
 
 
 def mt_last_error(ctx) -> str:

@@ -34,9 +34,11 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 #include <chrono>
 #include <deque>
+#include <map>
 #include <memory>
 #include <string>
 #include <vector>
@@ -154,6 +156,47 @@ struct mt_ctx {
   std::vector<char> upd_pending;  // per streamed unit: update not applied yet
   bool embed_upd_pending = false;
 
+  // live per-kernel timing (mt_kernel_timing)
+  struct KRec {
+    hipEvent_t a, b;
+    const char* name;
+    double flop, bytes;
+  };
+  struct KTot {
+    int64_t n = 0;
+    double ms = 0, flop = 0, bytes = 0;
+  };
+  bool ktiming = false;
+  std::vector<hipEvent_t> ev_pool;
+  std::vector<KRec> krec;
+  std::map<std::string, KTot> ktot;
+  hipEvent_t take_event() {
+    if (!ev_pool.empty()) {
+      hipEvent_t e = ev_pool.back();
+      ev_pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+  hipError_t collect_kernel_times() {
+    for (auto& r : krec) {
+      float ms = 0.0f;
+      hipError_t e = hipEventElapsedTime(&ms, r.a, r.b);
+      if (e != hipSuccess) return e;
+      KTot& t = ktot[r.name];
+      t.n += 1;
+      t.ms += ms;
+      t.flop += r.flop;
+      t.bytes += r.bytes;
+      ev_pool.push_back(r.a);
+      ev_pool.push_back(r.b);
+    }
+    krec.clear();
+    return hipSuccess;
+  }
+
   std::mutex err_mu;
   std::string err;
   std::atomic<bool> poisoned{false};
@@ -243,12 +286,46 @@ Acts acts_of(mt_ctx* c, int w, float* x) {
               reinterpret_cast<uint16_t*>(b + s.m)};
 }
 
-hipError_t gemm(hipStream_t s, int layout, int epi, int64_t M, int64_t N, int64_t K,
+// Records timing events around one launch when mt_kernel_timing is on.
+struct KScope {
+  mt_ctx* c;
+  hipStream_t s;
+  hipEvent_t a = nullptr;
+  const char* name;
+  double flop, bytes;
+  KScope(mt_ctx* c_, hipStream_t s_, const char* n, double f, double b)
+      : c(c_), s(s_), name(n), flop(f), bytes(b) {
+    if (c->ktiming && (a = c->take_event()) && hipEventRecord(a, s) != hipSuccess) a = nullptr;
+  }
+  ~KScope() {
+    if (!a) return;
+    hipEvent_t b = c->take_event();
+    if (b && hipEventRecord(b, s) == hipSuccess) c->krec.push_back({a, b, name, flop, bytes});
+  }
+};
+
+const char* gemm_name(int layout, int epi) {
+  static const char* n[3][6] = {
+      {"gemm_nt_bf16", "gemm_nt_f32", "gemm_nt_resid", "gemm_nt_accum", "gemm_nt_swiglu", "gemm_nt_x"},
+      {"gemm_nn_bf16", "gemm_nn_f32", "gemm_nn_resid", "gemm_nn_accum", "gemm_nn_x", "gemm_nn_swiglu_bwd"},
+      {"gemm_tn_bf16", "gemm_tn_f32", "gemm_tn_resid", "gemm_tn_accum", "gemm_tn_x", "gemm_tn_x"}};
+  return n[layout][epi];
+}
+
+hipError_t gemm(mt_ctx* c, hipStream_t s, int layout, int epi, int64_t M, int64_t N, int64_t K,
                 const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, void* C,
                 int64_t ldc, const float* R = nullptr, int64_t ldr = 0, uint16_t* gu = nullptr,
                 int64_t ldgu = 0, int64_t ffn = 0) {
   mt_gemm_args a{layout, epi, M, N, K, A, lda, B, ldb, C, ldc, R, ldr, gu, ldgu, ffn};
+  // the SwiGLU product computes both the gate and the up projection
+  const double nn = (epi == MT_EPI_SWIGLU) ? 2.0 * N : (double)N;
+  KScope k(c, s, gemm_name(layout, epi), 2.0 * M * nn * K, 2.0 * (M * K + nn * K));
   return launch_gemm(a, s);
+}
+
+// Algorithmic work of the other kernels.
+double attn_pairs(const mt_config& g) {
+  return (double)g.micro_batch * g.n_heads * 0.5 * (double)g.seq_len * (g.seq_len + 1.0);
 }
 
 #define CK(expr)                            \
@@ -265,19 +342,33 @@ hipError_t block_forward(mt_ctx* c, const uint16_t* W, const Acts& a, float* y) 
   const int64_t T = p.T, h = g.hidden, F = g.ffn;
   hipStream_t s = c->sc;
   const TensorOff* L = p.layer;
-  CK(launch_rmsnorm_fwd(a.x, W + L[T_ATTN_NORM].off, a.n1, a.rstd1, T, (int)h, g.rms_eps, s));
-  CK(gemm(s, MT_GEMM_NT, MT_EPI_BF16, T, p.ldq, h, a.n1, h, W + L[T_WQ].off, h, a.qkv, p.ldq));
-  CK(launch_rope(a.qkv, T, g.seq_len, g.n_heads, g.n_kv_heads, g.head_dim,
-                 c->wsp<float>(p.ws.cos_t), c->wsp<float>(p.ws.sin_t), 0, s));
-  CK(launch_attn_fwd(a.qkv, a.o, a.lse, g.micro_batch, g.seq_len, g.n_heads, g.n_kv_heads,
-                     g.head_dim, s));
-  CK(gemm(s, MT_GEMM_NT, MT_EPI_F32_RESID, T, h, p.qd, a.o, p.qd, W + L[T_WO].off, p.qd, a.h1, h,
+  const double nb_fwd = (double)T * h * 6 + h * 2 + T * 4;   // rmsnorm: x in, bf16 out
+  const double nb_rope = (double)T * (p.qd + p.kvd) * 4;      // q, k read + written
+  {
+    KScope k(c, s, "rmsnorm_fwd", 0, nb_fwd);
+    CK(launch_rmsnorm_fwd(a.x, W + L[T_ATTN_NORM].off, a.n1, a.rstd1, T, (int)h, g.rms_eps, s));
+  }
+  CK(gemm(c, s, MT_GEMM_NT, MT_EPI_BF16, T, p.ldq, h, a.n1, h, W + L[T_WQ].off, h, a.qkv, p.ldq));
+  {
+    KScope k(c, s, "rope", 0, nb_rope);
+    CK(launch_rope(a.qkv, T, g.seq_len, g.n_heads, g.n_kv_heads, g.head_dim,
+                   c->wsp<float>(p.ws.cos_t), c->wsp<float>(p.ws.sin_t), 0, s));
+  }
+  {
+    KScope k(c, s, "attn_fwd", 4.0 * g.head_dim * attn_pairs(g), 0);
+    CK(launch_attn_fwd(a.qkv, a.o, a.lse, g.micro_batch, g.seq_len, g.n_heads, g.n_kv_heads,
+                       g.head_dim, s));
+  }
+  CK(gemm(c, s, MT_GEMM_NT, MT_EPI_F32_RESID, T, h, p.qd, a.o, p.qd, W + L[T_WO].off, p.qd, a.h1, h,
           a.x, h));
-  CK(launch_rmsnorm_fwd(a.h1, W + L[T_MLP_NORM].off, a.n2, a.rstd2, T, (int)h, g.rms_eps, s));
-  CK(gemm(s, MT_GEMM_NT, MT_EPI_SWIGLU, T, F, h, a.n2, h, W + L[T_WGATE].off, h, a.m, F, nullptr,
+  {
+    KScope k(c, s, "rmsnorm_fwd", 0, nb_fwd);
+    CK(launch_rmsnorm_fwd(a.h1, W + L[T_MLP_NORM].off, a.n2, a.rstd2, T, (int)h, g.rms_eps, s));
+  }
+  CK(gemm(c, s, MT_GEMM_NT, MT_EPI_SWIGLU, T, F, h, a.n2, h, W + L[T_WGATE].off, h, a.m, F, nullptr,
           0, a.gu, 2 * F, F));
   if (y)
-    CK(gemm(s, MT_GEMM_NT, MT_EPI_F32_RESID, T, h, F, a.m, F, W + L[T_WDOWN].off, F, y, h, a.h1,
+    CK(gemm(c, s, MT_GEMM_NT, MT_EPI_F32_RESID, T, h, F, a.m, F, W + L[T_WDOWN].off, F, y, h, a.h1,
             h));
   return hipSuccess;
 }
@@ -308,24 +399,37 @@ hipError_t block_backward(mt_ctx* c, const uint16_t* W, const Acts& a, const flo
   auto dg32 = [&](int t) { return sb ? nullptr : static_cast<float*>(slab(t)); };
   auto dg16 = [&](int t) { return sb ? static_cast<uint16_t*>(slab(t)) : nullptr; };
   // MLP: dm = dy Wd, fused SwiGLU backward -> dgu = [da | du]
-  CK(gemm(s, MT_GEMM_NN, MT_EPI_SWIGLU_BWD, T, F, h, dyb, h, W + L[T_WDOWN].off, F, dgu, 2 * F,
+  CK(gemm(c, s, MT_GEMM_NN, MT_EPI_SWIGLU_BWD, T, F, h, dyb, h, W + L[T_WDOWN].off, F, dgu, 2 * F,
           nullptr, 0, a.gu, 2 * F, F));
-  CK(gemm(s, MT_GEMM_TN, wepi, h, F, T, dyb, h, a.m, F, slab(T_WDOWN), F));
-  CK(gemm(s, MT_GEMM_TN, wepi, 2 * F, h, T, dgu, 2 * F, a.n2, h, slab(T_WGATE), h));
-  CK(gemm(s, MT_GEMM_NN, MT_EPI_F32, T, h, 2 * F, dgu, 2 * F, W + L[T_WGATE].off, h, dn, h));
-  CK(launch_rmsnorm_bwd(dn, a.h1, a.rstd2, W + L[T_MLP_NORM].off, dy, dh1, dh1b,
-                        dg32(T_MLP_NORM), dg16(T_MLP_NORM), partial, T, (int)h, s));
+  CK(gemm(c, s, MT_GEMM_TN, wepi, h, F, T, dyb, h, a.m, F, slab(T_WDOWN), F));
+  CK(gemm(c, s, MT_GEMM_TN, wepi, 2 * F, h, T, dgu, 2 * F, a.n2, h, slab(T_WGATE), h));
+  CK(gemm(c, s, MT_GEMM_NN, MT_EPI_F32, T, h, 2 * F, dgu, 2 * F, W + L[T_WGATE].off, h, dn, h));
+  const double nb_bwd = (double)T * h * 18;  // dn, x, resid in; dx (fp32 + bf16) out
+  {
+    KScope k(c, s, "rmsnorm_bwd", 0, nb_bwd);
+    CK(launch_rmsnorm_bwd(dn, a.h1, a.rstd2, W + L[T_MLP_NORM].off, dy, dh1, dh1b,
+                          dg32(T_MLP_NORM), dg16(T_MLP_NORM), partial, T, (int)h, s));
+  }
   // attention
-  CK(gemm(s, MT_GEMM_NN, MT_EPI_BF16, T, p.qd, h, dh1b, h, W + L[T_WO].off, p.qd, dout, p.qd));
-  CK(gemm(s, MT_GEMM_TN, wepi, h, p.qd, T, dh1b, h, a.o, p.qd, slab(T_WO), p.qd));
-  CK(launch_attn_bwd(a.qkv, a.o, dout, a.lse, c->wsp<float>(p.ws.dsum), dqkv, g.micro_batch,
-                     g.seq_len, g.n_heads, g.n_kv_heads, g.head_dim, s));
-  CK(launch_rope(dqkv, T, g.seq_len, g.n_heads, g.n_kv_heads, g.head_dim,
-                 c->wsp<float>(p.ws.cos_t), c->wsp<float>(p.ws.sin_t), 1, s));
-  CK(gemm(s, MT_GEMM_TN, wepi, p.ldq, h, T, dqkv, p.ldq, a.n1, h, slab(T_WQ), h));
-  CK(gemm(s, MT_GEMM_NN, MT_EPI_F32, T, h, p.ldq, dqkv, p.ldq, W + L[T_WQ].off, h, dn, h));
-  CK(launch_rmsnorm_bwd(dn, a.x, a.rstd1, W + L[T_ATTN_NORM].off, dh1, dx, dyb,
-                        dg32(T_ATTN_NORM), dg16(T_ATTN_NORM), partial, T, (int)h, s));
+  CK(gemm(c, s, MT_GEMM_NN, MT_EPI_BF16, T, p.qd, h, dh1b, h, W + L[T_WO].off, p.qd, dout, p.qd));
+  CK(gemm(c, s, MT_GEMM_TN, wepi, h, p.qd, T, dh1b, h, a.o, p.qd, slab(T_WO), p.qd));
+  {
+    KScope k(c, s, "attn_bwd", 10.0 * g.head_dim * attn_pairs(g), 0);
+    CK(launch_attn_bwd(a.qkv, a.o, dout, a.lse, c->wsp<float>(p.ws.dsum), dqkv, g.micro_batch,
+                       g.seq_len, g.n_heads, g.n_kv_heads, g.head_dim, s));
+  }
+  {
+    KScope k(c, s, "rope", 0, (double)T * (p.qd + p.kvd) * 4);
+    CK(launch_rope(dqkv, T, g.seq_len, g.n_heads, g.n_kv_heads, g.head_dim,
+                   c->wsp<float>(p.ws.cos_t), c->wsp<float>(p.ws.sin_t), 1, s));
+  }
+  CK(gemm(c, s, MT_GEMM_TN, wepi, p.ldq, h, T, dqkv, p.ldq, a.n1, h, slab(T_WQ), h));
+  CK(gemm(c, s, MT_GEMM_NN, MT_EPI_F32, T, h, p.ldq, dqkv, p.ldq, W + L[T_WQ].off, h, dn, h));
+  {
+    KScope k(c, s, "rmsnorm_bwd", 0, nb_bwd);
+    CK(launch_rmsnorm_bwd(dn, a.x, a.rstd1, W + L[T_ATTN_NORM].off, dh1, dx, dyb,
+                          dg32(T_ATTN_NORM), dg16(T_ATTN_NORM), partial, T, (int)h, s));
+  }
   return hipSuccess;
 }
 
@@ -473,7 +577,10 @@ mt_status offload_slab(mt_ctx* c, int s, int group, int64_t e0, int64_t n, int u
   MT_HIP(c, hipEventRecord(c->ev_written[s], c->sc));
   MT_HIP(c, hipStreamWaitEvent(c->so, c->ev_written[s], 0));
   const size_t bytes = (size_t)n * (c->p.slab_bf16 ? 2 : 4);
-  MT_HIP(c, launch_copy(c->hslab[s], c->dslab[s], bytes, kDrainWorkgroups, c->so));
+  {
+    KScope k(c, c->so, "drain_d2h", 0, (double)bytes);
+    MT_HIP(c, launch_copy(c->hslab[s], c->dslab[s], bytes, kDrainWorkgroups, c->so));
+  }
   MT_HIP(c, hipEventRecord(c->ev_copied[s], c->so));
   c->st.d2h_bytes += (int64_t)bytes;
   Job j;
@@ -634,7 +741,7 @@ mt_status run_step(mt_ctx* c, const Step& s) {
         MT_HIP(c, launch_rmsnorm_fwd(c->wsp<float>(p.ws.xL), W + p.head[0].off,
                                      c->wsp<uint16_t>(p.ws.xf), c->wsp<float>(p.ws.rstd_f), T,
                                      (int)h, g.rms_eps, cs));
-      MT_HIP(c, gemm(cs, MT_GEMM_NT, MT_EPI_F32, T, nr, h, c->wsp<uint16_t>(p.ws.xf), h, Wr, h,
+      MT_HIP(c, gemm(c, cs, MT_GEMM_NT, MT_EPI_F32, T, nr, h, c->wsp<uint16_t>(p.ws.xf), h, Wr, h,
                      c->wsp<float>(p.ws.logits) + r0, V));
       break;
     }
@@ -655,10 +762,10 @@ mt_status run_step(mt_ctx* c, const Step& s) {
       if (ch == 0 && p.head[1].off > p.head[0].numel)
         MT_HIP(c, hipMemsetAsync(slab, 0, (size_t)p.head[1].off * es, cs));
       const uint16_t* dl = c->wsp<uint16_t>(p.ws.dlogits) + r0;
-      MT_HIP(c, gemm(cs, MT_GEMM_NN, c->head_grad_first ? MT_EPI_F32 : MT_EPI_F32_ACCUM, T, h, nr,
+      MT_HIP(c, gemm(c, cs, MT_GEMM_NN, c->head_grad_first ? MT_EPI_F32 : MT_EPI_F32_ACCUM, T, h, nr,
                      dl, V, Wr, h, c->wsp<float>(p.ws.dxf), h));
       c->head_grad_first = false;
-      MT_HIP(c, gemm(cs, MT_GEMM_TN, sb ? MT_EPI_BF16 : MT_EPI_F32, nr, h, T, dl, V,
+      MT_HIP(c, gemm(c, cs, MT_GEMM_TN, sb ? MT_EPI_BF16 : MT_EPI_F32, nr, h, T, dl, V,
                      c->wsp<uint16_t>(p.ws.xf), h, dWr, h));
       if (ch == 0) {
         c->dy_idx = 0;
@@ -742,6 +849,7 @@ mt_status run_until(mt_ctx* c, size_t end, int64_t n_valid, float grad_scale) {
     }
     if (s.kind == K_CE) {
       const Plan& p = c->p;
+      KScope k(c, c->sc, "cross_entropy", 0, (double)p.T * p.c.vocab * 6);
       MT_HIP(c, launch_cross_entropy(c->wsp<float>(p.ws.logits), p.c.vocab,
                                      c->wsp<int32_t>(p.ws.labels[c->parity]), p.T, p.c.vocab,
                                      grad_scale, n_valid, c->wsp<uint16_t>(p.ws.dlogits),
@@ -875,6 +983,11 @@ extern "C" void mt_destroy(mt_ctx* c) {
   for (auto* e : evs)
     for (int i = 0; i < 2; ++i)
       if (e[i]) (void)hipEventDestroy(e[i]);
+  for (auto& r : c->krec) {
+    c->ev_pool.push_back(r.a);
+    c->ev_pool.push_back(r.b);
+  }
+  for (hipEvent_t e : c->ev_pool) (void)hipEventDestroy(e);
   for (int i = 0; i < c->nslab; ++i) {
     if (c->ev_written[i]) (void)hipEventDestroy(c->ev_written[i]);
     if (c->ev_copied[i]) (void)hipEventDestroy(c->ev_copied[i]);
@@ -1033,6 +1146,7 @@ extern "C" mt_status mt_flush_grads(mt_ctx* c) {
   MT_HIP(c, hipStreamSynchronize(c->sp));
   MT_HIP(c, hipStreamSynchronize(c->sc));
   MT_HIP(c, hipStreamSynchronize(c->so));
+  MT_HIP(c, c->collect_kernel_times());
   for (auto& pl : c->pending_loss) *pl.first = c->loss_pin[pl.second];
   c->pending_loss.clear();
   if (c->state == ST_BWD) c->state = ST_FLUSHED;
@@ -1060,5 +1174,42 @@ extern "C" mt_status mt_get_stats(mt_ctx* c, mt_stats* out) {
   if (!c || !out) return MT_E_ARG;
   std::lock_guard<std::mutex> g(c->mu);
   *out = c->st;
+  return MT_OK;
+}
+
+extern "C" mt_status mt_kernel_timing(mt_ctx* c, int32_t enable) {
+  mt_status r = check_live(c);
+  if (r != MT_OK) return r;
+  if (enable != 0 && enable != 1) return MT_E_ARG;
+  if (enable) {
+    c->ktot.clear();
+    for (auto& k : c->krec) {  // records of an earlier window are dropped unread
+      c->ev_pool.push_back(k.a);
+      c->ev_pool.push_back(k.b);
+    }
+    c->krec.clear();
+  }
+  c->ktiming = enable != 0;
+  return MT_OK;
+}
+
+extern "C" mt_status mt_get_kernel_times(mt_ctx* c, mt_kernel_time* out, int32_t cap,
+                                         int32_t* n_out) {
+  if (!c || !n_out || cap < 0 || (cap > 0 && !out)) return MT_E_ARG;
+  std::vector<std::pair<std::string, mt_ctx::KTot>> v(c->ktot.begin(), c->ktot.end());
+  std::sort(v.begin(), v.end(), [](const auto& a, const auto& b) { return a.second.ms > b.second.ms; });
+  int32_t n = 0;
+  for (auto& kv : v) {
+    if (n < cap) {
+      memset(out[n].name, 0, sizeof(out[n].name));
+      strncpy(out[n].name, kv.first.c_str(), sizeof(out[n].name) - 1);
+      out[n].launches = kv.second.n;
+      out[n].ms = kv.second.ms;
+      out[n].flop = kv.second.flop;
+      out[n].bytes = kv.second.bytes;
+    }
+    ++n;
+  }
+  *n_out = n;
   return MT_OK;
 }

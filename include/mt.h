@@ -208,6 +208,24 @@ mt_status mt_flush_grads(mt_ctx* ctx);
 mt_status mt_adamw_step(mt_ctx* ctx, const mt_adamw_hparams* hp, int64_t step);
 
 mt_status mt_get_stats(mt_ctx* ctx, mt_stats* out);
+
+/* Live per-kernel timing.  While enabled, the library records a pair of HIP
+ * timing events around every kernel it launches (on the stream the kernel
+ * runs on) and, at each mt_flush_grads, adds the elapsed times to per-kind
+ * totals together with each launch's algorithmic work: flop for the bf16 MFMA
+ * kernels (2*M*N*K for a GEMM; 4*d*(causal score pairs) per head forward and
+ * 10*d*pairs backward for attention) and bytes each kernel must read and
+ * write once for the memory-bound ones.  Enabling resets the totals. */
+typedef struct mt_kernel_time {
+  char name[32];
+  int64_t launches;
+  double ms;       /* summed device time */
+  double flop;     /* summed algorithmic floating-point operations */
+  double bytes;    /* summed algorithmic HBM (or host-link) bytes */
+} mt_kernel_time;
+mt_status mt_kernel_timing(mt_ctx* ctx, int32_t enable);
+/* Kinds seen since timing was enabled, by descending device time. */
+mt_status mt_get_kernel_times(mt_ctx* ctx, mt_kernel_time* out, int32_t cap, int32_t* n_out);
 const char* mt_last_error(const mt_ctx* ctx);
 void mt_destroy(mt_ctx* ctx);
 
