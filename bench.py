@@ -130,6 +130,76 @@ def link_roofline(nbytes: int, reps: int = 4):
     return out
 
 
+def block_gemm_shapes(cfg):
+    """(kind, layout, epilogue, M, N, K) of every GEMM of one block at this shape."""
+    import host_memory_centric_stateless_amd as mt
+    T, h, F = cfg.micro_batch * cfg.seq_len, cfg.hidden, cfg.ffn
+    qd, kvd = cfg.n_heads * cfg.head_dim, cfg.n_kv_heads * cfg.head_dim
+    ldq = qd + 2 * kvd
+    NT, NN, TN = mt.MT_GEMM_NT, mt.MT_GEMM_NN, mt.MT_GEMM_TN
+    return [("gemm_nt_bf16 qkv", NT, mt.MT_EPI_BF16, T, ldq, h),
+            ("gemm_nt_resid o", NT, mt.MT_EPI_F32_RESID, T, h, qd),
+            ("gemm_nt_swiglu gate/up", NT, mt.MT_EPI_SWIGLU, T, F, h),
+            ("gemm_nt_resid down", NT, mt.MT_EPI_F32_RESID, T, h, F),
+            ("gemm_nn_swiglu_bwd dm", NN, mt.MT_EPI_SWIGLU_BWD, T, F, h),
+            ("gemm_tn_bf16 dWdown", TN, mt.MT_EPI_BF16, h, F, T),
+            ("gemm_tn_bf16 dWgate/up", TN, mt.MT_EPI_BF16, 2 * F, h, T),
+            ("gemm_nn_f32 dn2", NN, mt.MT_EPI_F32, T, h, 2 * F),
+            ("gemm_nn_bf16 dO", NN, mt.MT_EPI_BF16, T, qd, h),
+            ("gemm_tn_bf16 dWo", TN, mt.MT_EPI_BF16, h, qd, T),
+            ("gemm_tn_bf16 dWqkv", TN, mt.MT_EPI_BF16, ldq, h, T),
+            ("gemm_nn_f32 dn1", NN, mt.MT_EPI_F32, T, h, ldq)]
+
+
+def probe(cfg, reps: int = 2):
+    """Run every block GEMM at this shape `reps` times, then a device copy of
+    known size (the calibration reference for hardware byte counters), one
+    launch per line, timed with HIP events."""
+    import torch
+    import host_memory_centric_stateless_amd as mt
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device="cpu").manual_seed(7)
+    out = []
+    for name, lay, epi, M, N, K in block_gemm_shapes(cfg):
+        NN_ = 2 * N if epi == mt.MT_EPI_SWIGLU else N
+        A = (torch.randn(M if lay != mt.MT_GEMM_TN else K, K if lay != mt.MT_GEMM_TN else M,
+                         generator=g) * 0.5).to(torch.bfloat16).to(dev)
+        B = (torch.randn(NN_ if lay == mt.MT_GEMM_NT else K, K if lay == mt.MT_GEMM_NT else NN_,
+                         generator=g) * 0.02).to(torch.bfloat16).to(dev)
+        lda, ldb = A.shape[1], B.shape[1]
+        ob = 2 if epi in (mt.MT_EPI_BF16, mt.MT_EPI_SWIGLU, mt.MT_EPI_SWIGLU_BWD) else 4
+        ldc = 2 * N if epi == mt.MT_EPI_SWIGLU_BWD else N
+        C = torch.empty(M * ldc * ob, dtype=torch.uint8, device=dev)
+        R = torch.zeros(M, N, dtype=torch.float32, device=dev) if epi == mt.MT_EPI_F32_RESID else None
+        gu = torch.randn(M, 2 * N, generator=g).to(torch.bfloat16).to(dev) \
+            if epi in (mt.MT_EPI_SWIGLU, mt.MT_EPI_SWIGLU_BWD) else None
+        kw = dict(R=R, ldr=N if R is not None else 0, gu=gu, ldgu=2 * N if gu is not None else 0,
+                  ffn=N if gu is not None else 0)
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            mt.mtk_gemm(lay, epi, M, N, K, A, lda, B, ldb, C, ldc, **kw)
+            e1.record()
+            e1.synchronize()
+            ms = e0.elapsed_time(e1)
+            flop = 2.0 * M * NN_ * K
+            out.append({"kernel": name, "MNK": [M, N, K], "ms": ms, "TFLOPs": flop / ms / 1e9,
+                        "algorithmic_bytes": A.numel() * 2 + B.numel() * 2 + M * NN_ * ob})
+        del A, B, C, R, gu
+    nb = 1 << 30
+    src = torch.empty(nb, dtype=torch.uint8, device=dev)
+    dst = torch.empty(nb, dtype=torch.uint8, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    mt.mtk_copy(dst, src, nb, 1024)
+    e1.record()
+    e1.synchronize()
+    out.append({"kernel": "calibration copy16 1 GiB device->device", "bytes_read": nb,
+                "bytes_written": nb, "ms": e0.elapsed_time(e1),
+                "GBps": 2 * nb / e0.elapsed_time(e1) / 1e6})
+    return out
+
+
 def cpu_baseline(cfg, budget_s: float = 30.0):
     """The oracle (fp32 NumPy) on one decoder layer at the same shape:
     forward + recompute forward + backward, on this host's cores."""
@@ -165,6 +235,8 @@ def main():
     ap.add_argument("--config", default="C3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--host-threads", type=int, default=0)
+    ap.add_argument("--probe", action="store_true",
+                    help="only run each block GEMM at this shape and a calibration copy")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the method's multi-GPU "
@@ -176,6 +248,10 @@ def main():
     from synth_inputs import PRESETS, make_batch, weight_stream
 
     cfg = PRESETS[args.config]
+    if args.probe:
+        for row in probe(cfg):
+            print(json.dumps(row), flush=True)
+        return
     t0 = time.perf_counter()
     sess = Session(cfg, host_threads=args.host_threads)
     sess.load_weights(weight_stream(cfg, 0))

@@ -4,9 +4,9 @@
 // (the block's dedicated forward/backward replaces an autograd graph:
 // zhichai.net "MegaTrain：单卡训百亿大模型的突破与实践", design point 4).
 //
-// Tiling: 128x128 output tile per 256-thread workgroup (4 waves as 2x2, each
-// wave 64x64 = 2x2 v_mfma_f32_32x32x16_bf16 tiles), K step 64, LDS double
-// buffered.  LDS holds both operands as [row][k] (k contiguous, row stride 72
+// Tiling: 256x256 (large products) or 128x128 output tile per 256-thread
+// workgroup, 4 waves as 2x2 each owning a quadrant of 32x32
+// v_mfma_f32_32x32x16_bf16 tiles, K step 64, LDS double buffered.  LDS holds both operands as [row][k] (k contiguous, row stride 72
 // elements so 16-byte fragment reads are conflict-free).  Operands whose
 // reduction dimension is the slow one in memory (the transposed layouts of
 // the input- and weight-gradient products) are transposed in registers on the
@@ -22,116 +22,173 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int BM = 128, BN = 128, BK = 64;
+constexpr int BK = 64;
 constexpr int LDSK = BK + 8;  // elements per LDS row
-constexpr int NT = 256;
+constexpr int NT = 256;       // 4 waves as 2 x 2
 
 __device__ inline bf16x8_t frag(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(p));
 }
 
-// Row r (0..127) of a B tile in the SwiGLU product: rows 0..63 are gate rows
-// f0..f0+63, rows 64..127 the matching up rows.
+// Global row of tile row r, clamped into the matrix (out-of-range rows are
+// loaded from a valid row and zeroed, so the loads carry no branches).  In the
+// SwiGLU product the B tile holds gate rows f0..f0+H-1 followed by the
+// matching up rows (H = half the tile).
+template <int H, bool SWI>
 struct RowMap {
-  int64_t row0, nrows;   // plain: global row = row0 + r, valid if < nrows
-  int64_t ffn;           // swiglu: > 0
+  int64_t row0, nrows;   // rows valid below nrows (SwiGLU: gate/up index below ffn)
+  int64_t ffn;
   __device__ inline int64_t map(int r, bool& ok) const {
-    if (ffn > 0) {
-      int64_t f = row0 + (r & 63);
+    if constexpr (SWI) {
+      const int64_t f = row0 + (r % H);
       ok = f < nrows;
-      return (r < 64) ? f : ffn + f;
+      const int64_t fc = ok ? f : nrows - 1;
+      return (r < H) ? fc : ffn + fc;
+    } else {
+      const int64_t g = row0 + r;
+      ok = g < nrows;
+      return ok ? g : nrows - 1;
     }
-    int64_t g = row0 + r;
-    ok = g < nrows;
-    return g;
   }
 };
 
-// Operand stored [row][k] (k contiguous): 128 rows x 64 k, 4 x 16 B per thread.
+// Operand stored [row][k] (k contiguous): R rows x 64 k, R/32 vectors of
+// 16 B per thread.  Out-of-range vectors are zeroed when written to LDS, not
+// when loaded, so no wait on the loads is needed until after the MFMAs.
+template <int R>
 struct LoadK {
-  u32x4 r[4];
-  __device__ inline void load(const uint16_t* base, int64_t ld, const RowMap& rm, int64_t k0,
+  static constexpr int V = R * 8 / NT;
+  u32x4 r[V];
+  uint32_t ok = 0;  // bit i: vector i is inside the matrix
+  template <class Map>
+  __device__ inline void load(const uint16_t* base, int64_t ld, const Map& rm, int64_t k0,
                               int64_t K, int tid) {
+    ok = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int idx = tid + NT * i;
-      int row = idx >> 3;
-      int64_t k = k0 + (idx & 7) * 8;
-      bool ok;
-      int64_t g = rm.map(row, ok);
-      if (ok && k < K)
-        r[i] = *reinterpret_cast<const u32x4*>(base + g * ld + k);
-      else
-        r[i] = u32x4{0, 0, 0, 0};
+    for (int i = 0; i < V; ++i) {
+      const int idx = tid + NT * i;
+      const int64_t k = k0 + (idx & 7) * 8;
+      bool rok;
+      const int64_t g = rm.map(idx >> 3, rok);
+      const bool in = rok && k < K;
+      ok |= (uint32_t)in << i;
+      r[i] = *reinterpret_cast<const u32x4*>(base + g * ld + (in ? k : 0));
     }
   }
   __device__ inline void store(uint16_t* lds, int tid) const {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int idx = tid + NT * i;
-      *reinterpret_cast<u32x4*>(lds + (idx >> 3) * LDSK + (idx & 7) * 8) = r[i];
+    for (int i = 0; i < V; ++i) {
+      const int idx = tid + NT * i;
+      *reinterpret_cast<u32x4*>(lds + (idx >> 3) * LDSK + (idx & 7) * 8) =
+          ((ok >> i) & 1) ? r[i] : u32x4{0, 0, 0, 0};
     }
   }
 };
 
-// Operand stored [k][row] (row contiguous): 64 k x 128 rows.  Thread owns the
-// 8 x 4 block k = kb*8.., rows mb*4.. and writes it transposed into LDS.
+// Operand stored [k][row] (row contiguous): 64 k x R rows, cut into 8 (k) x
+// 4 (row) blocks; each thread reads R/128 blocks with 8-byte loads and writes
+// them transposed as 16-byte LDS rows (zeroing out-of-range parts there).
+template <int R>
 struct LoadT {
-  u32x2 r[8];
+  static constexpr int NB = 2 * R / NT, RB = R / 4;
+  u32x2 r[NB][8];
+  uint32_t ok = 0;  // bit 8b+i: row i of block b is inside the matrix
   __device__ inline void load(const uint16_t* base, int64_t ld, int64_t row0, int64_t nrows,
                               int64_t k0, int64_t K, int tid) {
-    const int kb = tid >> 5, mb = tid & 31;
-    const int64_t g = row0 + mb * 4;
+    ok = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      int64_t k = k0 + kb * 8 + i;
-      if (k < K && g < nrows)
-        r[i] = *reinterpret_cast<const u32x2*>(base + k * ld + g);
-      else
-        r[i] = u32x2{0, 0};
+    for (int b = 0; b < NB; ++b) {
+      const int blk = tid + NT * b;
+      const int kb = blk / RB, mb = blk % RB;
+      const int64_t g = row0 + mb * 4;
+      const bool gin = g < nrows;
+      const int64_t gc = gin ? g : 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int64_t k = k0 + kb * 8 + i;
+        const bool in = gin && k < K;
+        ok |= (uint32_t)in << (8 * b + i);
+        r[b][i] = *reinterpret_cast<const u32x2*>(base + (in ? k : 0) * ld + gc);
+      }
     }
   }
   __device__ inline void store(uint16_t* lds, int tid) const {
-    const int kb = tid >> 5, mb = tid & 31;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      u32x4 o;
+    for (int b = 0; b < NB; ++b) {
+      const int blk = tid + NT * b;
+      const int kb = blk / RB, mb = blk % RB;
+      u32x2 v[8];
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        uint32_t w0 = r[2 * p][j >> 1], w1 = r[2 * p + 1][j >> 1];
-        uint32_t lo = (j & 1) ? (w0 >> 16) : (w0 & 0xffffu);
-        uint32_t hi = (j & 1) ? (w1 & 0xffff0000u) : (w1 << 16);
-        o[p] = lo | hi;
+      for (int i = 0; i < 8; ++i) v[i] = ((ok >> (8 * b + i)) & 1) ? r[b][i] : u32x2{0, 0};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u32x4 o;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const uint32_t w0 = v[2 * p][j >> 1], w1 = v[2 * p + 1][j >> 1];
+          const uint32_t lo = (j & 1) ? (w0 >> 16) : (w0 & 0xffffu);
+          const uint32_t hi = (j & 1) ? (w1 & 0xffff0000u) : (w1 << 16);
+          o[p] = lo | hi;
+        }
+        *reinterpret_cast<u32x4*>(lds + (mb * 4 + j) * LDSK + kb * 8) = o;
       }
-      *reinterpret_cast<u32x4*>(lds + (mb * 4 + j) * LDSK + kb * 8) = o;
     }
   }
 };
 
 __device__ inline float silu_f(float a) { return a / (1.0f + expf(-a)); }
 
-template <int LAYOUT, int EPI>
-__global__ __launch_bounds__(NT) void gemm_kernel(mt_gemm_args p) {
+// Tile order.  Workgroup i of a launch goes to XCD i % 8 and each XCD has its
+// own L2, so the linear id is first regrouped per XCD (XCD x gets the x-th
+// contiguous share of the tile list), and inside a share tiles run down
+// groups of GROUP_M row tiles before moving to the next column tile, so the
+// workgroups an XCD runs at once cover a compact block of tiles and share
+// their A row-panels and B column-panels in that XCD's L2.
+constexpr int NXCD = 8, GROUP_M = 8;
+
+__device__ inline bool tile_of(int bid, int nm, int nn, int& tm, int& tn) {
+  const int total = nm * nn;
+  const int per = (total + NXCD - 1) / NXCD;
+  const int t = (bid % NXCD) * per + bid / NXCD;
+  if (t >= total) return false;
+  const int group = t / (GROUP_M * nn);
+  const int first = group * GROUP_M;
+  const int gsize = min(GROUP_M, nm - first);
+  const int r = t - group * GROUP_M * nn;
+  tm = first + r % gsize;
+  tn = r / gsize;
+  return true;
+}
+
+// BM x BN output tile per workgroup; each of the 4 waves owns a
+// (BM/2) x (BN/2) quadrant = TM x TN tiles of 32 x 32.  Larger tiles issue
+// fewer LDS fragment reads per MFMA (TM + TN reads feed TM * TN MFMAs).
+template <int LAYOUT, int EPI, int BM, int BN>
+__global__ __launch_bounds__(NT) void gemm_kernel(mt_gemm_args p, int nm, int nn) {
   constexpr bool A_T = (LAYOUT == MT_GEMM_TN);
   constexpr bool B_T = (LAYOUT != MT_GEMM_NT);
   constexpr bool SWI = (EPI == MT_EPI_SWIGLU);
+  constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
+  constexpr int HALF = BN / 2;  // SwiGLU: gate rows, then up rows
   __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDSK];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LDSK];
 
+  int tm, tn;
+  if (!tile_of(blockIdx.x, nm, nn, tm, tn)) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int64_t m0 = (int64_t)blockIdx.y * BM;
-  const int64_t n0 = (int64_t)blockIdx.x * (SWI ? BN / 2 : BN);
+  const int64_t m0 = (int64_t)tm * BM;
+  const int64_t n0 = (int64_t)tn * (SWI ? HALF : BN);
   const int64_t K = p.K;
   const uint16_t* A = p.A;
   const uint16_t* B = p.B;
 
-  RowMap ra{m0, p.M, 0};
-  RowMap rb{n0, p.N, SWI ? p.ffn : 0};
+  RowMap<BM, false> ra{m0, p.M, 0};
+  RowMap<HALF, SWI> rb{n0, p.N, SWI ? p.ffn : 0};
 
-  typename std::conditional<A_T, LoadT, LoadK>::type la;
-  typename std::conditional<B_T, LoadT, LoadK>::type lb;
+  typename std::conditional<A_T, LoadT<BM>, LoadK<BM>>::type la;
+  typename std::conditional<B_T, LoadT<BN>, LoadK<BN>>::type lb;
 
   auto load_tiles = [&](int64_t k0) {
     if constexpr (A_T) la.load(A, p.lda, m0, p.M, k0, K, tid);
@@ -140,11 +197,11 @@ __global__ __launch_bounds__(NT) void gemm_kernel(mt_gemm_args p) {
     else lb.load(B, p.ldb, rb, k0, K, tid);
   };
 
-  f32x16_t acc[2][2];
+  f32x16_t acc[TM][TN];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
@@ -154,9 +211,16 @@ __global__ __launch_bounds__(NT) void gemm_kernel(mt_gemm_args p) {
   lb.store(Bs[0], tid);
   __syncthreads();
 
-  const int arow = wm * 64 + (lane & 31);
-  const int brow0 = SWI ? (wn * 32 + (lane & 31)) : (wn * 64 + (lane & 31));
-  const int bstep = SWI ? 64 : 32;  // LDS row distance between the wave's two N sub-tiles
+  // LDS row of the wave's j-th B sub-tile: plain tiles are contiguous; in the
+  // SwiGLU product sub-tiles 0..TN/2-1 are gate columns and TN/2.. the
+  // matching up columns.
+  auto brow = [&](int j) {
+    if constexpr (SWI)
+      return (j < TN / 2) ? wn * (WN / 2) + j * 32 : HALF + wn * (WN / 2) + (j - TN / 2) * 32;
+    else
+      return wn * WN + j * 32;
+  };
+  const int arow = wm * WM + (lane & 31);
   const int kofs = (lane >> 5) * 8;
 
   for (int kt = 0; kt < nk; ++kt) {
@@ -166,14 +230,17 @@ __global__ __launch_bounds__(NT) void gemm_kernel(mt_gemm_args p) {
     const uint16_t* bs = Bs[cur];
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8_t a0 = frag(as + arow * LDSK + ks * 16 + kofs);
-      bf16x8_t a1 = frag(as + (arow + 32) * LDSK + ks * 16 + kofs);
-      bf16x8_t b0 = frag(bs + brow0 * LDSK + ks * 16 + kofs);
-      bf16x8_t b1 = frag(bs + (brow0 + bstep) * LDSK + ks * 16 + kofs);
-      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc[0][0], 0, 0, 0);
-      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc[0][1], 0, 0, 0);
-      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc[1][0], 0, 0, 0);
-      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc[1][1], 0, 0, 0);
+      bf16x8_t a[TM], b[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) a[i] = frag(as + (arow + i * 32) * LDSK + ks * 16 + kofs);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        b[j] = frag(bs + (brow(j) + (lane & 31)) * LDSK + ks * 16 + kofs);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
     if (kt + 1 < nk) {
       la.store(As[cur ^ 1], tid);
@@ -187,16 +254,18 @@ __global__ __launch_bounds__(NT) void gemm_kernel(mt_gemm_args p) {
   // col = lane%32 inside the 32x32 sub-tile (i, j).
   const int g4 = (lane >> 5) * 4;
   if constexpr (SWI) {
-    const int64_t f = n0 + wn * 32 + (lane & 31);
-    if (f < p.N) {
-      uint16_t* C = static_cast<uint16_t*>(p.C);
+    uint16_t* C = static_cast<uint16_t*>(p.C);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < TN / 2; ++j) {
+      const int64_t f = n0 + wn * (WN / 2) + j * 32 + (lane & 31);
+      if (f >= p.N) continue;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          int64_t row = m0 + wm * 64 + i * 32 + (r >> 2) * 8 + g4 + (r & 3);
+          const int64_t row = m0 + wm * WM + i * 32 + (r >> 2) * 8 + g4 + (r & 3);
           if (row < p.M) {
-            float a = acc[i][0][r], u = acc[i][1][r];
+            const float a = acc[i][j][r], u = acc[i][j + TN / 2][r];
             p.gu[row * p.ldgu + f] = f2bf(a);
             p.gu[row * p.ldgu + p.ffn + f] = f2bf(u);
             C[row * p.ldc + f] = f2bf(silu_f(a) * u);
@@ -205,16 +274,16 @@ __global__ __launch_bounds__(NT) void gemm_kernel(mt_gemm_args p) {
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t col = n0 + wn * 64 + j * 32 + (lane & 31);
+    for (int j = 0; j < TN; ++j) {
+      const int64_t col = n0 + wn * WN + j * 32 + (lane & 31);
       if (col >= p.N) continue;
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          int64_t row = m0 + wm * 64 + i * 32 + (r >> 2) * 8 + g4 + (r & 3);
+          const int64_t row = m0 + wm * WM + i * 32 + (r >> 2) * 8 + g4 + (r & 3);
           if (row >= p.M) continue;
-          float v = acc[i][j][r];
+          const float v = acc[i][j][r];
           if constexpr (EPI == MT_EPI_BF16) {
             static_cast<uint16_t*>(p.C)[row * p.ldc + col] = f2bf(v);
           } else if constexpr (EPI == MT_EPI_F32) {
@@ -224,9 +293,9 @@ __global__ __launch_bounds__(NT) void gemm_kernel(mt_gemm_args p) {
           } else if constexpr (EPI == MT_EPI_F32_ACCUM) {
             static_cast<float*>(p.C)[row * p.ldc + col] += v;
           } else if constexpr (EPI == MT_EPI_SWIGLU_BWD) {
-            float a = bf2f(p.gu[row * p.ldgu + col]);
-            float u = bf2f(p.gu[row * p.ldgu + p.ffn + col]);
-            float s = 1.0f / (1.0f + expf(-a));
+            const float a = bf2f(p.gu[row * p.ldgu + col]);
+            const float u = bf2f(p.gu[row * p.ldgu + p.ffn + col]);
+            const float s = 1.0f / (1.0f + expf(-a));
             uint16_t* C = static_cast<uint16_t*>(p.C);
             C[row * p.ldc + col] = f2bf(v * u * s * (1.0f + a * (1.0f - s)));
             C[row * p.ldc + p.ffn + col] = f2bf(v * a * s);
@@ -236,12 +305,26 @@ __global__ __launch_bounds__(NT) void gemm_kernel(mt_gemm_args p) {
   }
 }
 
+template <int LAYOUT, int EPI, int BM, int BN>
+hipError_t launch_tiles(const mt_gemm_args& a, hipStream_t s) {
+  const int nn = (int)((EPI == MT_EPI_SWIGLU) ? (a.N + BN / 2 - 1) / (BN / 2) : (a.N + BN - 1) / BN);
+  const int nm = (int)((a.M + BM - 1) / BM);
+  const int per = (nm * nn + NXCD - 1) / NXCD;
+  hipLaunchKernelGGL((gemm_kernel<LAYOUT, EPI, BM, BN>), dim3((unsigned)(per * NXCD)), dim3(NT), 0,
+                     s, a, nm, nn);
+  return hipGetLastError();
+}
+
+// 256 x 256 tiles when the product has enough of them to fill the chip,
+// 128 x 128 otherwise.
 template <int LAYOUT, int EPI>
 hipError_t launch_one(const mt_gemm_args& a, hipStream_t s) {
-  const int64_t nt = (EPI == MT_EPI_SWIGLU) ? (a.N + 63) / 64 : (a.N + BN - 1) / BN;
-  dim3 grid((unsigned)nt, (unsigned)((a.M + BM - 1) / BM));
-  hipLaunchKernelGGL((gemm_kernel<LAYOUT, EPI>), grid, dim3(NT), 0, s, a);
-  return hipGetLastError();
+  const int64_t nbig = ((a.M + 255) / 256) * ((a.N + 255) / 256);
+  // (the SwiGLU-backward epilogue does not fit the 256 x 256 register budget)
+  if constexpr (EPI != MT_EPI_SWIGLU_BWD) {
+    if (a.M >= 1024 && a.N >= 1024 && nbig >= 128) return launch_tiles<LAYOUT, EPI, 256, 256>(a, s);
+  }
+  return launch_tiles<LAYOUT, EPI, 128, 128>(a, s);
 }
 
 }  // namespace
@@ -252,7 +335,7 @@ bool gemm_shape_ok(const mt_gemm_args& a, const char** why) {
   if (a.epilogue < 0 || a.epilogue > 5) return bad("epilogue");
   if (a.M <= 0 || a.N <= 0 || a.K <= 0) return bad("empty or negative dimension");
   if (a.M % 8 || a.N % 8 || a.K % 8) return bad("M, N, K must be multiples of 8");
-  if (a.M / 128 >= 65535) return bad("M too large");
+  if ((a.M / 128 + 1) * (a.N / 64 + 1) >= (1LL << 31)) return bad("too many tiles");
   if (!a.A || !a.B || !a.C) return bad("null operand");
   if (a.lda % 8 || a.ldb % 8) return bad("lda/ldb must be multiples of 8");
   const bool at = a.layout == MT_GEMM_TN, bt = a.layout != MT_GEMM_NT;
