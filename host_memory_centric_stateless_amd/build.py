@@ -27,7 +27,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           f"-I{os.path.join(ROOT, 'include')}"]
 DEVICE = [f"--offload-arch={ARCH}", "-mcode-object-version=5",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-HOST = ["-ffp-contract=off", "-march=x86-64-v3", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include"]
+HOST = ["-ffp-contract=off", "-fno-math-errno", "-march=x86-64-v3", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include"]
 
 
 def hipcc() -> str:

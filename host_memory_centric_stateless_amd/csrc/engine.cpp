@@ -137,6 +137,9 @@ struct mt_ctx {
 
   std::unique_ptr<ThreadPool> pool;
   std::unique_ptr<ThreadPool> opt_pool;  // optimizer work, separate from slab draining
+  // Caller-thread work (embedding gather): its own few threads, so that the
+  // next micro-batch's input is never queued behind gradient accumulation.
+  std::unique_ptr<ThreadPool> io_pool;
   std::thread opt_worker;
   std::deque<Job> opt_jobs;
   std::condition_variable opt_cv;
@@ -946,6 +949,7 @@ extern "C" mt_status mt_create(const mt_config* cfg, const mt_device_arena* a, m
 
   c->pool.reset(new ThreadPool(cfg->host_threads > 0 ? cfg->host_threads : default_threads()));
   c->opt_pool.reset(new ThreadPool(cfg->host_threads > 0 ? cfg->host_threads : default_threads()));
+  c->io_pool.reset(new ThreadPool(4));
   if (const char* d = getenv("MT_TEST_WORKER_DELAY_US")) c->delay_us = atoi(d);
   for (int i = c->nslab - 1; i >= 0; --i) c->free_slabs.push_back(i);
   c->worker = std::thread(worker_main, c.get());
@@ -1070,7 +1074,7 @@ extern "C" mt_status mt_forward(mt_ctx* c, const int32_t* tokens, const int32_t*
   const int par = c->parity;
   // staging of two micro-batches ago must have reached the device
   if (c->x0_used[par]) MT_HIP(c, hipEventSynchronize(c->ev_x0[par]));
-  embed_gather(*c->pool, c->embed.master, tokens, T, h, c->x0_stage[par]);
+  embed_gather(*c->io_pool, c->embed.master, tokens, T, h, c->x0_stage[par]);
   memcpy(c->lab_stage[par], labels, (size_t)T * 4);
   c->tok_cur.assign(tokens, tokens + T);
   // the device copies of x0 / labels of two micro-batches ago are free once

@@ -78,12 +78,14 @@ int default_threads() {
   return std::max(1, std::min(n, 16));
 }
 
+// Round to nearest even; NaN stays a (quiet) NaN.  Branch-free so that the
+// loops calling it vectorise.
 static inline uint16_t rne_bf16(float f) {
   uint32_t u;
   memcpy(&u, &f, 4);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  const uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t q = (u >> 16) | 0x40u;
+  return (uint16_t)(((u & 0x7fffffffu) > 0x7f800000u) ? q : r);
 }
 
 static constexpr int64_t kChunk = 1 << 18;  // elements per task
@@ -99,44 +101,72 @@ static void chunked(ThreadPool& pool, int64_t n, F&& f) {
 
 void cast_bf16(ThreadPool& pool, const float* src, uint16_t* dst, int64_t n) {
   chunked(pool, n, [&](int64_t b, int64_t e) {
-    for (int64_t i = b; i < e; ++i) dst[i] = rne_bf16(src[i]);
+    const float* __restrict s = src;
+    uint16_t* __restrict d = dst;
+    for (int64_t i = b; i < e; ++i) d[i] = rne_bf16(s[i]);
   });
 }
 
+namespace {
+// fp32 AdamW coefficients, formed in double from the exact hyper-parameters.
+struct AdamCoef {
+  float decay, b1, b2, c1, c2, bc1, bc2, lr, eps;
+  AdamCoef(const mt_adamw_hparams& hp, int64_t step)
+      : decay((float)(1.0 - hp.lr * hp.weight_decay)),
+        b1((float)hp.beta1),
+        b2((float)hp.beta2),
+        c1((float)(1.0 - hp.beta1)),
+        c2((float)(1.0 - hp.beta2)),
+        bc1((float)(1.0 - pow(hp.beta1, (double)step))),
+        bc2((float)(1.0 - pow(hp.beta2, (double)step))),
+        lr((float)hp.lr),
+        eps((float)hp.eps) {}
+};
+
+// One element of the update, in the order of the per-element definition:
+// decay, first and second moments, bias-corrected step.  Every operation is a
+// separately rounded fp32 operation (built with contraction off).
+template <bool BF>
+inline void adam_range(const AdamCoef& k, float* __restrict p, const float* __restrict g,
+                       float* __restrict m, float* __restrict v, uint16_t* __restrict bf,
+                       int64_t b, int64_t e) {
+  for (int64_t i = b; i < e; ++i) {
+    const float gi = g[i];
+    float pi = p[i] * k.decay;
+    float mi = m[i] * k.b1;
+    mi = mi + k.c1 * gi;
+    float vi = v[i] * k.b2;
+    vi = vi + k.c2 * (gi * gi);
+    const float mh = mi / k.bc1;
+    const float vh = vi / k.bc2;
+    pi = pi - (k.lr * mh) / (sqrtf(vh) + k.eps);
+    p[i] = pi;
+    m[i] = mi;
+    v[i] = vi;
+    if (BF) bf[i] = rne_bf16(pi);
+  }
+}
+}  // namespace
+
 void adamw(ThreadPool& pool, float* p, const float* g, float* m, float* v, uint16_t* bf, int64_t n,
            const mt_adamw_hparams& hp, int64_t step) {
-  // Coefficients formed in double, used in fp32 (as a float32 array op would).
-  const float decay = (float)(1.0 - hp.lr * hp.weight_decay);
-  const float b1 = (float)hp.beta1, b2 = (float)hp.beta2;
-  const float c1 = (float)(1.0 - hp.beta1), c2 = (float)(1.0 - hp.beta2);
-  const float bc1 = (float)(1.0 - pow(hp.beta1, (double)step));
-  const float bc2 = (float)(1.0 - pow(hp.beta2, (double)step));
-  const float lr = (float)hp.lr, eps = (float)hp.eps;
+  const AdamCoef k(hp, step);
   chunked(pool, n, [&](int64_t b, int64_t e) {
-    for (int64_t i = b; i < e; ++i) {
-      const float gi = g[i];
-      float pi = p[i] * decay;
-      float mi = m[i] * b1;
-      mi = mi + c1 * gi;
-      float vi = v[i] * b2;
-      vi = vi + c2 * (gi * gi);
-      const float mh = mi / bc1;
-      const float vh = vi / bc2;
-      pi = pi - (lr * mh) / (sqrtf(vh) + eps);
-      p[i] = pi;
-      m[i] = mi;
-      v[i] = vi;
-      if (bf) bf[i] = rne_bf16(pi);
-    }
+    if (bf)
+      adam_range<true>(k, p, g, m, v, bf, b, e);
+    else
+      adam_range<false>(k, p, g, m, v, nullptr, b, e);
   });
 }
 
 void accumulate(ThreadPool& pool, float* grad, const float* src, int64_t n, bool add) {
   chunked(pool, n, [&](int64_t b, int64_t e) {
+    float* __restrict d = grad;
+    const float* __restrict s = src;
     if (add) {
-      for (int64_t i = b; i < e; ++i) grad[i] += src[i];
+      for (int64_t i = b; i < e; ++i) d[i] += s[i];
     } else {
-      memcpy(grad + b, src + b, (size_t)(e - b) * sizeof(float));
+      memcpy(d + b, s + b, (size_t)(e - b) * sizeof(float));
     }
   });
 }
@@ -150,10 +180,12 @@ static inline float bf16_to_f32(uint16_t h) {
 
 void accumulate_bf16(ThreadPool& pool, float* grad, const uint16_t* src, int64_t n, bool add) {
   chunked(pool, n, [&](int64_t b, int64_t e) {
+    float* __restrict d = grad;
+    const uint16_t* __restrict s = src;
     if (add) {
-      for (int64_t i = b; i < e; ++i) grad[i] += bf16_to_f32(src[i]);
+      for (int64_t i = b; i < e; ++i) d[i] += bf16_to_f32(s[i]);
     } else {
-      for (int64_t i = b; i < e; ++i) grad[i] = bf16_to_f32(src[i]);
+      for (int64_t i = b; i < e; ++i) d[i] = bf16_to_f32(s[i]);
     }
   });
 }
@@ -173,8 +205,8 @@ void embed_scatter(ThreadPool& pool, float* demb, const int32_t* tok, int64_t T,
   pool.run((h + cols - 1) / cols, [&](int64_t k) {
     const int64_t c0 = k * cols, c1 = std::min(h, c0 + cols);
     for (int64_t t = 0; t < T; ++t) {
-      float* dst = demb + (int64_t)tok[t] * h;
-      const float* s = dx0 + t * h;
+      float* __restrict dst = demb + (int64_t)tok[t] * h;
+      const float* __restrict s = dx0 + t * h;
       for (int64_t c = c0; c < c1; ++c) dst[c] += s[c];
     }
   });

@@ -6,8 +6,9 @@ Reads <prefix>_kernel_trace.csv and <prefix>_memory_copy_trace.csv (rocprofv3
 --kernel-trace --memory-copy-trace --output-format csv) and prints:
 
 * per-kernel total / average duration and share of kernel time;
-* busy time (union of intervals) of kernels, host->device copies and
-  device->host copies;
+* busy time (union of intervals) of compute kernels, host->device copies and
+  device->host traffic (DMA copies plus the gradient drain, which is a copy
+  kernel writing pinned host memory and so appears in the kernel trace);
 * copy/compute overlap = |copies AND kernels| / min(|copies|, |kernels|)
   (union measure), for H2D, D2H and both;
 * large-copy durations (copies longer than 1 ms).
@@ -23,6 +24,7 @@ from collections import defaultdict
 from typing import List, Tuple
 
 Interval = Tuple[int, int]
+DRAIN = "copy16_kernel"  # gradient slab -> pinned host copy kernel
 
 
 def _read(path):
@@ -67,10 +69,12 @@ def summarize(prefix: str, t0: int = None, t1: int = None) -> str:
     kt = _read(prefix + "_kernel_trace.csv")
     mc = _read(prefix + "_memory_copy_trace.csv")
     kern = [(int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]) for r in kt]
+    drain = [(a, b) for a, b, n in kern if DRAIN in n]
+    kern = [k for k in kern if DRAIN not in k[2]]
     h2d = [(int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in mc
            if r["Direction"].endswith("HOST_TO_DEVICE")]
     d2h = [(int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in mc
-           if r["Direction"].endswith("DEVICE_TO_HOST")]
+           if r["Direction"].endswith("DEVICE_TO_HOST")] + drain
     lo = t0 if t0 is not None else min([k[0] for k in kern] + [c[0] for c in h2d + d2h])
     hi = t1 if t1 is not None else max([k[1] for k in kern] + [c[1] for c in h2d + d2h])
     kern = [(max(a, lo), min(b, hi), n) for a, b, n in kern if b > lo and a < hi]
@@ -87,7 +91,8 @@ def summarize(prefix: str, t0: int = None, t1: int = None) -> str:
     lines = [f"window: {(hi - lo) / 1e9:.3f} s",
              f"kernel busy (union): {measure(K) / 1e9:.3f} s  ({100 * measure(K) / (hi - lo):.1f}% of window)",
              f"H2D busy (union):    {measure(H) / 1e9:.3f} s  ({len(h2d)} copies)",
-             f"D2H busy (union):    {measure(D) / 1e9:.3f} s  ({len(d2h)} copies)",
+             f"D2H busy (union):    {measure(D) / 1e9:.3f} s  ({len(d2h)} copies, "
+             f"{len(drain)} of them drain kernels)",
              f"any copy busy:       {measure(C) / 1e9:.3f} s"]
     for name, X in (("H2D", H), ("D2H", D), ("any copy", C)):
         if measure(X) and measure(K):
@@ -98,6 +103,9 @@ def summarize(prefix: str, t0: int = None, t1: int = None) -> str:
         if big:
             lines.append(f"{name} copies > 1 ms: n={len(big)} mean {sum(big) / len(big) / 1e6:.2f} ms "
                          f"min {min(big) / 1e6:.2f} max {max(big) / 1e6:.2f}")
+    if drain:
+        dt = sum(b - a for a, b in clip(drain, lo, hi))
+        lines.append(f"drain kernels: n={len(drain)} total {dt / 1e6:.1f} ms")
     lines.append("")
     lines.append(f"{'kernel':70s} {'calls':>6s} {'total ms':>10s} {'avg us':>10s} {'share':>6s}")
     for n, (c, t) in sorted(per.items(), key=lambda kv: -kv[1][1]):
