@@ -227,6 +227,28 @@ def cpu_baseline(cfg, budget_s: float = 30.0):
                       f"{T / dt / cfg.n_layers:.1f}"}
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_tn_bf16_7b_shape_traffic.txt")
+
+
+def measured_traffic(kernel: str, cfg_name: str, default_shape: bool):
+    """HBM bytes per launch of the TN weight-gradient GEMM from the committed
+    FETCH_SIZE / WRITE_SIZE counter runs (calibrated), or None when the
+    counters do not describe this kernel, workload or kernel source."""
+    import hashlib
+    if kernel != "gemm_tn_bf16" or cfg_name != "llama-7B-shape" or not default_shape:
+        return None
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    fields = dict(l.split(": ", 1) for l in text.splitlines() if ": " in l and not l.startswith(" "))
+    src = os.path.join(ROOT, "host_memory_centric_stateless_amd", "csrc", "gemm.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if fields.get("gemm_source_sha256", "").strip() != sha:
+        return None
+    return float(fields["traffic_bytes_per_launch"])
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -235,6 +257,10 @@ def main():
     ap.add_argument("--config", default="C3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--host-threads", type=int, default=0)
+    ap.add_argument("--micro-batch", type=int, default=0,
+                    help="override the configuration's sequences per micro-batch")
+    ap.add_argument("--grad-accum", type=int, default=0,
+                    help="override the configuration's micro-batches per step")
     ap.add_argument("--probe", action="store_true",
                     help="only run each block GEMM at this shape and a calibration copy")
     args = ap.parse_args()
@@ -248,6 +274,9 @@ def main():
     from synth_inputs import PRESETS, make_batch, weight_stream
 
     cfg = PRESETS[args.config]
+    if args.micro_batch or args.grad_accum:
+        cfg = cfg.replace(micro_batch=args.micro_batch or cfg.micro_batch,
+                          grad_accum=args.grad_accum or cfg.grad_accum)
     if args.probe:
         for row in probe(cfg):
             print(json.dumps(row), flush=True)
@@ -309,10 +338,13 @@ def main():
         ach = dom["bytes"] / (dom["ms"] * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": ach / HBM_PEAK_GBPS}
-    roofline.update({"traffic": None, "kernel": dom["name"], "launches": dom["launches"],
+    traffic = measured_traffic(dom["name"], cfg.name, not (args.micro_batch or args.grad_accum))
+    roofline.update({"traffic": traffic, "kernel": dom["name"], "launches": dom["launches"],
                      "avg_launch_ms": dom["ms"] / dom["launches"],
                      "algorithmic_per_launch": (dom["flop"] or dom["bytes"]) / dom["launches"],
-                     "measured": "HIP events around each launch on its stream, timed steps"})
+                     "measured": "HIP events around each launch on its stream, timed steps",
+                     "traffic_unit": "HBM bytes per launch (FETCH_SIZE x 2 + WRITE_SIZE, "
+                                     "calibrated on a 1 GiB copy)" if traffic else None})
     sess.close()
     base = None if args.no_cpu_baseline else cpu_baseline(cfg)
 
