@@ -30,7 +30,7 @@ sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
-KERNEL_COPY_WGS = (8, 32)
+KERNEL_COPY_WGS = (4, 8, 32)
 
 
 def model_flops_per_token(cfg) -> float:
@@ -257,6 +257,9 @@ def main():
     ap.add_argument("--config", default="C3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--host-threads", type=int, default=0)
+    ap.add_argument("--drain-workgroups", type=int, default=None,
+                    help="slab drain: 0 = DMA engine, n = copy kernel of n workgroups "
+                         "(default: the library's)")
     ap.add_argument("--micro-batch", type=int, default=0,
                     help="override the configuration's sequences per micro-batch")
     ap.add_argument("--grad-accum", type=int, default=0,
@@ -282,7 +285,7 @@ def main():
             print(json.dumps(row), flush=True)
         return
     t0 = time.perf_counter()
-    sess = Session(cfg, host_threads=args.host_threads)
+    sess = Session(cfg, host_threads=args.host_threads, drain_workgroups=args.drain_workgroups)
     sess.load_weights(weight_stream(cfg, 0))
     print(f"[bench] {cfg.name}: init {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
 
@@ -359,6 +362,8 @@ def main():
                    "grad_accum": cfg.grad_accum, "ckpt_interval": cfg.ckpt_interval,
                    "grad_slabs": cfg.n_grad_slabs, "global_batch_tokens": tokens_per_step},
         "tokens_per_s": tok_s, "hardware_tflops": hw_tflops,
+        "slab_drain": ("dma" if sess.c.drain_workgroups == 0
+                       else f"copy kernel, {sess.c.drain_workgroups} workgroups"),
         "mfma_frac_end_to_end": model_tflops / MFMA_BF16_PEAK_TFLOPS,
         "h2d_GBps": h2d, "d2h_GBps": d2h, "adamw_s_per_step": adamw_s,
         "loss_last": losses[-1],

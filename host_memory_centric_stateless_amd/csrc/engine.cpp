@@ -78,13 +78,13 @@ struct Job {
 
 enum State { ST_UNBOUND, ST_IDLE, ST_FWD, ST_BWD, ST_FLUSHED };
 
-// Gradients drain to pinned host memory through a small copy kernel rather
-// than the copy engine.  Measured on the MI355X host link (810 MB slabs): two
-// engine copies in opposite directions leave device->host at ~28 GB/s
-// (~13 GB/s under the streaming load), while 8 copy workgroups keep ~41 GB/s
-// device->host next to ~52 GB/s host->device.  With 12 or more workgroups the
-// first GEMM launched beside the copy stalls for 4-10 ms, with 8 it does not.
-constexpr int kDrainWorkgroups = 8;
+// Slabs leave the device either by the DMA engine or by a copy kernel that
+// writes the pinned host slab (mt_config.drain_workgroups).  Measured on the
+// MI355X host link with 405 MB slabs: DMA copies in both directions at once
+// give ~28 GB/s device->host beside ~57 GB/s host->device; an 8-workgroup copy
+// kernel keeps ~41 GB/s device->host, but kernels running beside it take 2-4x
+// longer (the CUs that hold a copy workgroup stall on its host-memory stores,
+// and every tile scheduled on them finishes late).
 
 double now_s() {
   return std::chrono::duration<double>(std::chrono::steady_clock::now().time_since_epoch())
@@ -574,6 +574,14 @@ int acquire_slab(mt_ctx* c) {
   return s;
 }
 
+// Device -> pinned host copy on the offload stream, by the DMA engine or by
+// a copy kernel (mt_config.drain_workgroups).
+hipError_t drain(mt_ctx* c, void* host, const void* dev, size_t bytes) {
+  const int wgs = c->p.c.drain_workgroups;
+  if (wgs == 0) return hipMemcpyAsync(host, dev, bytes, hipMemcpyDeviceToHost, c->so);
+  return launch_copy(host, dev, bytes, wgs, c->so);
+}
+
 // Gradient of a unit is complete in device slab s: copy it out and hand it to
 // the worker.
 mt_status offload_slab(mt_ctx* c, int s, int group, int64_t e0, int64_t n, int unit) {
@@ -582,7 +590,7 @@ mt_status offload_slab(mt_ctx* c, int s, int group, int64_t e0, int64_t n, int u
   const size_t bytes = (size_t)n * (c->p.slab_bf16 ? 2 : 4);
   {
     KScope k(c, c->so, "drain_d2h", 0, (double)bytes);
-    MT_HIP(c, launch_copy(c->hslab[s], c->dslab[s], bytes, kDrainWorkgroups, c->so));
+    MT_HIP(c, drain(c, c->hslab[s], c->dslab[s], bytes));
   }
   MT_HIP(c, hipEventRecord(c->ev_copied[s], c->so));
   c->st.d2h_bytes += (int64_t)bytes;
@@ -813,7 +821,7 @@ mt_status run_step(mt_ctx* c, const Step& s) {
       float* dx0 = c->wsp<float>(c->dy_idx ? p.ws.dy1 : p.ws.dy0);
       MT_HIP(c, hipEventRecord(c->ev_dx0[par], cs));
       MT_HIP(c, hipStreamWaitEvent(c->so, c->ev_dx0[par], 0));
-      MT_HIP(c, launch_copy(c->dx0_stage[par], dx0, (size_t)T * h * 4, kDrainWorkgroups, c->so));
+      MT_HIP(c, drain(c, c->dx0_stage[par], dx0, (size_t)T * h * 4));
       MT_HIP(c, hipEventRecord(c->ev_dx0_copied[par], c->so));
       c->st.d2h_bytes += T * h * 4;
       Job j;

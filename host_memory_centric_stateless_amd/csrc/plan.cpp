@@ -44,6 +44,7 @@ std::string make_plan(const mt_config& c, Plan* p) {
   if (!(c.rms_eps >= 0.0f) || !(c.rope_base > 1.0f)) return "rms_eps / rope_base";
   if (c.host_threads < 0) return "host_threads must be >= 0";
   if (c.slab_bf16 != 0 && c.slab_bf16 != 1) return "slab_bf16 must be 0 or 1";
+  if (c.drain_workgroups < 0 || c.drain_workgroups > 256) return "drain_workgroups must be in 0..256";
 
   p->c = c;
   const int64_t h = c.hidden, F = c.ffn, V = c.vocab;

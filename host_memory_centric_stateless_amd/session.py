@@ -12,7 +12,7 @@ from typing import Dict, Iterable, Optional, Tuple
 import numpy as np
 import torch
 
-from . import (MT_GROUP_EMBED, MT_GROUP_HEAD, make_config, mt_adamw_hparams, mt_adamw_step,
+from . import (DEFAULT_DRAIN_WORKGROUPS, MT_GROUP_EMBED, MT_GROUP_HEAD, make_config, mt_adamw_hparams, mt_adamw_step,
                mt_backward, mt_backward_step, mt_bind_layer, mt_create, mt_destroy, mt_device_arena,
                mt_device_requirements, mt_flush_grads, mt_forward, mt_get_stats, mt_layout)
 
@@ -27,13 +27,15 @@ def aligned_zeros(n: int, align: int = 64) -> np.ndarray:
 class Session:
     def __init__(self, cfg, host_threads: int = 0, device: str = "cuda:0",
                  ckpt_interval: Optional[int] = None, n_grad_slabs: Optional[int] = None,
-                 slab_bf16: bool = True):
+                 slab_bf16: bool = True, drain_workgroups: Optional[int] = None):
         if ckpt_interval is not None:
             cfg = cfg.replace(ckpt_interval=ckpt_interval)
         if n_grad_slabs is not None:
             cfg = cfg.replace(n_grad_slabs=n_grad_slabs)
         self.cfg = cfg
-        self.c = make_config(cfg, host_threads, slab_bf16)
+        self.c = make_config(cfg, host_threads, slab_bf16,
+                             DEFAULT_DRAIN_WORKGROUPS if drain_workgroups is None
+                             else drain_workgroups)
         self.req = mt_device_requirements(self.c)
         self.groups = [MT_GROUP_EMBED] + list(range(cfg.n_layers)) + [MT_GROUP_HEAD]
         self.layout: Dict[int, Tuple[list, int]] = {g: mt_layout(self.c, g) for g in self.groups}

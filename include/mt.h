@@ -71,6 +71,10 @@ typedef struct mt_config {
   int32_t slab_bf16;      /* 1: gradient slabs carry bf16 (half the device->host
                              bytes; rounded once per micro-batch, accumulated in
                              fp32 on the host); 0: fp32 slabs                   */
+  int32_t drain_workgroups; /* device->host copy of each slab: 0 = the DMA
+                             engine (hipMemcpyAsync on the offload stream);
+                             n in 1..256 = a copy kernel of n workgroups that
+                             writes the pinned host slab directly            */
 } mt_config;
 
 /* One tensor of a group's flat layout. */

@@ -150,7 +150,7 @@ def test_pipeline_invariants_bit_exact():
     cfg = PRESETS["C1"].replace(grad_accum=2)
     base_loss, base, _ = _grads_after_one_step(cfg, ckpt_interval=1)
     for kw in ({"ckpt_interval": 2}, {"n_grad_slabs": 1}, {"n_grad_slabs": 2},
-               {"host_threads": 3}):
+               {"host_threads": 3}, {"drain_workgroups": 0}, {"drain_workgroups": 8}):
         print("variant", kw, flush=True)
         loss, g, stats = _grads_after_one_step(cfg, **kw)
         assert loss == base_loss, kw
