@@ -223,30 +223,77 @@ __global__ __launch_bounds__(NT) void gemm_kernel(mt_gemm_args p, int nm, int nn
   const int arow = wm * WM + (lane & 31);
   const int kofs = (lane >> 5) * 8;
 
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) load_tiles((int64_t)(kt + 1) * BK);
-    const uint16_t* as = As[cur];
-    const uint16_t* bs = Bs[cur];
+  // MFMA operands are double-buffered in registers: the fragments of k-step
+  // s+1 are read from LDS while the MFMAs of k-step s run.  The last k-step
+  // of a tile runs after the barrier, under the reads of the next tile's
+  // first fragments, so the matrix cores never wait on LDS at a tile edge.
+  bf16x8_t fa[2][TM], fb[2][TN];
+  auto read_frags = [&](const uint16_t* as, const uint16_t* bs, int ks, int slot) {
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8_t a[TM], b[TN];
+    for (int i = 0; i < TM; ++i) fa[slot][i] = frag(as + (arow + i * 32) * LDSK + ks * 16 + kofs);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) a[i] = frag(as + (arow + i * 32) * LDSK + ks * 16 + kofs);
+    for (int j = 0; j < TN; ++j)
+      fb[slot][j] = frag(bs + (brow(j) + (lane & 31)) * LDSK + ks * 16 + kofs);
+  };
+  auto mfmas = [&](int slot) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        b[j] = frag(bs + (brow(j) + (lane & 31)) * LDSK + ks * 16 + kofs);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j], acc[i][j], 0,
+                                                            0, 0);
+  };
+  constexpr int KS = BK / 16;  // k-steps per tile (even, so slots alternate 0,1,0,1)
+  static_assert(KS % 2 == 0, "k-steps per tile must be even");
+
+  read_frags(As[0], Bs[0], 0, 0);
+  if constexpr (!A_T) {
+    // NT / NN: the loop body has no branches, so that each half of it is one
+    // scheduling region (in the last iteration the loads fall past K; every
+    // vector is masked, so zeros go to the idle LDS buffer and are never
+    // read).  Scheduling barriers keep the next tile's global loads ahead of
+    // the MFMAs, where three k-steps hide their latency, and the LDS stores
+    // after them.
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      load_tiles((int64_t)(kt + 1) * BK);
+      __builtin_amdgcn_sched_barrier(0);
+      const uint16_t* as = As[cur];
+      const uint16_t* bs = Bs[cur];
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) {
+      for (int ks = 0; ks < KS - 1; ++ks) {
+        read_frags(as, bs, ks + 1, (ks + 1) & 1);
+        mfmas(ks & 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
       la.store(As[cur ^ 1], tid);
       lb.store(Bs[cur ^ 1], tid);
+      __syncthreads();
+      read_frags(As[cur ^ 1], Bs[cur ^ 1], 0, 0);
+      mfmas((KS - 1) & 1);
     }
-    __syncthreads();
+  } else {
+    // TN (both operands transposed in registers): left to the compiler's
+    // schedule, which spreads the transposes among the MFMAs.
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      const bool more = kt + 1 < nk;
+      if (more) load_tiles((int64_t)(kt + 1) * BK);
+      const uint16_t* as = As[cur];
+      const uint16_t* bs = Bs[cur];
+#pragma unroll
+      for (int ks = 0; ks < KS - 1; ++ks) {
+        read_frags(as, bs, ks + 1, (ks + 1) & 1);
+        mfmas(ks & 1);
+      }
+      if (more) {
+        la.store(As[cur ^ 1], tid);
+        lb.store(Bs[cur ^ 1], tid);
+      }
+      __syncthreads();
+      if (more) read_frags(As[cur ^ 1], Bs[cur ^ 1], 0, 0);
+      mfmas((KS - 1) & 1);
+    }
   }
 
   // ------------------------------------------------------------ epilogue
