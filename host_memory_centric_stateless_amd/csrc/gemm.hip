@@ -85,56 +85,63 @@ struct LoadK {
   }
 };
 
-// Operand stored [k][row] (row contiguous): 64 k x R rows, cut into 8 (k) x
-// 4 (row) blocks; each thread reads R/128 blocks with 8-byte loads and writes
-// them transposed as 16-byte LDS rows (zeroing out-of-range parts there).
+// Operand stored [k][row] (row contiguous): the 64 (k) x R (row) tile is
+// copied unchanged into a k-major LDS tile of pitch PT with 16-byte vectors;
+// MFMA fragments are then taken from it with LDS transpose reads (frag_t).
+// The pitch is R + 32 elements (64 bytes past a multiple of 256): the four
+// k-rows that one transpose read touches fall on disjoint banks.
 template <int R>
-struct LoadT {
-  static constexpr int NB = 2 * R / NT, RB = R / 4;
-  u32x2 r[NB][8];
-  uint32_t ok = 0;  // bit 8b+i: row i of block b is inside the matrix
+struct LoadKT {
+  static constexpr int PT = R + 32;
+  static constexpr int VPR = R / 8;          // 16-byte vectors per k-row
+  static constexpr int V = 64 * VPR / NT;    // vectors per thread
+  static constexpr int LDS_ELEMS = 64 * PT;
+  u32x4 r[V];
+  uint32_t ok = 0;  // bit i: vector i is inside the matrix
+  // nrows is a multiple of 8, so a vector is wholly inside or outside.
   __device__ inline void load(const uint16_t* base, int64_t ld, int64_t row0, int64_t nrows,
                               int64_t k0, int64_t K, int tid) {
     ok = 0;
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const int blk = tid + NT * b;
-      const int kb = blk / RB, mb = blk % RB;
-      const int64_t g = row0 + mb * 4;
-      const bool gin = g < nrows;
-      const int64_t gc = gin ? g : 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int64_t k = k0 + kb * 8 + i;
-        const bool in = gin && k < K;
-        ok |= (uint32_t)in << (8 * b + i);
-        r[b][i] = *reinterpret_cast<const u32x2*>(base + (in ? k : 0) * ld + gc);
-      }
+    for (int i = 0; i < V; ++i) {
+      const int idx = tid + NT * i;
+      const int64_t k = k0 + idx / VPR;
+      const int64_t row = row0 + (idx % VPR) * 8;
+      const bool in = k < K && row < nrows;
+      ok |= (uint32_t)in << i;
+      r[i] = *reinterpret_cast<const u32x4*>(base + (in ? k * ld + row : 0));
     }
   }
   __device__ inline void store(uint16_t* lds, int tid) const {
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const int blk = tid + NT * b;
-      const int kb = blk / RB, mb = blk % RB;
-      u32x2 v[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = ((ok >> (8 * b + i)) & 1) ? r[b][i] : u32x2{0, 0};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        u32x4 o;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const uint32_t w0 = v[2 * p][j >> 1], w1 = v[2 * p + 1][j >> 1];
-          const uint32_t lo = (j & 1) ? (w0 >> 16) : (w0 & 0xffffu);
-          const uint32_t hi = (j & 1) ? (w1 & 0xffff0000u) : (w1 << 16);
-          o[p] = lo | hi;
-        }
-        *reinterpret_cast<u32x4*>(lds + (mb * 4 + j) * LDSK + kb * 8) = o;
-      }
+    for (int i = 0; i < V; ++i) {
+      const int idx = tid + NT * i;
+      *reinterpret_cast<u32x4*>(lds + (idx / VPR) * PT + (idx % VPR) * 8) =
+          ((ok >> i) & 1) ? r[i] : u32x4{0, 0, 0, 0};
     }
   }
 };
+
+// MFMA fragment (rows row_base..+31, k-step ks) from a k-major LDS tile.  One
+// ds_read_b64_tr_b16 over a 16-lane group returns, to lane i, element i%4 of
+// the 8-byte chunks addressed by lanes i/4, i/4+4, i/4+8, i/4+12.  Lane s of
+// the group addresses k-row kb + s/4 at row offset r0 + 4*(s%4), so lane i
+// receives row r0 + i at k-rows kb..kb+3; a second read at kb+4 completes the
+// eight k values of the 32x32x16 operand layout (row = lane%32,
+// k = 8*(lane/32) + 0..7).
+__device__ inline bf16x8_t frag_t(const uint16_t* lds, int pitch, int row_base, int ks,
+                                  int lane) {
+  typedef short s4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s4 lds_s4;
+  const int g = lane >> 4, sl = lane & 15;
+  const int k = ks * 16 + 8 * (g >> 1) + (sl >> 2);
+  const int row = row_base + 16 * (g & 1) + 4 * (sl & 3);
+  const uint16_t* q = lds + k * pitch + row;
+  const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)q);
+  const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(q + 4 * pitch));
+  const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+  return __builtin_bit_cast(bf16x8_t, u32x4{a[0], a[1], b[0], b[1]});
+}
 
 __device__ inline float silu_f(float a) { return a / (1.0f + expf(-a)); }
 
@@ -168,10 +175,13 @@ __global__ __launch_bounds__(NT) void gemm_kernel(mt_gemm_args p, int nm, int nn
   constexpr bool A_T = (LAYOUT == MT_GEMM_TN);
   constexpr bool B_T = (LAYOUT != MT_GEMM_NT);
   constexpr bool SWI = (EPI == MT_EPI_SWIGLU);
+  static_assert(!(SWI && B_T), "the SwiGLU product takes B as [rows][k]");
   constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
   constexpr int HALF = BN / 2;  // SwiGLU: gate rows, then up rows
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDSK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LDSK];
+  constexpr int SA = A_T ? LoadKT<BM>::LDS_ELEMS : BM * LDSK;
+  constexpr int SB = B_T ? LoadKT<BN>::LDS_ELEMS : BN * LDSK;
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][SA];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][SB];
 
   int tm, tn;
   if (!tile_of(blockIdx.x, nm, nn, tm, tn)) return;
@@ -187,8 +197,8 @@ __global__ __launch_bounds__(NT) void gemm_kernel(mt_gemm_args p, int nm, int nn
   RowMap<BM, false> ra{m0, p.M, 0};
   RowMap<HALF, SWI> rb{n0, p.N, SWI ? p.ffn : 0};
 
-  typename std::conditional<A_T, LoadT<BM>, LoadK<BM>>::type la;
-  typename std::conditional<B_T, LoadT<BN>, LoadK<BN>>::type lb;
+  typename std::conditional<A_T, LoadKT<BM>, LoadK<BM>>::type la;
+  typename std::conditional<B_T, LoadKT<BN>, LoadK<BN>>::type lb;
 
   auto load_tiles = [&](int64_t k0) {
     if constexpr (A_T) la.load(A, p.lda, m0, p.M, k0, K, tid);
@@ -230,10 +240,19 @@ __global__ __launch_bounds__(NT) void gemm_kernel(mt_gemm_args p, int nm, int nn
   bf16x8_t fa[2][TM], fb[2][TN];
   auto read_frags = [&](const uint16_t* as, const uint16_t* bs, int ks, int slot) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i) fa[slot][i] = frag(as + (arow + i * 32) * LDSK + ks * 16 + kofs);
+    for (int i = 0; i < TM; ++i) {
+      if constexpr (A_T)
+        fa[slot][i] = frag_t(as, LoadKT<BM>::PT, wm * WM + i * 32, ks, lane);
+      else
+        fa[slot][i] = frag(as + (arow + i * 32) * LDSK + ks * 16 + kofs);
+    }
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
-      fb[slot][j] = frag(bs + (brow(j) + (lane & 31)) * LDSK + ks * 16 + kofs);
+    for (int j = 0; j < TN; ++j) {
+      if constexpr (B_T)
+        fb[slot][j] = frag_t(bs, LoadKT<BN>::PT, wn * WN + j * 32, ks, lane);
+      else
+        fb[slot][j] = frag(bs + (brow(j) + (lane & 31)) * LDSK + ks * 16 + kofs);
+    }
   };
   auto mfmas = [&](int slot) {
 #pragma unroll
@@ -246,54 +265,29 @@ __global__ __launch_bounds__(NT) void gemm_kernel(mt_gemm_args p, int nm, int nn
   constexpr int KS = BK / 16;  // k-steps per tile (even, so slots alternate 0,1,0,1)
   static_assert(KS % 2 == 0, "k-steps per tile must be even");
 
+  // The loop body has no branches, so that each half of it is one scheduling
+  // region (in the last iteration the loads fall past K; every vector is
+  // masked, so zeros go to the idle LDS buffer and are never read).
+  // Scheduling barriers keep the next tile's global loads ahead of the MFMAs,
+  // where three k-steps hide their latency, and the LDS stores after them.
   read_frags(As[0], Bs[0], 0, 0);
-  if constexpr (!A_T) {
-    // NT / NN: the loop body has no branches, so that each half of it is one
-    // scheduling region (in the last iteration the loads fall past K; every
-    // vector is masked, so zeros go to the idle LDS buffer and are never
-    // read).  Scheduling barriers keep the next tile's global loads ahead of
-    // the MFMAs, where three k-steps hide their latency, and the LDS stores
-    // after them.
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      load_tiles((int64_t)(kt + 1) * BK);
-      __builtin_amdgcn_sched_barrier(0);
-      const uint16_t* as = As[cur];
-      const uint16_t* bs = Bs[cur];
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    load_tiles((int64_t)(kt + 1) * BK);
+    __builtin_amdgcn_sched_barrier(0);
+    const uint16_t* as = As[cur];
+    const uint16_t* bs = Bs[cur];
 #pragma unroll
-      for (int ks = 0; ks < KS - 1; ++ks) {
-        read_frags(as, bs, ks + 1, (ks + 1) & 1);
-        mfmas(ks & 1);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      la.store(As[cur ^ 1], tid);
-      lb.store(Bs[cur ^ 1], tid);
-      __syncthreads();
-      read_frags(As[cur ^ 1], Bs[cur ^ 1], 0, 0);
-      mfmas((KS - 1) & 1);
+    for (int ks = 0; ks < KS - 1; ++ks) {
+      read_frags(as, bs, ks + 1, (ks + 1) & 1);
+      mfmas(ks & 1);
     }
-  } else {
-    // TN (both operands transposed in registers): left to the compiler's
-    // schedule, which spreads the transposes among the MFMAs.
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      const bool more = kt + 1 < nk;
-      if (more) load_tiles((int64_t)(kt + 1) * BK);
-      const uint16_t* as = As[cur];
-      const uint16_t* bs = Bs[cur];
-#pragma unroll
-      for (int ks = 0; ks < KS - 1; ++ks) {
-        read_frags(as, bs, ks + 1, (ks + 1) & 1);
-        mfmas(ks & 1);
-      }
-      if (more) {
-        la.store(As[cur ^ 1], tid);
-        lb.store(Bs[cur ^ 1], tid);
-      }
-      __syncthreads();
-      if (more) read_frags(As[cur ^ 1], Bs[cur ^ 1], 0, 0);
-      mfmas((KS - 1) & 1);
-    }
+    __builtin_amdgcn_sched_barrier(0);
+    la.store(As[cur ^ 1], tid);
+    lb.store(Bs[cur ^ 1], tid);
+    __syncthreads();
+    read_frags(As[cur ^ 1], Bs[cur ^ 1], 0, 0);
+    mfmas((KS - 1) & 1);
   }
 
   // ------------------------------------------------------------ epilogue
