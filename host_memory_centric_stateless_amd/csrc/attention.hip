@@ -37,16 +37,6 @@ __device__ inline bf16x8_t as_frag(u32x4 v) { return __builtin_bit_cast(bf16x8_t
 __device__ inline bf16x8_t ld_frag(const uint16_t* p) {
   return as_frag(*reinterpret_cast<const u32x4*>(p));
 }
-// Two 4-element halves (8 bytes each) -> one fragment.
-__device__ inline bf16x8_t ld_frag2(const uint16_t* p0, const uint16_t* p1) {
-  u32x2 a = *reinterpret_cast<const u32x2*>(p0);
-  u32x2 b = *reinterpret_cast<const u32x2*>(p1);
-  return as_frag(u32x4{a[0], a[1], b[0], b[1]});
-}
-__device__ inline bf16x8_t pack_frag(const float* v) {
-  return as_frag(u32x4{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]), pack_bf2(v[4], v[5]),
-                       pack_bf2(v[6], v[7])});
-}
 __device__ inline f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -55,50 +45,76 @@ __device__ inline void zero(f32x16_t& a) {
   for (int r = 0; r < 16; ++r) a[r] = 0.0f;
 }
 
-// Copy a [ROWS][D] bf16 tile (global row stride ld) into LDS: normal copy
-// [ROWS][D+8] and/or transposed copy [D][ROWS+8].  Work is split into 8x8
-// blocks handled by threads t0..t0+nthr-1 (t = threadIdx.x - t0).
+// LDS tiles are [ROWS][D] row-major copies of global rows (pitch PITCH
+// elements), read two ways: 16-byte row reads (MFMA operand with rows = tile
+// rows, k = d) and transpose reads (operand with rows = d, k = tile rows).
+// PITCH = 152 elements = 304 bytes = 48 mod 256: the 16 rows of a row read hit
+// distinct 16-byte bank slots, and the four tile rows of one transpose read
+// (32 bytes each, two 16-lane groups side by side) fall on disjoint banks.
+constexpr int PITCH = 152;
+
+// Global -> registers -> LDS copy of one [ROWS][D] tile by 256 threads, split
+// so that the global loads can be issued a tile ahead of the LDS stores.
 template <int ROWS, int D>
-__device__ inline void load_tile(const uint16_t* src, int64_t ld, uint16_t* nrm, uint16_t* trn,
-                                 int t, int nthr) {
-  constexpr int DB = D / 8, NB = (ROWS / 8) * DB;
-  for (int blk = t; blk < NB; blk += nthr) {
-    const int rb = blk / DB, db = blk % DB;
-    u32x4 r[8];
+struct TileCopy {
+  static constexpr int VPR = D / 8;                // 16-byte vectors per row
+  static constexpr int V = ROWS * VPR / 256;       // vectors per thread
+  static_assert(V >= 1 && ROWS * VPR % 256 == 0, "tile does not split over 256 threads");
+  u32x4 r[V];
+  __device__ inline void load(const uint16_t* src, int64_t ld, int tid) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      r[i] = *reinterpret_cast<const u32x4*>(src + (int64_t)(rb * 8 + i) * ld + db * 8);
-    if (nrm) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        *reinterpret_cast<u32x4*>(nrm + (rb * 8 + i) * (D + 8) + db * 8) = r[i];
-    }
-    if (trn) {
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        u32x4 o;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          uint32_t w0 = r[2 * p][jj >> 1], w1 = r[2 * p + 1][jj >> 1];
-          uint32_t lo = (jj & 1) ? (w0 >> 16) : (w0 & 0xffffu);
-          uint32_t hi = (jj & 1) ? (w1 & 0xffff0000u) : (w1 << 16);
-          o[p] = lo | hi;
-        }
-        *reinterpret_cast<u32x4*>(trn + (db * 8 + jj) * (ROWS + 8) + rb * 8) = o;
-      }
+    for (int i = 0; i < V; ++i) {
+      const int idx = tid + 256 * i;
+      r[i] = *reinterpret_cast<const u32x4*>(src + (int64_t)(idx / VPR) * ld + (idx % VPR) * 8);
     }
   }
+  __device__ inline void store(uint16_t* lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const int idx = tid + 256 * i;
+      *reinterpret_cast<u32x4*>(lds + (idx / VPR) * PITCH + (idx % VPR) * 8) = r[i];
+    }
+  }
+};
+
+// Row-read fragment: rows row0 + lane%32, k = d0 + 8*(lane/32) + 0..7.
+__device__ inline bf16x8_t row_frag(const uint16_t* t, int row0, int d0, int lane) {
+  return ld_frag(t + (row0 + (lane & 31)) * PITCH + d0 + (lane >> 5) * 8);
+}
+
+// Transpose-read fragment: rows d = d0 + lane%32 of a [rows][d] tile, with
+// the eight k values (tile rows) in the order the probabilities use as the B
+// operand: k = r0 + 8*(e/4) + 4*(lane/32) + e%4 for element e.  One
+// ds_read_b64_tr_b16 over a 16-lane group hands lane i element i%4 of the
+// 8-byte chunks addressed by lanes i/4 + 4j (j = 0..3); lane s of the group
+// addresses tile row kb + s/4 at column d0 + 16*(group&1) + 4*(s%4), so lane
+// i receives column d0 + 16*(group&1) + i at tile rows kb..kb+3.
+__device__ inline bf16x8_t tr_frag(const uint16_t* t, int r0, int d0, int lane) {
+  typedef short s4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s4 lds_s4;
+  const int grp = lane >> 4, sl = lane & 15;
+  const int row = r0 + 4 * (grp >> 1) + (sl >> 2);
+  const int col = d0 + 16 * (grp & 1) + 4 * (sl & 3);
+  const uint16_t* q = t + row * PITCH + col;
+  const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)q);
+  const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(q + 8 * PITCH));
+  const u32x2 x = __builtin_bit_cast(u32x2, lo), y = __builtin_bit_cast(u32x2, hi);
+  return as_frag(u32x4{x[0], x[1], y[0], y[1]});
 }
 
 // --------------------------------------------------------------- forward
+// 256 threads = 4 waves x 32 queries; key/value tiles of 64 rows, double
+// buffered: the next tile's global loads are in flight while this tile's
+// scores, softmax and P V run.  At most 256 VGPRs, so two workgroups share a
+// CU.
 template <int D>
-__global__ __launch_bounds__(256) void attn_fwd_kernel(const uint16_t* __restrict__ qkv,
-                                                       uint16_t* __restrict__ out,
-                                                       float* __restrict__ lse, int seq, int nq,
-                                                       int nkv, int64_t T) {
+__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __restrict__ qkv,
+                                                          uint16_t* __restrict__ out,
+                                                          float* __restrict__ lse, int seq,
+                                                          int nq, int nkv, int64_t T) {
   constexpr int BKV = 64, KS = D / 16, DT = D / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BKV * (D + 8)];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * (BKV + 8)];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BKV * PITCH];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BKV * PITCH];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5;
   const int qb = gridDim.x - 1 - blockIdx.x;
@@ -122,32 +138,39 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const uint16_t* __restric
   for (int dd = 0; dd < DT; ++dd) zero(acc[dd]);
   float m_run = -INFINITY, l_run = 0.0f;
 
-  const int nkb = (qb * 128 + 127) / BKV + 1;
+  TileCopy<BKV, D> ck, cv;
+  const int nkb = (qb * 128 + 127) / BKV + 1;  // key tiles up to the block's last query
+  ck.load(Kp + row0 * ld, ld, tid);
+  cv.load(Vp + row0 * ld, ld, tid);
+  ck.store(Ks[0], tid);
+  cv.store(Vs[0], tid);
+  __syncthreads();
   for (int kb = 0; kb < nkb; ++kb) {
-    const int kv0 = kb * BKV;
-    if (tid < 128)
-      load_tile<BKV, D>(Kp + (row0 + kv0) * ld, ld, Ks, nullptr, tid, 128);
-    else
-      load_tile<BKV, D>(Vp + (row0 + kv0) * ld, ld, nullptr, Vt, tid - 128, 128);
-    __syncthreads();
+    const int cur = kb & 1, kv0 = kb * BKV;
+    const bool more = kb + 1 < nkb;
+    if (more) {
+      ck.load(Kp + (row0 + kv0 + BKV) * ld, ld, tid);
+      cv.load(Vp + (row0 + kv0 + BKV) * ld, ld, tid);
+    }
     if (kv0 <= q0 + 31) {
-      f32x16_t s[2];
+      const uint16_t* ks_t = Ks[cur];
+      const uint16_t* vs_t = Vs[cur];
+      f32x16_t sc[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        zero(s[i]);
+        zero(sc[i]);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          s[i] = mfma(ld_frag(Ks + (i * 32 + (lane & 31)) * (D + 8) + ks * 16 + g * 8), qf[ks],
-                      s[i]);
+        for (int ks = 0; ks < KS; ++ks) sc[i] = mfma(row_frag(ks_t, i * 32, ks * 16, lane), qf[ks], sc[i]);
       }
+      const bool diag = kv0 + BKV - 1 > q0;  // some keys of this tile lie after some queries
       float mloc = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int kv = kv0 + i * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-          float v = (kv <= q) ? s[i][r] * sl2 : -INFINITY;
-          s[i][r] = v;
+          const float v = (!diag || kv <= q) ? sc[i][r] * sl2 : -INFINITY;
+          sc[i][r] = v;
           mloc = fmaxf(mloc, v);
         }
       mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
@@ -159,27 +182,31 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const uint16_t* __restric
       for (int dd = 0; dd < DT; ++dd)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[dd][r] *= alpha;
-      float pv[2][16];
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float pr = exp2f(s[i][r] - m_new);
-          pv[i][r] = pr;
+          const float pr = exp2f(sc[i][r] - m_new);
+          sc[i][r] = pr;
           l_run += pr;
         }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          bf16x8_t pf = pack_frag(&pv[i][hh * 8]);
-          const int kvo = i * 32 + hh * 16 + g * 4;
+          const f32x16_t& pv = sc[i];
+          const bf16x8_t pf = as_frag(u32x4{pack_bf2(pv[hh * 8 + 0], pv[hh * 8 + 1]),
+                                            pack_bf2(pv[hh * 8 + 2], pv[hh * 8 + 3]),
+                                            pack_bf2(pv[hh * 8 + 4], pv[hh * 8 + 5]),
+                                            pack_bf2(pv[hh * 8 + 6], pv[hh * 8 + 7])});
 #pragma unroll
-          for (int dd = 0; dd < DT; ++dd) {
-            const uint16_t* vr = Vt + (dd * 32 + (lane & 31)) * (BKV + 8) + kvo;
-            acc[dd] = mfma(ld_frag2(vr, vr + 8), pf, acc[dd]);
-          }
+          for (int dd = 0; dd < DT; ++dd)
+            acc[dd] = mfma(tr_frag(vs_t, i * 32 + hh * 16, dd * 32, lane), pf, acc[dd]);
         }
+    }
+    if (more) {
+      ck.store(Ks[cur ^ 1], tid);
+      cv.store(Vs[cur ^ 1], tid);
     }
     __syncthreads();
   }
@@ -223,15 +250,17 @@ __global__ void attn_dsum_kernel(const uint16_t* __restrict__ o, const uint16_t*
 }
 
 // ------------------------------------------------------- backward: dQ
+// Query block outer (4 waves x 32 queries), key/value tiles of 64 rows,
+// double buffered.  dQ^T += K^T dS^T takes K^T from the same LDS tile through
+// transpose reads.
 template <int D>
-__global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
+__global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(
     const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ dsum, uint16_t* __restrict__ dqkv,
     int seq, int nq, int nkv, int64_t T) {
   constexpr int BKV = 64, KS = D / 16, DT = D / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BKV * (D + 8)];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[BKV * (D + 8)];
-  __shared__ __attribute__((aligned(16))) uint16_t Kt[D * (BKV + 8)];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BKV * PITCH];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BKV * PITCH];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5;
   const int qb = gridDim.x - 1 - blockIdx.x;
@@ -260,48 +289,60 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
 #pragma unroll
   for (int dd = 0; dd < DT; ++dd) zero(acc[dd]);
 
+  TileCopy<BKV, D> ck, cv;
   const int nkb = (qb * 128 + 127) / BKV + 1;
+  ck.load(Kp + row0 * ld, ld, tid);
+  cv.load(Vp + row0 * ld, ld, tid);
+  ck.store(Ks[0], tid);
+  cv.store(Vs[0], tid);
+  __syncthreads();
   for (int kb = 0; kb < nkb; ++kb) {
-    const int kv0 = kb * BKV;
-    if (tid < 128)
-      load_tile<BKV, D>(Kp + (row0 + kv0) * ld, ld, Ks, Kt, tid, 128);
-    else
-      load_tile<BKV, D>(Vp + (row0 + kv0) * ld, ld, Vs, nullptr, tid - 128, 128);
-    __syncthreads();
+    const int cur = kb & 1, kv0 = kb * BKV;
+    const bool more = kb + 1 < nkb;
+    if (more) {
+      ck.load(Kp + (row0 + kv0 + BKV) * ld, ld, tid);
+      cv.load(Vp + (row0 + kv0 + BKV) * ld, ld, tid);
+    }
     if (kv0 <= q0 + 31) {
-      f32x16_t s[2], dp[2];
+      const uint16_t* ks_t = Ks[cur];
+      const uint16_t* vs_t = Vs[cur];
+      f32x16_t sc[2], dp[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        zero(s[i]);
+        zero(sc[i]);
         zero(dp[i]);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const int ro = (i * 32 + (lane & 31)) * (D + 8) + ks * 16 + g * 8;
-          s[i] = mfma(ld_frag(Ks + ro), qf[ks], s[i]);
-          dp[i] = mfma(ld_frag(Vs + ro), df[ks], dp[i]);
+          sc[i] = mfma(row_frag(ks_t, i * 32, ks * 16, lane), qf[ks], sc[i]);
+          dp[i] = mfma(row_frag(vs_t, i * 32, ks * 16, lane), df[ks], dp[i]);
         }
       }
-      float ds[2][16];
+      const bool diag = kv0 + BKV - 1 > q0;
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int kv = kv0 + i * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-          float pr = (kv <= q) ? exp2f(s[i][r] * sl2 - lse2) : 0.0f;
-          ds[i][r] = pr * (dp[i][r] - dq_sum);
+          const float pr = (!diag || kv <= q) ? exp2f(sc[i][r] * sl2 - lse2) : 0.0f;
+          sc[i][r] = pr * (dp[i][r] - dq_sum);
         }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          bf16x8_t sf = pack_frag(&ds[i][hh * 8]);
-          const int kvo = i * 32 + hh * 16 + g * 4;
+          const f32x16_t& dsv = sc[i];
+          const bf16x8_t sf = as_frag(u32x4{pack_bf2(dsv[hh * 8 + 0], dsv[hh * 8 + 1]),
+                                            pack_bf2(dsv[hh * 8 + 2], dsv[hh * 8 + 3]),
+                                            pack_bf2(dsv[hh * 8 + 4], dsv[hh * 8 + 5]),
+                                            pack_bf2(dsv[hh * 8 + 6], dsv[hh * 8 + 7])});
 #pragma unroll
-          for (int dd = 0; dd < DT; ++dd) {
-            const uint16_t* kr = Kt + (dd * 32 + (lane & 31)) * (BKV + 8) + kvo;
-            acc[dd] = mfma(ld_frag2(kr, kr + 8), sf, acc[dd]);
-          }
+          for (int dd = 0; dd < DT; ++dd)
+            acc[dd] = mfma(tr_frag(ks_t, i * 32 + hh * 16, dd * 32, lane), sf, acc[dd]);
         }
+    }
+    if (more) {
+      ck.store(Ks[cur ^ 1], tid);
+      cv.store(Vs[cur ^ 1], tid);
     }
     __syncthreads();
   }
@@ -319,18 +360,21 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
 }
 
 // ---------------------------------------------------- backward: dK, dV
+// Key block outer (4 waves x 32 keys, one key per lane), so grouped query
+// heads are summed in a fixed order without atomics.  The (query head, query
+// tile) pairs after the block form one sequence of 64-row Q / dO tiles, double
+// buffered with their LSE and D rows; dV^T += dO^T P and dK^T += Q^T dS read
+// dO^T and Q^T from the same tiles through transpose reads.
 template <int D>
-__global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
+__global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ dsum, uint16_t* __restrict__ dqkv,
     int seq, int nq, int nkv, int64_t T) {
   constexpr int BQ = 64, KS = D / 16, DT = D / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[BQ * (D + 8)];
-  __shared__ __attribute__((aligned(16))) uint16_t Qt[D * (BQ + 8)];
-  __shared__ __attribute__((aligned(16))) uint16_t Os[BQ * (D + 8)];  // dO, normal
-  __shared__ __attribute__((aligned(16))) uint16_t Ot[D * (BQ + 8)];  // dO, transposed
-  __shared__ __attribute__((aligned(16))) float Ls[BQ];
-  __shared__ __attribute__((aligned(16))) float Ds[BQ];
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][BQ * PITCH];
+  __shared__ __attribute__((aligned(16))) uint16_t Os[2][BQ * PITCH];  // dO
+  __shared__ __attribute__((aligned(16))) float Ls[2][BQ];
+  __shared__ __attribute__((aligned(16))) float Ds[2][BQ];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5;
   const int kvb = gridDim.x - 1 - blockIdx.x;
@@ -357,71 +401,89 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
     zero(adk[dd]);
     zero(adv[dd]);
   }
-  const int nqt = seq / BQ;
-  for (int hq = 0; hq < grp; ++hq) {
-    const int j = kvh * grp + hq;
-    const uint16_t* Qp = qkv + j * D;
-    const uint16_t* dOp = dout + j * D;
-    for (int qt = (kvb * 128) / BQ; qt < nqt; ++qt) {
-      const int q0 = qt * BQ;
-      if (tid < 128)
-        load_tile<BQ, D>(Qp + (row0 + q0) * ld, ld, Qs, Qt, tid, 128);
-      else
-        load_tile<BQ, D>(dOp + (row0 + q0) * ldo, ldo, Os, Ot, tid - 128, 128);
-      if (tid < BQ) {
-        Ls[tid] = lse[(int64_t)j * T + row0 + q0 + tid] * LOG2E;
-        Ds[tid] = dsum[(int64_t)j * T + row0 + q0 + tid];
-      }
-      __syncthreads();
-      if (q0 + BQ - 1 >= kw0) {
-        f32x16_t s[2], dp[2];
+  const int qt0 = (kvb * 128) / BQ, nqt = seq / BQ;
+  const int per_head = nqt - qt0, n_it = grp * per_head;
+
+  TileCopy<BQ, D> cq, co;
+  float stat = 0.0f;  // threads 0..63: LSE row, 64..127: D row of the tile
+  auto gload = [&](int it) {
+    const int j = kvh * grp + it / per_head;
+    const int q0 = (qt0 + it % per_head) * BQ;
+    cq.load(qkv + j * D + (row0 + q0) * ld, ld, tid);
+    co.load(dout + j * D + (row0 + q0) * ldo, ldo, tid);
+    if (tid < BQ)
+      stat = lse[(int64_t)j * T + row0 + q0 + tid] * LOG2E;
+    else if (tid < 2 * BQ)
+      stat = dsum[(int64_t)j * T + row0 + q0 + tid - BQ];
+  };
+  auto sstore = [&](int buf) {
+    cq.store(Qs[buf], tid);
+    co.store(Os[buf], tid);
+    if (tid < BQ)
+      Ls[buf][tid] = stat;
+    else if (tid < 2 * BQ)
+      Ds[buf][tid - BQ] = stat;
+  };
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int it = 0; it < n_it; ++it) {
+    const int cur = it & 1;
+    const int q0 = (qt0 + it % per_head) * BQ;
+    const bool more = it + 1 < n_it;
+    if (more) gload(it + 1);
+    if (q0 + BQ - 1 >= kw0) {
+      const uint16_t* qs_t = Qs[cur];
+      const uint16_t* os_t = Os[cur];
+      const bool diag = q0 < kw0 + 31;  // some query of the tile precedes some key
+      // the two 32-query halves of the tile one after the other (fewer live
+      // registers); the accumulation order stays fixed
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          zero(s[i]);
-          zero(dp[i]);
+      for (int i = 0; i < 2; ++i) {
+        f32x16_t sc, dp;
+        zero(sc);
+        zero(dp);
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            const int ro = (i * 32 + (lane & 31)) * (D + 8) + ks * 16 + g * 8;
-            s[i] = mfma(ld_frag(Qs + ro), kf[ks], s[i]);
-            dp[i] = mfma(ld_frag(Os + ro), vf[ks], dp[i]);
+        for (int ks = 0; ks < KS; ++ks) {
+          sc = mfma(row_frag(qs_t, i * 32, ks * 16, lane), kf[ks], sc);
+          dp = mfma(row_frag(os_t, i * 32, ks * 16, lane), vf[ks], dp);
+        }
+        f32x16_t pv;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int ql = i * 32 + rr * 8 + g * 4;
+          const float4 l4 = *reinterpret_cast<const float4*>(&Ls[cur][ql]);
+          const float4 d4 = *reinterpret_cast<const float4*>(&Ds[cur][ql]);
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+          const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = rr * 4 + e;
+            const float pr = (!diag || kv <= q0 + ql + e) ? exp2f(sc[r] * sl2 - lv[e]) : 0.0f;
+            pv[r] = pr;
+            sc[r] = pr * (dp[r] - dv[e]);
           }
         }
-        float pv[2][16], ds[2][16];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int hh = 0; hh < 2; ++hh) {
+          const bf16x8_t pf = as_frag(u32x4{pack_bf2(pv[hh * 8 + 0], pv[hh * 8 + 1]),
+                                            pack_bf2(pv[hh * 8 + 2], pv[hh * 8 + 3]),
+                                            pack_bf2(pv[hh * 8 + 4], pv[hh * 8 + 5]),
+                                            pack_bf2(pv[hh * 8 + 6], pv[hh * 8 + 7])});
+          const bf16x8_t sf = as_frag(u32x4{pack_bf2(sc[hh * 8 + 0], sc[hh * 8 + 1]),
+                                            pack_bf2(sc[hh * 8 + 2], sc[hh * 8 + 3]),
+                                            pack_bf2(sc[hh * 8 + 4], sc[hh * 8 + 5]),
+                                            pack_bf2(sc[hh * 8 + 6], sc[hh * 8 + 7])});
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
-            const int ql = i * 32 + rr * 8 + g * 4;
-            const float4 l4 = *reinterpret_cast<const float4*>(Ls + ql);
-            const float4 d4 = *reinterpret_cast<const float4*>(Ds + ql);
-            const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-            const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = rr * 4 + e;
-              const int qq = q0 + ql + e;
-              float pr = (kv <= qq) ? exp2f(s[i][r] * sl2 - lv[e]) : 0.0f;
-              pv[i][r] = pr;
-              ds[i][r] = pr * (dp[i][r] - dv[e]);
-            }
+          for (int dd = 0; dd < DT; ++dd) {
+            adv[dd] = mfma(tr_frag(os_t, i * 32 + hh * 16, dd * 32, lane), pf, adv[dd]);
+            adk[dd] = mfma(tr_frag(qs_t, i * 32 + hh * 16, dd * 32, lane), sf, adk[dd]);
           }
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            bf16x8_t pf = pack_frag(&pv[i][hh * 8]);
-            bf16x8_t sf = pack_frag(&ds[i][hh * 8]);
-            const int qo = i * 32 + hh * 16 + g * 4;
-#pragma unroll
-            for (int dd = 0; dd < DT; ++dd) {
-              const int ro = (dd * 32 + (lane & 31)) * (BQ + 8) + qo;
-              adv[dd] = mfma(ld_frag2(Ot + ro, Ot + ro + 8), pf, adv[dd]);
-              adk[dd] = mfma(ld_frag2(Qt + ro, Qt + ro + 8), sf, adk[dd]);
-            }
-          }
+        }
       }
-      __syncthreads();
     }
+    if (more) sstore(cur ^ 1);
+    __syncthreads();
   }
   const float scale = 1.0f / sqrtf((float)D);
   uint16_t* dk = dqkv + (row0 + kv) * ld + (int64_t)nq * D + kvh * D;
