@@ -264,6 +264,11 @@ def main():
                     help="override the configuration's sequences per micro-batch")
     ap.add_argument("--grad-accum", type=int, default=0,
                     help="override the configuration's micro-batches per step")
+    ap.add_argument("--micro-batches-per-pass", type=int, default=1,
+                    help="micro-batches sharing each weight residency in the headline run")
+    ap.add_argument("--no-layer-major", action="store_true",
+                    help="skip the second measurement with all of a step's micro-batches "
+                         "in one pass")
     ap.add_argument("--probe", action="store_true",
                     help="only run each block GEMM at this shape and a calibration copy")
     args = ap.parse_args()
@@ -285,7 +290,8 @@ def main():
             print(json.dumps(row), flush=True)
         return
     t0 = time.perf_counter()
-    sess = Session(cfg, host_threads=args.host_threads, drain_workgroups=args.drain_workgroups)
+    sess = Session(cfg, host_threads=args.host_threads, drain_workgroups=args.drain_workgroups,
+                   micro_batches_per_pass=args.micro_batches_per_pass)
     sess.load_weights(weight_stream(cfg, 0))
     print(f"[bench] {cfg.name}: init {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
 
@@ -322,6 +328,7 @@ def main():
 
     gemm = time_dominant_gemm(sess)
     link = link_roofline(sess.req.weight_buf)
+    step_no = 1 + args.warmup + args.steps
     kernels = []
     for k in ktimes:
         row = {"kernel": k["name"], "launches_per_step": k["launches"] / args.steps,
@@ -349,6 +356,47 @@ def main():
                      "traffic_unit": "HBM bytes per launch (FETCH_SIZE x 2 + WRITE_SIZE, "
                                      "calibrated on a 1 GiB copy)" if traffic else None})
     sess.close()
+
+    # The same training step with every micro-batch of the step in one pass
+    # (layer-major gradient accumulation): each layer's weights cross the
+    # host link once per step instead of once per micro-batch.
+    layer_major = None
+    if cfg.grad_accum > 1 and args.micro_batches_per_pass == 1 and not args.no_layer_major:
+        t0 = time.perf_counter()
+        lm = Session(cfg, host_threads=args.host_threads, drain_workgroups=args.drain_workgroups,
+                     micro_batches_per_pass=cfg.grad_accum, host_from=sess)
+        lm.bind()
+        print(f"[bench] layer-major pass: init {time.perf_counter() - t0:.1f} s", file=sys.stderr,
+              flush=True)
+        for w in range(args.warmup):
+            tok, lab = make_batch(cfg, step_no)
+            lm.step(tok, lab, step_no)
+            step_no += 1
+        lb = [make_batch(cfg, step_no + k) for k in range(args.steps)]
+        l0 = lm.stats()
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        lm_losses = []
+        for k in range(args.steps):
+            tok, lab = lb[k]
+            lm_losses.append(lm.step(tok, lab, step_no + k))
+        torch.cuda.synchronize()
+        lel = time.perf_counter() - t_start
+        l1 = lm.stats()
+        lm.close()
+        ltok = tokens_per_step * args.steps / lel
+        layer_major = {
+            "micro_batches_per_pass": cfg.grad_accum, "ms_per_step": 1e3 * lel / args.steps,
+            "tokens_per_s": ltok, "model_tflops": model_flops_per_token(cfg) * ltok / 1e12,
+            "hardware_tflops": hardware_flops_per_token(cfg) * ltok / 1e12,
+            "h2d_GBps": (l1["h2d_bytes"] - l0["h2d_bytes"]) / lel / 1e9,
+            "weight_loads_per_step": (l1["weight_loads"] - l0["weight_loads"]) / args.steps,
+            "loss_last": lm_losses[-1],
+            "note": "same step (4 micro-batches of 1 x 4096, each normalised by its own "
+                    "label count, gradients accumulated); the micro-batches share each "
+                    "weight residency"}
+        print(f"[bench] layer-major pass: {layer_major['ms_per_step']:.0f} ms/step, "
+              f"{ltok:.0f} tokens/s", file=sys.stderr, flush=True)
     base = None if args.no_cpu_baseline else cpu_baseline(cfg)
 
     out = {
@@ -360,7 +408,8 @@ def main():
                    "heads": cfg.n_heads, "kv_heads": cfg.n_kv_heads, "ffn": cfg.ffn,
                    "vocab": cfg.vocab, "micro_batch": cfg.micro_batch, "seq_len": cfg.seq_len,
                    "grad_accum": cfg.grad_accum, "ckpt_interval": cfg.ckpt_interval,
-                   "grad_slabs": cfg.n_grad_slabs, "global_batch_tokens": tokens_per_step},
+                   "grad_slabs": cfg.n_grad_slabs, "global_batch_tokens": tokens_per_step,
+                   "micro_batches_per_pass": args.micro_batches_per_pass},
         "tokens_per_s": tok_s, "hardware_tflops": hw_tflops,
         "slab_drain": ("dma" if sess.c.drain_workgroups == 0
                        else f"copy kernel, {sess.c.drain_workgroups} workgroups"),
@@ -374,6 +423,7 @@ def main():
                       "layer_backwards")},
         "roofline": roofline, "kernels": kernels,
         "isolated_swiglu_gemm": {"TFLOPs": gemm["tflops"], "ms": gemm["ms"], "shape_MNK": gemm["shape"]},
+        "layer_major": layer_major,
         "cpu_baseline": base,
     }
     print(json.dumps(out))

@@ -57,6 +57,8 @@ hipError_t launch_attn_fwd(const uint16_t* qkv, uint16_t* o, float* lse, int bat
 hipError_t launch_attn_bwd(const uint16_t* qkv, const uint16_t* o, const uint16_t* dout,
                            const float* lse, float* dsum, uint16_t* dqkv, int batch, int seq,
                            int nq, int nkv, int d, hipStream_t s);
+// out[0] = mean of v[0..n) (one workgroup, fixed order).
+hipError_t launch_mean(const float* v, int64_t n, float* out, hipStream_t s);
 hipError_t launch_cross_entropy(const float* logits, int64_t ld, const int32_t* labels, int64_t T,
                                 int V, float grad_scale, int64_t n_valid, uint16_t* dlogits,
                                 int64_t ld_d, float* loss_rows, float* loss_out, hipStream_t s);

@@ -325,6 +325,11 @@ hipError_t launch_rope(uint16_t* qkv, int64_t T, int seq, int nq, int nkv, int d
   return hipGetLastError();
 }
 
+hipError_t launch_mean(const float* v, int64_t n, float* out, hipStream_t s) {
+  hipLaunchKernelGGL(loss_reduce_kernel, dim3(1), dim3(NT), 0, s, v, n, 1.0f / (float)n, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_cross_entropy(const float* logits, int64_t ld, const int32_t* labels, int64_t T,
                                 int V, float grad_scale, int64_t n_valid, uint16_t* dlogits,
                                 int64_t ld_d, float* loss_rows, float* loss_out, hipStream_t s) {

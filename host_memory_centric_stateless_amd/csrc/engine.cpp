@@ -328,7 +328,8 @@ hipError_t gemm(mt_ctx* c, hipStream_t s, int layout, int epi, int64_t M, int64_
 
 // Algorithmic work of the other kernels.
 double attn_pairs(const mt_config& g) {
-  return (double)g.micro_batch * g.n_heads * 0.5 * (double)g.seq_len * (g.seq_len + 1.0);
+  return (double)g.micro_batch * g.micro_batches_per_pass * g.n_heads * 0.5 * (double)g.seq_len *
+         (g.seq_len + 1.0);
 }
 
 #define CK(expr)                            \
@@ -359,7 +360,7 @@ hipError_t block_forward(mt_ctx* c, const uint16_t* W, const Acts& a, float* y) 
   }
   {
     KScope k(c, s, "attn_fwd", 4.0 * g.head_dim * attn_pairs(g), 0);
-    CK(launch_attn_fwd(a.qkv, a.o, a.lse, g.micro_batch, g.seq_len, g.n_heads, g.n_kv_heads,
+    CK(launch_attn_fwd(a.qkv, a.o, a.lse, (int)(T / g.seq_len), g.seq_len, g.n_heads, g.n_kv_heads,
                        g.head_dim, s));
   }
   CK(gemm(c, s, MT_GEMM_NT, MT_EPI_F32_RESID, T, h, p.qd, a.o, p.qd, W + L[T_WO].off, p.qd, a.h1, h,
@@ -418,7 +419,7 @@ hipError_t block_backward(mt_ctx* c, const uint16_t* W, const Acts& a, const flo
   CK(gemm(c, s, MT_GEMM_TN, wepi, h, p.qd, T, dh1b, h, a.o, p.qd, slab(T_WO), p.qd));
   {
     KScope k(c, s, "attn_bwd", 10.0 * g.head_dim * attn_pairs(g), 0);
-    CK(launch_attn_bwd(a.qkv, a.o, dout, a.lse, c->wsp<float>(p.ws.dsum), dqkv, g.micro_batch,
+    CK(launch_attn_bwd(a.qkv, a.o, dout, a.lse, c->wsp<float>(p.ws.dsum), dqkv, (int)(T / g.seq_len),
                        g.seq_len, g.n_heads, g.n_kv_heads, g.head_dim, s));
   }
   {
@@ -848,7 +849,7 @@ mt_status run_step(mt_ctx* c, const Step& s) {
 
 // Enqueue steps [next_step, end), issuing each copy as soon as the step that
 // frees its buffer is enqueued.
-mt_status run_until(mt_ctx* c, size_t end, int64_t n_valid, float grad_scale) {
+mt_status run_until(mt_ctx* c, size_t end, const int64_t* n_valid, float grad_scale) {
   mt_status r = issue_ready_loads(c, (int)c->next_step - 1);
   if (r != MT_OK) return r;
   for (; c->next_step < end; ++c->next_step) {
@@ -859,13 +860,20 @@ mt_status run_until(mt_ctx* c, size_t end, int64_t n_valid, float grad_scale) {
       return MT_E_STATE;
     }
     if (s.kind == K_CE) {
+      // one launch per micro-batch of the pass, each normalised by its own
+      // valid-label count; the pass loss (slot 0) is the mean of theirs
       const Plan& p = c->p;
       KScope k(c, c->sc, "cross_entropy", 0, (double)p.T * p.c.vocab * 6);
-      MT_HIP(c, launch_cross_entropy(c->wsp<float>(p.ws.logits), p.c.vocab,
-                                     c->wsp<int32_t>(p.ws.labels[c->parity]), p.T, p.c.vocab,
-                                     grad_scale, n_valid, c->wsp<uint16_t>(p.ws.dlogits),
-                                     p.c.vocab, c->wsp<float>(p.ws.loss_rows),
-                                     c->wsp<float>(p.ws.loss), c->sc));
+      const int64_t V = p.c.vocab, Tm = p.T_mb;
+      float* loss = c->wsp<float>(p.ws.loss);
+      for (int mb = 0; mb < p.n_mb; ++mb)
+        MT_HIP(c, launch_cross_entropy(c->wsp<float>(p.ws.logits) + mb * Tm * V, V,
+                                       c->wsp<int32_t>(p.ws.labels[c->parity]) + mb * Tm, Tm,
+                                       (int)V, grad_scale, n_valid[mb],
+                                       c->wsp<uint16_t>(p.ws.dlogits) + mb * Tm * V, V,
+                                       c->wsp<float>(p.ws.loss_rows) + mb * Tm,
+                                       p.n_mb == 1 ? loss : loss + 1 + mb, c->sc));
+      if (p.n_mb > 1) MT_HIP(c, launch_mean(loss + 1, p.n_mb, loss, c->sc));
     } else {
       r = run_step(c, s);
       if (r != MT_OK) return r;
@@ -1067,11 +1075,11 @@ extern "C" mt_status mt_forward(mt_ctx* c, const int32_t* tokens, const int32_t*
   if (!tokens || !labels || !(grad_scale == grad_scale)) return MT_E_ARG;
   const Plan& p = c->p;
   const int64_t T = p.T, h = p.c.hidden;
-  int64_t n_valid = 0;
+  int64_t n_valid[32] = {0};  // per micro-batch of the pass
   for (int64_t t = 0; t < T; ++t) {
     if (tokens[t] < 0 || tokens[t] >= p.c.vocab) return MT_E_ARG;
     if (labels[t] >= p.c.vocab || labels[t] < -1) return MT_E_ARG;
-    n_valid += labels[t] >= 0;
+    n_valid[t / p.T_mb] += labels[t] >= 0;
   }
   {  // an overlapped optimizer step may still be updating the embedding
     std::unique_lock<std::mutex> lk(c->mu);
@@ -1126,7 +1134,7 @@ static mt_status backward_impl(mt_ctx* c, int32_t accumulate_flag, const mt_adam
     c->hp = *hp;
     c->opt_step = step;
   }
-  r = run_until(c, c->steps.size(), 0, 0.0f);
+  r = run_until(c, c->steps.size(), nullptr, 0.0f);
   c->fused = false;
   if (r != MT_OK) return r;
   if (hp) c->buf_unit[0] = c->buf_unit[1] = -1;  // working copies are being rewritten

@@ -45,10 +45,14 @@ std::string make_plan(const mt_config& c, Plan* p) {
   if (c.host_threads < 0) return "host_threads must be >= 0";
   if (c.slab_bf16 != 0 && c.slab_bf16 != 1) return "slab_bf16 must be 0 or 1";
   if (c.drain_workgroups < 0 || c.drain_workgroups > 256) return "drain_workgroups must be in 0..256";
+  if (c.micro_batches_per_pass < 1 || c.micro_batches_per_pass > 32)
+    return "micro_batches_per_pass must be in 1..32";
 
   p->c = c;
   const int64_t h = c.hidden, F = c.ffn, V = c.vocab;
-  p->T = (int64_t)c.micro_batch * c.seq_len;
+  p->T_mb = (int64_t)c.micro_batch * c.seq_len;
+  p->n_mb = c.micro_batches_per_pass;
+  p->T = p->T_mb * p->n_mb;
   p->qd = (int64_t)c.n_heads * c.head_dim;
   p->kvd = (int64_t)c.n_kv_heads * c.head_dim;
   p->ldq = p->qd + 2 * p->kvd;

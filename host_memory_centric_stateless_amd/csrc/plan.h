@@ -38,7 +38,9 @@ enum { T_ATTN_NORM = 0, T_WQ, T_WK, T_WV, T_WO, T_MLP_NORM, T_WGATE, T_WUP, T_WD
 
 struct Plan {
   mt_config c;
-  int64_t T;            // tokens per micro-batch
+  int64_t T;            // tokens per pass (n_mb micro-batches)
+  int64_t T_mb;         // tokens per micro-batch
+  int n_mb;             // micro-batches per pass
   int64_t qd, kvd, ldq; // q width, kv width, qkv row width
   TensorOff layer[T_COUNT];
   int64_t layer_elems;

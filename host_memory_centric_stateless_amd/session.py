@@ -27,7 +27,10 @@ def aligned_zeros(n: int, align: int = 64) -> np.ndarray:
 class Session:
     def __init__(self, cfg, host_threads: int = 0, device: str = "cuda:0",
                  ckpt_interval: Optional[int] = None, n_grad_slabs: Optional[int] = None,
-                 slab_bf16: bool = True, drain_workgroups: Optional[int] = None):
+                 slab_bf16: bool = True, drain_workgroups: Optional[int] = None,
+                 micro_batches_per_pass: int = 1, host_from: Optional["Session"] = None):
+        """host_from: use that session's host fp32 state (same model shape)
+        instead of allocating a new one; call bind() before the first step."""
         if ckpt_interval is not None:
             cfg = cfg.replace(ckpt_interval=ckpt_interval)
         if n_grad_slabs is not None:
@@ -35,17 +38,25 @@ class Session:
         self.cfg = cfg
         self.c = make_config(cfg, host_threads, slab_bf16,
                              DEFAULT_DRAIN_WORKGROUPS if drain_workgroups is None
-                             else drain_workgroups)
+                             else drain_workgroups, micro_batches_per_pass)
+        self.mb_per_pass = micro_batches_per_pass
         self.req = mt_device_requirements(self.c)
         self.groups = [MT_GROUP_EMBED] + list(range(cfg.n_layers)) + [MT_GROUP_HEAD]
         self.layout: Dict[int, Tuple[list, int]] = {g: mt_layout(self.c, g) for g in self.groups}
-        self.master, self.grad, self.m, self.v = {}, {}, {}, {}
-        for g in self.groups:
-            n = self.layout[g][1]
-            self.master[g] = aligned_zeros(n)
-            self.grad[g] = aligned_zeros(n)
-            self.m[g] = aligned_zeros(n)
-            self.v[g] = aligned_zeros(n)
+        if host_from is not None:
+            if {g: host_from.layout[g][1] for g in self.groups} != \
+                    {g: self.layout[g][1] for g in self.groups}:
+                raise ValueError("host_from has a different model shape")
+            self.master, self.grad = host_from.master, host_from.grad
+            self.m, self.v = host_from.m, host_from.v
+        else:
+            self.master, self.grad, self.m, self.v = {}, {}, {}, {}
+            for g in self.groups:
+                n = self.layout[g][1]
+                self.master[g] = aligned_zeros(n)
+                self.grad[g] = aligned_zeros(n)
+                self.m[g] = aligned_zeros(n)
+                self.v[g] = aligned_zeros(n)
 
         self.device = torch.device(device)
         r = self.req
@@ -104,15 +115,26 @@ class Session:
         """All micro-batches of one step (tokens/labels [acc, b, s]); grads
         land in self.grad.  Returns the mean micro-batch loss."""
         acc = tokens.shape[0]
-        losses = np.zeros(acc, dtype=np.float32)
+        npass, tok, lab = self._passes(tokens, labels)
+        losses = np.zeros(npass, dtype=np.float32)
         with torch.cuda.device(self.device):
-            for mb in range(acc):
-                out = losses[mb:mb + 1]
-                mt_forward(self.ctx, tokens[mb].reshape(-1), labels[mb].reshape(-1), 1.0 / acc, out)
-                mt_backward(self.ctx, 1 if mb > 0 else 0)
+            for k in range(npass):
+                out = losses[k:k + 1]
+                mt_forward(self.ctx, tok[k], lab[k], 1.0 / acc, out)
+                mt_backward(self.ctx, 1 if k > 0 else 0)
             mt_flush_grads(self.ctx)
         self._losses = losses  # keep the output buffer alive until flush wrote it
         return float(losses.mean())
+
+    def _passes(self, tokens: np.ndarray, labels: np.ndarray):
+        """[acc, b, s] micro-batches -> passes of mb_per_pass micro-batches,
+        each a contiguous int32 array (micro-batch-major)."""
+        acc, n = tokens.shape[0], self.mb_per_pass
+        if acc % n:
+            raise ValueError(f"{acc} micro-batches do not split into passes of {n}")
+        tok = np.ascontiguousarray(tokens, dtype=np.int32).reshape(acc // n, -1)
+        lab = np.ascontiguousarray(labels, dtype=np.int32).reshape(acc // n, -1)
+        return acc // n, tok, lab
 
     def step(self, tokens: np.ndarray, labels: np.ndarray, step: int, lr: Optional[float] = None,
              weight_decay: float = 0.01, overlap_optimizer: bool = True) -> float:
@@ -125,15 +147,15 @@ class Session:
             mt_adamw_step(self.ctx, hp, step)
             return loss
         acc = tokens.shape[0]
-        losses = np.zeros(acc, dtype=np.float32)
+        npass, tok, lab = self._passes(tokens, labels)
+        losses = np.zeros(npass, dtype=np.float32)
         with torch.cuda.device(self.device):
-            for mb in range(acc):
-                mt_forward(self.ctx, tokens[mb].reshape(-1), labels[mb].reshape(-1), 1.0 / acc,
-                           losses[mb:mb + 1])
-                if mb + 1 < acc:
-                    mt_backward(self.ctx, 1 if mb > 0 else 0)
+            for k in range(npass):
+                mt_forward(self.ctx, tok[k], lab[k], 1.0 / acc, losses[k:k + 1])
+                if k + 1 < npass:
+                    mt_backward(self.ctx, 1 if k > 0 else 0)
                 else:
-                    mt_backward_step(self.ctx, 1 if mb > 0 else 0, hp, step)
+                    mt_backward_step(self.ctx, 1 if k > 0 else 0, hp, step)
             mt_flush_grads(self.ctx)
         self._losses = losses
         return float(losses.mean())

@@ -75,6 +75,16 @@ typedef struct mt_config {
                              engine (hipMemcpyAsync on the offload stream);
                              n in 1..256 = a copy kernel of n workgroups that
                              writes the pinned host slab directly            */
+  int32_t micro_batches_per_pass; /* 1..32: micro-batches that share each
+                             weight residency.  mt_forward then takes this
+                             many micro-batches of micro_batch sequences at
+                             once (tokens [n][micro_batch][seq_len]); each is
+                             normalised by its own valid-label count, and
+                             their weight gradients are summed on the device
+                             before the slab drains: gradient accumulation in
+                             layer-major order, with weights crossing the host
+                             link once per pass instead of once per
+                             micro-batch.  1 = one micro-batch per pass.      */
 } mt_config;
 
 /* One tensor of a group's flat layout. */
@@ -169,14 +179,16 @@ mt_status mt_create(const mt_config* cfg, const mt_device_arena* arena, mt_ctx**
 mt_status mt_bind_layer(mt_ctx* ctx, int32_t group, float* master, float* grad, float* adam_m,
                         float* adam_v, int64_t numel);
 
-/* Enqueue the forward pass of one micro-batch: embedding gather on the host,
- * streamed block forwards with a checkpoint every K layers, the LM head in
- * vocabulary chunks, cross-entropy and its gradient scaled by
- * grad_scale / (labelled tokens).  tokens and labels are host int32 arrays of
- * micro_batch*seq_len entries (sequence-major); label -1 is ignored; tokens
- * must be in [0, vocab).  The micro-batch mean loss is written to *loss_out
- * when mt_flush_grads returns (loss_out may be NULL).  Returns without waiting
- * for the GPU. */
+/* Enqueue the forward pass of one pass of micro_batches_per_pass
+ * micro-batches: embedding gather on the host, streamed block forwards with a
+ * checkpoint every K layers, the LM head in vocabulary chunks, cross-entropy
+ * and its gradient, scaled for each micro-batch by grad_scale / (labelled
+ * tokens of that micro-batch).  tokens and labels are host int32 arrays of
+ * micro_batches_per_pass*micro_batch*seq_len entries (micro-batch-major, then
+ * sequence-major); label -1 is ignored; tokens must be in [0, vocab).  The
+ * mean over the pass's micro-batches of their mean losses is written to
+ * *loss_out when mt_flush_grads returns (loss_out may be NULL).  Returns
+ * without waiting for the GPU. */
 mt_status mt_forward(mt_ctx* ctx, const int32_t* tokens, const int32_t* labels, float grad_scale,
                      float* loss_out);
 

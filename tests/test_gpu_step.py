@@ -146,6 +146,41 @@ def _grads_after_one_step(cfg, **kw):
         sess.close()
 
 
+def test_layer_major_pass_matches_oracle_and_microbatch_order():
+    """Two micro-batches per weight residency (micro_batches_per_pass=2): the
+    same step as one micro-batch per pass, including per-micro-batch loss
+    normalisation when the micro-batches hold different numbers of labels."""
+    cfg = PRESETS["C1"].replace(grad_accum=2)
+    tok, lab = make_batch(cfg, 1)
+    lab = lab.copy()
+    lab[0, 0, :40] = -1  # micro-batch 0 has 40 fewer labelled tokens
+    st = HostState(cfg, np.float32)
+    st.load_weights(weight_stream(cfg, 0))
+    ol = train_step(st, tok, lab, 1)
+    og = _tensors(cfg, st.grad)
+    got = {}
+    for n in (1, 2):
+        print("micro_batches_per_pass", n, flush=True)
+        sess = _session(cfg, micro_batches_per_pass=n)
+        try:
+            loss = sess.forward_backward(tok, lab)
+            got[n] = (loss, _tensors(cfg, sess.grad), sess.stats())
+        finally:
+            sess.close()
+    for n, (loss, gg, stats) in got.items():
+        worst = max(rel_l2(gg[k], og[k]) for k in og)
+        print(f"n={n} loss gpu {loss:.6f} oracle {ol:.6f} worst grad rel L2 {worst:.3e}", flush=True)
+        assert abs(loss - ol) <= LOSS_TOL
+        assert worst <= GRAD_TOL
+    # same math, different summation order: the two GPU runs agree closely
+    l1, g1, s1 = got[1]
+    l2, g2, s2 = got[2]
+    assert abs(l1 - l2) <= 1e-3
+    assert max(rel_l2(g2[k], g1[k]) for k in g1) <= 1e-2
+    # each weight streams once per pass
+    assert s2["weight_loads"] < s1["weight_loads"]
+
+
 def test_pipeline_invariants_bit_exact():
     cfg = PRESETS["C1"].replace(grad_accum=2)
     base_loss, base, _ = _grads_after_one_step(cfg, ckpt_interval=1)
