@@ -249,6 +249,14 @@ def measured_traffic(kernel: str, cfg_name: str, default_shape: bool):
     return float(fields["traffic_bytes_per_launch"])
 
 
+def mem_available_gib() -> float:
+    with open("/proc/meminfo") as f:
+        for line in f:
+            if line.startswith("MemAvailable:"):
+                return int(line.split()[1]) / 2**20
+    return float("inf")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -269,6 +277,9 @@ def main():
     ap.add_argument("--no-layer-major", action="store_true",
                     help="skip the second measurement with all of a step's micro-batches "
                          "in one pass")
+    ap.add_argument("--host-mem-gib", type=float, default=0.0,
+                    help="host memory the run may use (default: MemAvailable); the run stops "
+                         "before allocating if the host state and pinned buffers exceed it")
     ap.add_argument("--probe", action="store_true",
                     help="only run each block GEMM at this shape and a calibration copy")
     args = ap.parse_args()
@@ -289,6 +300,16 @@ def main():
         for row in probe(cfg):
             print(json.dumps(row), flush=True)
         return
+    from host_memory_centric_stateless_amd import make_config, mt_device_requirements
+    req = mt_device_requirements(make_config(cfg, micro_batches_per_pass=args.micro_batches_per_pass))
+    need_gib = (req.host_state + req.pinned_host) / 2**30 + 6.0  # + interpreter, torch, staging
+    limit_gib = args.host_mem_gib or mem_available_gib()
+    print(f"[bench] host memory: need ~{need_gib:.0f} GiB, limit {limit_gib:.0f} GiB",
+          file=sys.stderr, flush=True)
+    if need_gib > limit_gib:
+        print(f"bench.py: {cfg.name} needs ~{need_gib:.0f} GiB of host memory for its fp32 state "
+              f"and pinned buffers; {limit_gib:.0f} GiB are available", file=sys.stderr)
+        sys.exit(3)
     t0 = time.perf_counter()
     sess = Session(cfg, host_threads=args.host_threads, drain_workgroups=args.drain_workgroups,
                    micro_batches_per_pass=args.micro_batches_per_pass)

@@ -254,7 +254,7 @@ __global__ void attn_dsum_kernel(const uint16_t* __restrict__ o, const uint16_t*
 // double buffered.  dQ^T += K^T dS^T takes K^T from the same LDS tile through
 // transpose reads.
 template <int D>
-__global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
     const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ dsum, uint16_t* __restrict__ dqkv,
     int seq, int nq, int nkv, int64_t T) {
@@ -306,39 +306,36 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(
     if (kv0 <= q0 + 31) {
       const uint16_t* ks_t = Ks[cur];
       const uint16_t* vs_t = Vs[cur];
-      f32x16_t sc[2], dp[2];
+      const bool diag = kv0 + BKV - 1 > q0;
+      // the two 32-key halves of the tile one after the other (fewer live
+      // registers); the accumulation order stays fixed
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        zero(sc[i]);
-        zero(dp[i]);
+        f32x16_t sc, dp;
+        zero(sc);
+        zero(dp);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          sc[i] = mfma(row_frag(ks_t, i * 32, ks * 16, lane), qf[ks], sc[i]);
-          dp[i] = mfma(row_frag(vs_t, i * 32, ks * 16, lane), df[ks], dp[i]);
+          sc = mfma(row_frag(ks_t, i * 32, ks * 16, lane), qf[ks], sc);
+          dp = mfma(row_frag(vs_t, i * 32, ks * 16, lane), df[ks], dp);
         }
-      }
-      const bool diag = kv0 + BKV - 1 > q0;
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int kv = kv0 + i * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-          const float pr = (!diag || kv <= q) ? exp2f(sc[i][r] * sl2 - lse2) : 0.0f;
-          sc[i][r] = pr * (dp[i][r] - dq_sum);
+          const float pr = (!diag || kv <= q) ? exp2f(sc[r] * sl2 - lse2) : 0.0f;
+          sc[r] = pr * (dp[r] - dq_sum);
         }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          const f32x16_t& dsv = sc[i];
-          const bf16x8_t sf = as_frag(u32x4{pack_bf2(dsv[hh * 8 + 0], dsv[hh * 8 + 1]),
-                                            pack_bf2(dsv[hh * 8 + 2], dsv[hh * 8 + 3]),
-                                            pack_bf2(dsv[hh * 8 + 4], dsv[hh * 8 + 5]),
-                                            pack_bf2(dsv[hh * 8 + 6], dsv[hh * 8 + 7])});
+          const bf16x8_t sf = as_frag(u32x4{pack_bf2(sc[hh * 8 + 0], sc[hh * 8 + 1]),
+                                            pack_bf2(sc[hh * 8 + 2], sc[hh * 8 + 3]),
+                                            pack_bf2(sc[hh * 8 + 4], sc[hh * 8 + 5]),
+                                            pack_bf2(sc[hh * 8 + 6], sc[hh * 8 + 7])});
 #pragma unroll
           for (int dd = 0; dd < DT; ++dd)
             acc[dd] = mfma(tr_frag(ks_t, i * 32 + hh * 16, dd * 32, lane), sf, acc[dd]);
         }
+      }
     }
     if (more) {
       ck.store(Ks[cur ^ 1], tid);

@@ -694,8 +694,14 @@ void opt_main(mt_ctx* c) {
       std::unique_lock<std::mutex> lk(c->mu);
       c->opt_cv.wait(lk, [&] { return c->stop || !c->opt_jobs.empty(); });
       if (c->opt_jobs.empty()) return;
-      j = std::move(c->opt_jobs.front());
-      c->opt_jobs.pop_front();
+      // Serve pending units in the order the next forward reads them
+      // (embedding, blocks 0..L-1, head chunks): the backward hands them over
+      // last-block-first, and any backlog would otherwise hold up block 0.
+      auto key = [](const Job& x) { return x.kind == Job::SLAB ? x.unit : -1; };
+      auto it = std::min_element(c->opt_jobs.begin(), c->opt_jobs.end(),
+                                 [&](const Job& a, const Job& b) { return key(a) < key(b); });
+      j = std::move(*it);
+      c->opt_jobs.erase(it);
     }
     const double t0 = now_s();
     const mt_ctx::Bind& b = c->bind_of(j.group);

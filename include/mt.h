@@ -98,9 +98,11 @@ typedef struct mt_tensor_desc {
 /* Device and host memory the library needs for a configuration. */
 typedef struct mt_device_req {
   size_t weight_buf;      /* bytes of EACH of the two bf16 ping-pong buffers    */
-  size_t grad_slab;       /* bytes of EACH fp32 gradient slab                   */
+  size_t grad_slab;       /* bytes of EACH gradient slab (bf16 or fp32)         */
   size_t window;          /* activations of one K-layer recompute window        */
-  size_t checkpoints;     /* ceil(L/K) fp32 [T, h] layer inputs                 */
+  size_t checkpoints;     /* max(1, ceil(L/K) - 1) fp32 [T, h] inputs of layers
+                             K, 2K, ... (layer 0's input is the x0 staging in
+                             the workspace)                                     */
   size_t workspace;       /* head logits, gradients in flight, RoPE table, ...  */
   size_t device_total;    /* 2*weight_buf + n_slabs*grad_slab + the rest        */
   size_t pinned_host;     /* pinned host bytes the library allocates itself     */
