@@ -80,11 +80,12 @@ enum State { ST_UNBOUND, ST_IDLE, ST_FWD, ST_BWD, ST_FLUSHED };
 
 // Slabs leave the device either by the DMA engine or by a copy kernel that
 // writes the pinned host slab (mt_config.drain_workgroups).  Measured on the
-// MI355X host link with 405 MB slabs: DMA copies in both directions at once
-// give ~28 GB/s device->host beside ~57 GB/s host->device; an 8-workgroup copy
-// kernel keeps ~41 GB/s device->host, but kernels running beside it take 2-4x
-// longer (the CUs that hold a copy workgroup stall on its host-memory stores,
-// and every tile scheduled on them finishes late).
+// MI355X host link with 405 MB slabs: beside the weight loads, the runtime
+// ran many DMA device->host copies as blit kernels on the CUs, and the rest
+// fell to 7-16 GB/s on the copy engine.  A 4-workgroup copy kernel keeps
+// ~38 GB/s device->host with host->device unchanged at ~57 GB/s; with 8 or
+// more workgroups the two directions saturate the link and kernels sharing
+// CUs with the copy stall on its host stores for milliseconds.
 
 double now_s() {
   return std::chrono::duration<double>(std::chrono::steady_clock::now().time_since_epoch())
@@ -634,7 +635,12 @@ void worker_main(mt_ctx* c) {
       if (c->delay_us > 0) std::this_thread::sleep_for(std::chrono::microseconds(c->delay_us));
       const double t0 = now_s();
       const mt_ctx::Bind& b = c->bind_of(j.kind == Job::SLAB ? j.group : MT_GROUP_EMBED);
-      if (j.kind == Job::SLAB) {
+      // A slab holding a unit's last gradient of the step goes to the
+      // optimizer thread as is: it adds the slab and steps in one pass over
+      // the host state, then returns the slab.
+      const bool fused = j.adamw && j.kind == Job::SLAB;
+      if (fused) {
+      } else if (j.kind == Job::SLAB) {
         if (c->p.slab_bf16)
           accumulate_bf16(*c->pool, b.grad + j.e0, reinterpret_cast<const uint16_t*>(c->hslab[j.slab]),
                           j.n, j.add);
@@ -647,7 +653,7 @@ void worker_main(mt_ctx* c) {
                       c->dx0_stage[j.parity]);
       }
       const double t1 = now_s();
-      {  // the staging memory is consumed: hand it back before the optimizer runs
+      if (!fused) {  // the staging memory is consumed: hand it back before the optimizer runs
         std::lock_guard<std::mutex> g(c->mu);
         c->st.accumulate_s += t1 - t0;
         if (j.kind == Job::SLAB)
@@ -665,6 +671,8 @@ void worker_main(mt_ctx* c) {
         o.e0 = j.kind == Job::SLAB ? j.e0 : 0;
         o.n = j.kind == Job::SLAB ? j.n : b.n;
         o.unit = j.unit;
+        o.slab = fused ? j.slab : -1;
+        o.add = j.add;
         c->opt_jobs.push_back(std::move(o));
         c->outstanding += 1;
         c->opt_cv.notify_all();
@@ -705,11 +713,20 @@ void opt_main(mt_ctx* c) {
     }
     const double t0 = now_s();
     const mt_ctx::Bind& b = c->bind_of(j.group);
-    adamw(*c->opt_pool, b.master + j.e0, b.grad + j.e0, b.m + j.e0, b.v + j.e0,
-          b.pinned ? b.pinned + j.e0 : nullptr, j.n, c->hp, c->opt_step);
+    if (j.slab >= 0)  // last gradient still in its slab: add it and step in one pass
+      adamw_slab(*c->opt_pool, b.master + j.e0, b.grad + j.e0, b.m + j.e0, b.v + j.e0,
+                 b.pinned ? b.pinned + j.e0 : nullptr, c->hslab[j.slab], c->p.slab_bf16, j.add,
+                 j.n, c->hp, c->opt_step);
+    else
+      adamw(*c->opt_pool, b.master + j.e0, b.grad + j.e0, b.m + j.e0, b.v + j.e0,
+            b.pinned ? b.pinned + j.e0 : nullptr, j.n, c->hp, c->opt_step);
     {
       std::lock_guard<std::mutex> g(c->mu);
       c->st.adamw_s += now_s() - t0;
+      if (j.slab >= 0) {
+        c->free_slabs.push_back(j.slab);
+        c->slab_cv.notify_all();
+      }
       if (j.kind == Job::SLAB)
         c->upd_pending[j.unit] = 0;
       else

@@ -123,6 +123,13 @@ struct AdamCoef {
         eps((float)hp.eps) {}
 };
 
+inline float bf16_bits_to_f32(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
 // One element of the update, in the order of the per-element definition:
 // decay, first and second moments, bias-corrected step.  Every operation is a
 // separately rounded fp32 operation (built with contraction off).
@@ -148,6 +155,33 @@ inline void adam_range(const AdamCoef& k, float* __restrict p, const float* __re
 }
 }  // namespace
 
+// Gradient element i of a slab job: (add ? grad[i] : 0) + slab[i], stored back
+// into grad (one fp32 add, as accumulate does), then the update.
+template <bool BF, bool SB, bool ADD>
+inline void adam_slab_range(const AdamCoef& k, float* __restrict p, float* __restrict g,
+                            float* __restrict m, float* __restrict v, uint16_t* __restrict bf,
+                            const void* __restrict slab, int64_t b, int64_t e) {
+  const uint16_t* __restrict s16 = static_cast<const uint16_t*>(slab);
+  const float* __restrict s32 = static_cast<const float*>(slab);
+  for (int64_t i = b; i < e; ++i) {
+    const float si = SB ? bf16_bits_to_f32(s16[i]) : s32[i];
+    const float gi = ADD ? g[i] + si : si;
+    g[i] = gi;
+    float pi = p[i] * k.decay;
+    float mi = m[i] * k.b1;
+    mi = mi + k.c1 * gi;
+    float vi = v[i] * k.b2;
+    vi = vi + k.c2 * (gi * gi);
+    const float mh = mi / k.bc1;
+    const float vh = vi / k.bc2;
+    pi = pi - (k.lr * mh) / (sqrtf(vh) + k.eps);
+    p[i] = pi;
+    m[i] = mi;
+    v[i] = vi;
+    if (BF) bf[i] = rne_bf16(pi);
+  }
+}
+
 void adamw(ThreadPool& pool, float* p, const float* g, float* m, float* v, uint16_t* bf, int64_t n,
            const mt_adamw_hparams& hp, int64_t step) {
   const AdamCoef k(hp, step);
@@ -156,6 +190,24 @@ void adamw(ThreadPool& pool, float* p, const float* g, float* m, float* v, uint1
       adam_range<true>(k, p, g, m, v, bf, b, e);
     else
       adam_range<false>(k, p, g, m, v, nullptr, b, e);
+  });
+}
+
+void adamw_slab(ThreadPool& pool, float* p, float* g, float* m, float* v, uint16_t* bf,
+                const void* slab, bool slab_bf16, bool add, int64_t n, const mt_adamw_hparams& hp,
+                int64_t step) {
+  const AdamCoef k(hp, step);
+  chunked(pool, n, [&](int64_t b, int64_t e) {
+#define MT_SLAB_CASE(BFV, SBV, ADDV)                                        \
+  if ((bf != nullptr) == BFV && slab_bf16 == SBV && add == ADDV) {          \
+    adam_slab_range<BFV, SBV, ADDV>(k, p, g, m, v, bf, slab, b, e);         \
+    return;                                                                 \
+  }
+    MT_SLAB_CASE(true, true, true) MT_SLAB_CASE(true, true, false)
+    MT_SLAB_CASE(true, false, true) MT_SLAB_CASE(true, false, false)
+    MT_SLAB_CASE(false, true, true) MT_SLAB_CASE(false, true, false)
+    MT_SLAB_CASE(false, false, true) MT_SLAB_CASE(false, false, false)
+#undef MT_SLAB_CASE
   });
 }
 

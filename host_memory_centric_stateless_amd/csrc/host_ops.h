@@ -40,6 +40,11 @@ int default_threads();
 void cast_bf16(ThreadPool& pool, const float* src, uint16_t* dst, int64_t n);
 void adamw(ThreadPool& pool, float* p, const float* g, float* m, float* v, uint16_t* bf, int64_t n,
            const mt_adamw_hparams& hp, int64_t step);
+// grad = (add ? grad : 0) + slab, then adamw on that gradient, in one pass:
+// the same values as accumulate/accumulate_bf16 followed by adamw.
+void adamw_slab(ThreadPool& pool, float* p, float* g, float* m, float* v, uint16_t* bf,
+                const void* slab, bool slab_bf16, bool add, int64_t n, const mt_adamw_hparams& hp,
+                int64_t step);
 void accumulate(ThreadPool& pool, float* grad, const float* src, int64_t n, bool add);
 // grad = float(src) or grad += float(src) for bf16 src.
 void accumulate_bf16(ThreadPool& pool, float* grad, const uint16_t* src, int64_t n, bool add);

@@ -201,19 +201,22 @@ def test_pipeline_invariants_bit_exact():
         np.testing.assert_array_equal(g[k], base[k], err_msg=f"delayed worker {k}")
 
 
-def test_overlapped_optimizer_bit_exact():
+@pytest.mark.parametrize("acc,slab_bf16,per_pass", [(2, True, 1), (1, False, 1), (2, True, 2)])
+def test_overlapped_optimizer_bit_exact(acc, slab_bf16, per_pass):
     """mt_backward_step (AdamW per group as its gradient lands, overlapped
-    with the rest of the backward) must give exactly the weights, moments and
-    working copies of mt_backward + mt_flush_grads + mt_adamw_step."""
-    cfg = PRESETS["C1"].replace(grad_accum=2)
+    with the rest of the backward; a unit's last slab is added and stepped in
+    one pass) must give exactly the weights, moments, gradients and working
+    copies of mt_backward + mt_flush_grads + mt_adamw_step."""
+    cfg = PRESETS["C1"].replace(grad_accum=acc)
     runs = []
     for overlap in (False, True):
-        sess = _session(cfg)
+        sess = _session(cfg, slab_bf16=slab_bf16, micro_batches_per_pass=per_pass)
         try:
             for step in (1, 2, 3):
                 tok, lab = make_batch(cfg, step)
                 sess.step(tok, lab, step, overlap_optimizer=overlap)
-            runs.append({g: (sess.master[g].copy(), sess.m[g].copy(), sess.v[g].copy())
+            runs.append({g: (sess.master[g].copy(), sess.m[g].copy(), sess.v[g].copy(),
+                             sess.grad[g].copy())
                          for g in sess.groups})
             print("overlap", overlap, sess.stats(), flush=True)
         finally:
