@@ -24,7 +24,6 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BK = 64;
 constexpr int LDSK = BK + 8;  // elements per LDS row
-constexpr int NT = 256;       // 4 waves as 2 x 2
 
 __device__ inline bf16x8_t frag(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(p));
@@ -55,9 +54,9 @@ struct RowMap {
 // Operand stored [row][k] (k contiguous): R rows x 64 k, R/32 vectors of
 // 16 B per thread.  Out-of-range vectors are zeroed when written to LDS, not
 // when loaded, so no wait on the loads is needed until after the MFMAs.
-template <int R>
+template <int R, int NTH>
 struct LoadK {
-  static constexpr int V = R * 8 / NT;
+  static constexpr int V = R * 8 / NTH;
   u32x4 r[V];
   uint32_t ok = 0;  // bit i: vector i is inside the matrix
   template <class Map>
@@ -66,7 +65,7 @@ struct LoadK {
     ok = 0;
 #pragma unroll
     for (int i = 0; i < V; ++i) {
-      const int idx = tid + NT * i;
+      const int idx = tid + NTH * i;
       const int64_t k = k0 + (idx & 7) * 8;
       bool rok;
       const int64_t g = rm.map(idx >> 3, rok);
@@ -78,7 +77,7 @@ struct LoadK {
   __device__ inline void store(uint16_t* lds, int tid) const {
 #pragma unroll
     for (int i = 0; i < V; ++i) {
-      const int idx = tid + NT * i;
+      const int idx = tid + NTH * i;
       *reinterpret_cast<u32x4*>(lds + (idx >> 3) * LDSK + (idx & 7) * 8) =
           ((ok >> i) & 1) ? r[i] : u32x4{0, 0, 0, 0};
     }
@@ -90,11 +89,11 @@ struct LoadK {
 // MFMA fragments are then taken from it with LDS transpose reads (frag_t).
 // The pitch is R + 32 elements (64 bytes past a multiple of 256): the four
 // k-rows that one transpose read touches fall on disjoint banks.
-template <int R>
+template <int R, int NTH>
 struct LoadKT {
   static constexpr int PT = R + 32;
   static constexpr int VPR = R / 8;          // 16-byte vectors per k-row
-  static constexpr int V = 64 * VPR / NT;    // vectors per thread
+  static constexpr int V = 64 * VPR / NTH;   // vectors per thread
   static constexpr int LDS_ELEMS = 64 * PT;
   u32x4 r[V];
   uint32_t ok = 0;  // bit i: vector i is inside the matrix
@@ -104,7 +103,7 @@ struct LoadKT {
     ok = 0;
 #pragma unroll
     for (int i = 0; i < V; ++i) {
-      const int idx = tid + NT * i;
+      const int idx = tid + NTH * i;
       const int64_t k = k0 + idx / VPR;
       const int64_t row = row0 + (idx % VPR) * 8;
       const bool in = k < K && row < nrows;
@@ -115,7 +114,7 @@ struct LoadKT {
   __device__ inline void store(uint16_t* lds, int tid) const {
 #pragma unroll
     for (int i = 0; i < V; ++i) {
-      const int idx = tid + NT * i;
+      const int idx = tid + NTH * i;
       *reinterpret_cast<u32x4*>(lds + (idx / VPR) * PT + (idx % VPR) * 8) =
           ((ok >> i) & 1) ? r[i] : u32x4{0, 0, 0, 0};
     }
@@ -170,16 +169,18 @@ __device__ inline bool tile_of(int bid, int nm, int nn, int& tm, int& tn) {
 // BM x BN output tile per workgroup; each of the 4 waves owns a
 // (BM/2) x (BN/2) quadrant = TM x TN tiles of 32 x 32.  Larger tiles issue
 // fewer LDS fragment reads per MFMA (TM + TN reads feed TM * TN MFMAs).
-template <int LAYOUT, int EPI, int BM, int BN>
-__global__ __launch_bounds__(NT) void gemm_kernel(mt_gemm_args p, int nm, int nn) {
+template <int LAYOUT, int EPI, int BM, int BN, int WVM, int WVN>
+__global__ __launch_bounds__(64 * WVM * WVN) void gemm_kernel(mt_gemm_args p, int nm, int nn) {
+  constexpr int NTH = 64 * WVM * WVN;  // WVM x WVN waves, each a (BM/WVM) x (BN/WVN) block
   constexpr bool A_T = (LAYOUT == MT_GEMM_TN);
   constexpr bool B_T = (LAYOUT != MT_GEMM_NT);
   constexpr bool SWI = (EPI == MT_EPI_SWIGLU);
   static_assert(!(SWI && B_T), "the SwiGLU product takes B as [rows][k]");
-  constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
+  constexpr int WM = BM / WVM, WN = BN / WVN, TM = WM / 32, TN = WN / 32;
+  static_assert(TM >= 1 && TN >= 1 && (!SWI || TN % 2 == 0), "wave block too small");
   constexpr int HALF = BN / 2;  // SwiGLU: gate rows, then up rows
-  constexpr int SA = A_T ? LoadKT<BM>::LDS_ELEMS : BM * LDSK;
-  constexpr int SB = B_T ? LoadKT<BN>::LDS_ELEMS : BN * LDSK;
+  constexpr int SA = A_T ? LoadKT<BM, NTH>::LDS_ELEMS : BM * LDSK;
+  constexpr int SB = B_T ? LoadKT<BN, NTH>::LDS_ELEMS : BN * LDSK;
   __shared__ __attribute__((aligned(16))) uint16_t As[2][SA];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][SB];
 
@@ -187,7 +188,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(mt_gemm_args p, int nm, int nn
   if (!tile_of(blockIdx.x, nm, nn, tm, tn)) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WVN, wn = wave % WVN;
   const int64_t m0 = (int64_t)tm * BM;
   const int64_t n0 = (int64_t)tn * (SWI ? HALF : BN);
   const int64_t K = p.K;
@@ -197,8 +198,8 @@ __global__ __launch_bounds__(NT) void gemm_kernel(mt_gemm_args p, int nm, int nn
   RowMap<BM, false> ra{m0, p.M, 0};
   RowMap<HALF, SWI> rb{n0, p.N, SWI ? p.ffn : 0};
 
-  typename std::conditional<A_T, LoadKT<BM>, LoadK<BM>>::type la;
-  typename std::conditional<B_T, LoadKT<BN>, LoadK<BN>>::type lb;
+  typename std::conditional<A_T, LoadKT<BM, NTH>, LoadK<BM, NTH>>::type la;
+  typename std::conditional<B_T, LoadKT<BN, NTH>, LoadK<BN, NTH>>::type lb;
 
   auto load_tiles = [&](int64_t k0) {
     if constexpr (A_T) la.load(A, p.lda, m0, p.M, k0, K, tid);
@@ -242,14 +243,14 @@ __global__ __launch_bounds__(NT) void gemm_kernel(mt_gemm_args p, int nm, int nn
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       if constexpr (A_T)
-        fa[slot][i] = frag_t(as, LoadKT<BM>::PT, wm * WM + i * 32, ks, lane);
+        fa[slot][i] = frag_t(as, LoadKT<BM, NTH>::PT, wm * WM + i * 32, ks, lane);
       else
         fa[slot][i] = frag(as + (arow + i * 32) * LDSK + ks * 16 + kofs);
     }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       if constexpr (B_T)
-        fb[slot][j] = frag_t(bs, LoadKT<BN>::PT, wn * WN + j * 32, ks, lane);
+        fb[slot][j] = frag_t(bs, LoadKT<BN, NTH>::PT, wn * WN + j * 32, ks, lane);
       else
         fb[slot][j] = frag(bs + (brow(j) + (lane & 31)) * LDSK + ks * 16 + kofs);
     }
@@ -346,26 +347,24 @@ __global__ __launch_bounds__(NT) void gemm_kernel(mt_gemm_args p, int nm, int nn
   }
 }
 
-template <int LAYOUT, int EPI, int BM, int BN>
+template <int LAYOUT, int EPI, int BM, int BN, int WVM, int WVN>
 hipError_t launch_tiles(const mt_gemm_args& a, hipStream_t s) {
   const int nn = (int)((EPI == MT_EPI_SWIGLU) ? (a.N + BN / 2 - 1) / (BN / 2) : (a.N + BN - 1) / BN);
   const int nm = (int)((a.M + BM - 1) / BM);
   const int per = (nm * nn + NXCD - 1) / NXCD;
-  hipLaunchKernelGGL((gemm_kernel<LAYOUT, EPI, BM, BN>), dim3((unsigned)(per * NXCD)), dim3(NT), 0,
-                     s, a, nm, nn);
+  hipLaunchKernelGGL((gemm_kernel<LAYOUT, EPI, BM, BN, WVM, WVN>), dim3((unsigned)(per * NXCD)),
+                     dim3(64 * WVM * WVN), 0, s, a, nm, nn);
   return hipGetLastError();
 }
 
-// 256 x 256 tiles when the product has enough of them to fill the chip,
-// 128 x 128 otherwise.
+// 256 x 256 tiles (8 waves of 128 x 64: two waves per SIMD) when the product
+// has enough of them to fill the chip, 128 x 128 (4 waves) otherwise.
 template <int LAYOUT, int EPI>
 hipError_t launch_one(const mt_gemm_args& a, hipStream_t s) {
   const int64_t nbig = ((a.M + 255) / 256) * ((a.N + 255) / 256);
-  // (the SwiGLU-backward epilogue does not fit the 256 x 256 register budget)
-  if constexpr (EPI != MT_EPI_SWIGLU_BWD) {
-    if (a.M >= 1024 && a.N >= 1024 && nbig >= 128) return launch_tiles<LAYOUT, EPI, 256, 256>(a, s);
-  }
-  return launch_tiles<LAYOUT, EPI, 128, 128>(a, s);
+  if (a.M >= 1024 && a.N >= 1024 && nbig >= 128)
+    return launch_tiles<LAYOUT, EPI, 256, 256, 2, 4>(a, s);
+  return launch_tiles<LAYOUT, EPI, 128, 128, 2, 2>(a, s);
 }
 
 }  // namespace
