@@ -360,13 +360,17 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
 // Key block outer (4 waves x 32 keys, one key per lane), so grouped query
 // heads are summed in a fixed order without atomics.  The (query head, query
 // tile) pairs after the block form one sequence of 64-row Q / dO tiles, double
-// buffered with their LSE and D rows; dV^T += dO^T P and dK^T += Q^T dS read
-// dO^T and Q^T from the same tiles through transpose reads.
-template <int D>
-__global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
-    const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dout,
-    const float* __restrict__ lse, const float* __restrict__ dsum, uint16_t* __restrict__ dqkv,
-    int seq, int nq, int nkv, int64_t T) {
+// buffered with their LSE and D rows.  dV^T += dO^T P and dK^T += Q^T dS take
+// dO^T and Q^T from the same tiles through transpose reads.  dK and dV are two
+// launches of this kernel (DK selects which): each then holds one accumulator
+// and fits two waves per SIMD, at the price of recomputing P in both.
+template <int D, bool DK>
+__device__ __forceinline__ void dkdv_body(const uint16_t* __restrict__ qkv,
+                                          const uint16_t* __restrict__ dout,
+                                          const float* __restrict__ lse,
+                                          const float* __restrict__ dsum,
+                                          uint16_t* __restrict__ dqkv, int seq, int nq, int nkv,
+                                          int64_t T) {
   constexpr int BQ = 64, KS = D / 16, DT = D / 32;
   __shared__ __attribute__((aligned(16))) uint16_t Qs[2][BQ * PITCH];
   __shared__ __attribute__((aligned(16))) uint16_t Os[2][BQ * PITCH];  // dO
@@ -386,18 +390,15 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
 
   const int kw0 = kvb * 128 + w * 32;
   const int kv = kw0 + (lane & 31);
-  bf16x8_t kf[KS], vf[KS];
+  bf16x8_t kf[KS], vf[DK ? KS : 1];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     kf[ks] = ld_frag(Kp + (row0 + kv) * ld + ks * 16 + g * 8);
-    vf[ks] = ld_frag(Vp + (row0 + kv) * ld + ks * 16 + g * 8);
+    if constexpr (DK) vf[ks] = ld_frag(Vp + (row0 + kv) * ld + ks * 16 + g * 8);
   }
-  f32x16_t adk[DT], adv[DT];
+  f32x16_t acc[DT];
 #pragma unroll
-  for (int dd = 0; dd < DT; ++dd) {
-    zero(adk[dd]);
-    zero(adv[dd]);
-  }
+  for (int dd = 0; dd < DT; ++dd) zero(acc[dd]);
   const int qt0 = (kvb * 128) / BQ, nqt = seq / BQ;
   const int per_head = nqt - qt0, n_it = grp * per_head;
 
@@ -410,7 +411,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
     co.load(dout + j * D + (row0 + q0) * ldo, ldo, tid);
     if (tid < BQ)
       stat = lse[(int64_t)j * T + row0 + q0 + tid] * LOG2E;
-    else if (tid < 2 * BQ)
+    else if (DK && tid < 2 * BQ)
       stat = dsum[(int64_t)j * T + row0 + q0 + tid - BQ];
   };
   auto sstore = [&](int buf) {
@@ -418,7 +419,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
     co.store(Os[buf], tid);
     if (tid < BQ)
       Ls[buf][tid] = stat;
-    else if (tid < 2 * BQ)
+    else if (DK && tid < 2 * BQ)
       Ds[buf][tid - BQ] = stat;
   };
   gload(0);
@@ -439,64 +440,78 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
       for (int i = 0; i < 2; ++i) {
         f32x16_t sc, dp;
         zero(sc);
-        zero(dp);
+        if constexpr (DK) zero(dp);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           sc = mfma(row_frag(qs_t, i * 32, ks * 16, lane), kf[ks], sc);
-          dp = mfma(row_frag(os_t, i * 32, ks * 16, lane), vf[ks], dp);
+          if constexpr (DK) dp = mfma(row_frag(os_t, i * 32, ks * 16, lane), vf[ks], dp);
         }
-        f32x16_t pv;
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int ql = i * 32 + rr * 8 + g * 4;
           const float4 l4 = *reinterpret_cast<const float4*>(&Ls[cur][ql]);
-          const float4 d4 = *reinterpret_cast<const float4*>(&Ds[cur][ql]);
           const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-          const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+          float dv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+          if constexpr (DK) {
+            const float4 d4 = *reinterpret_cast<const float4*>(&Ds[cur][ql]);
+            dv[0] = d4.x; dv[1] = d4.y; dv[2] = d4.z; dv[3] = d4.w;
+          }
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = rr * 4 + e;
             const float pr = (!diag || kv <= q0 + ql + e) ? exp2f(sc[r] * sl2 - lv[e]) : 0.0f;
-            pv[r] = pr;
-            sc[r] = pr * (dp[r] - dv[e]);
+            sc[r] = DK ? pr * (dp[r] - dv[e]) : pr;  // dS for dK, P for dV
           }
         }
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          const bf16x8_t pf = as_frag(u32x4{pack_bf2(pv[hh * 8 + 0], pv[hh * 8 + 1]),
-                                            pack_bf2(pv[hh * 8 + 2], pv[hh * 8 + 3]),
-                                            pack_bf2(pv[hh * 8 + 4], pv[hh * 8 + 5]),
-                                            pack_bf2(pv[hh * 8 + 6], pv[hh * 8 + 7])});
-          const bf16x8_t sf = as_frag(u32x4{pack_bf2(sc[hh * 8 + 0], sc[hh * 8 + 1]),
-                                            pack_bf2(sc[hh * 8 + 2], sc[hh * 8 + 3]),
-                                            pack_bf2(sc[hh * 8 + 4], sc[hh * 8 + 5]),
-                                            pack_bf2(sc[hh * 8 + 6], sc[hh * 8 + 7])});
+          const bf16x8_t f = as_frag(u32x4{pack_bf2(sc[hh * 8 + 0], sc[hh * 8 + 1]),
+                                           pack_bf2(sc[hh * 8 + 2], sc[hh * 8 + 3]),
+                                           pack_bf2(sc[hh * 8 + 4], sc[hh * 8 + 5]),
+                                           pack_bf2(sc[hh * 8 + 6], sc[hh * 8 + 7])});
 #pragma unroll
-          for (int dd = 0; dd < DT; ++dd) {
-            adv[dd] = mfma(tr_frag(os_t, i * 32 + hh * 16, dd * 32, lane), pf, adv[dd]);
-            adk[dd] = mfma(tr_frag(qs_t, i * 32 + hh * 16, dd * 32, lane), sf, adk[dd]);
-          }
+          for (int dd = 0; dd < DT; ++dd)
+            acc[dd] = mfma(tr_frag(DK ? qs_t : os_t, i * 32 + hh * 16, dd * 32, lane), f, acc[dd]);
         }
       }
     }
     if (more) sstore(cur ^ 1);
     __syncthreads();
   }
-  const float scale = 1.0f / sqrtf((float)D);
-  uint16_t* dk = dqkv + (row0 + kv) * ld + (int64_t)nq * D + kvh * D;
-  uint16_t* dv = dqkv + (row0 + kv) * ld + (int64_t)(nq + nkv) * D + kvh * D;
+  const float scale = DK ? 1.0f / sqrtf((float)D) : 1.0f;
+  uint16_t* dst = dqkv + (row0 + kv) * ld + (int64_t)(DK ? nq : nq + nkv) * D + kvh * D;
 #pragma unroll
   for (int dd = 0; dd < DT; ++dd)
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       const int d = dd * 32 + rr * 8 + g * 4;
-      u32x2 k2{pack_bf2(adk[dd][rr * 4 + 0] * scale, adk[dd][rr * 4 + 1] * scale),
-               pack_bf2(adk[dd][rr * 4 + 2] * scale, adk[dd][rr * 4 + 3] * scale)};
-      u32x2 v2{pack_bf2(adv[dd][rr * 4 + 0], adv[dd][rr * 4 + 1]),
-               pack_bf2(adv[dd][rr * 4 + 2], adv[dd][rr * 4 + 3])};
-      *reinterpret_cast<u32x2*>(dk + d) = k2;
-      *reinterpret_cast<u32x2*>(dv + d) = v2;
+      u32x2 v2{pack_bf2(acc[dd][rr * 4 + 0] * scale, acc[dd][rr * 4 + 1] * scale),
+               pack_bf2(acc[dd][rr * 4 + 2] * scale, acc[dd][rr * 4 + 3] * scale)};
+      *reinterpret_cast<u32x2*>(dst + d) = v2;
     }
+}
+
+// dK holds both K and V fragments: at two waves per SIMD a few registers
+// spill, which still beats one wave per SIMD (7B shape: backward 1.76 ms
+// against 2.12 ms).
+#ifndef MT_DK_WAVES_PER_SIMD
+#define MT_DK_WAVES_PER_SIMD 2
+#endif
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void attn_bwd_dv_kernel(
+    const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dout,
+    const float* __restrict__ lse, const float* __restrict__ dsum, uint16_t* __restrict__ dqkv,
+    int seq, int nq, int nkv, int64_t T) {
+  dkdv_body<D, false>(qkv, dout, lse, dsum, dqkv, seq, nq, nkv, T);
+}
+
+template <int D>
+__global__ __launch_bounds__(256, MT_DK_WAVES_PER_SIMD) void attn_bwd_dk_kernel(
+    const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dout,
+    const float* __restrict__ lse, const float* __restrict__ dsum, uint16_t* __restrict__ dqkv,
+    int seq, int nq, int nkv, int64_t T) {
+  dkdv_body<D, true>(qkv, dout, lse, dsum, dqkv, seq, nq, nkv, T);
 }
 
 template <int D>
@@ -515,7 +530,9 @@ hipError_t bwd_d(const uint16_t* qkv, const uint16_t* o, const uint16_t* dout, c
   const int64_t n = T * nq;
   hipLaunchKernelGGL(attn_dsum_kernel<D>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, o,
                      dout, dsum, nq, T);
-  hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, dim3(seq / 128, nkv, batch), dim3(256), 0, s, qkv,
+  hipLaunchKernelGGL(attn_bwd_dv_kernel<D>, dim3(seq / 128, nkv, batch), dim3(256), 0, s, qkv,
+                     dout, lse, dsum, dqkv, seq, nq, nkv, T);
+  hipLaunchKernelGGL(attn_bwd_dk_kernel<D>, dim3(seq / 128, nkv, batch), dim3(256), 0, s, qkv,
                      dout, lse, dsum, dqkv, seq, nq, nkv, T);
   hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, dim3(seq / 128, nq, batch), dim3(256), 0, s, qkv,
                      dout, lse, dsum, dqkv, seq, nq, nkv, T);
