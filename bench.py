@@ -268,6 +268,8 @@ def main():
     ap.add_argument("--drain-workgroups", type=int, default=None,
                     help="slab drain: 0 = DMA engine, n = copy kernel of n workgroups "
                          "(default: the library's)")
+    ap.add_argument("--grad-slabs", type=int, default=0,
+                    help="override the configuration's gradient slab count")
     ap.add_argument("--micro-batch", type=int, default=0,
                     help="override the configuration's sequences per micro-batch")
     ap.add_argument("--grad-accum", type=int, default=0,
@@ -293,9 +295,10 @@ def main():
     from synth_inputs import PRESETS, make_batch, weight_stream
 
     cfg = PRESETS[args.config]
-    if args.micro_batch or args.grad_accum:
+    if args.micro_batch or args.grad_accum or args.grad_slabs:
         cfg = cfg.replace(micro_batch=args.micro_batch or cfg.micro_batch,
-                          grad_accum=args.grad_accum or cfg.grad_accum)
+                          grad_accum=args.grad_accum or cfg.grad_accum,
+                          n_grad_slabs=args.grad_slabs or cfg.n_grad_slabs)
     if args.probe:
         for row in probe(cfg):
             print(json.dumps(row), flush=True)
@@ -369,7 +372,8 @@ def main():
         ach = dom["bytes"] / (dom["ms"] * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": ach / HBM_PEAK_GBPS}
-    traffic = measured_traffic(dom["name"], cfg.name, not (args.micro_batch or args.grad_accum))
+    traffic = measured_traffic(dom["name"], cfg.name,
+                               not (args.micro_batch or args.grad_accum or args.grad_slabs))
     roofline.update({"traffic": traffic, "kernel": dom["name"], "launches": dom["launches"],
                      "avg_launch_ms": dom["ms"] / dom["launches"],
                      "algorithmic_per_launch": (dom["flop"] or dom["bytes"]) / dom["launches"],
