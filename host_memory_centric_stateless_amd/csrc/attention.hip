@@ -37,6 +37,10 @@ __device__ inline bf16x8_t as_frag(u32x4 v) { return __builtin_bit_cast(bf16x8_t
 __device__ inline bf16x8_t ld_frag(const uint16_t* p) {
   return as_frag(*reinterpret_cast<const u32x4*>(p));
 }
+// 2^x on the hardware exponential unit.  Arguments here are max-subtracted
+// (<= 0) logits; results that would be denormal are negligible against the
+// row sum, so the library's denormal-range scaling is not needed.
+__device__ inline float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ inline f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -175,7 +179,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
         }
       mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
       const float m_new = fmaxf(m_run, mloc);
-      const float alpha = exp2f(m_run - m_new);
+      const float alpha = exp2_hw(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
@@ -186,7 +190,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float pr = exp2f(sc[i][r] - m_new);
+          const float pr = exp2_hw(sc[i][r] - m_new);
           sc[i][r] = pr;
           l_run += pr;
         }
@@ -322,7 +326,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int kv = kv0 + i * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-          const float pr = (!diag || kv <= q) ? exp2f(sc[r] * sl2 - lse2) : 0.0f;
+          const float pr = (!diag || kv <= q) ? exp2_hw(sc[r] * sl2 - lse2) : 0.0f;
           sc[r] = pr * (dp[r] - dq_sum);
         }
 #pragma unroll
@@ -459,7 +463,7 @@ __device__ __forceinline__ void dkdv_body(const uint16_t* __restrict__ qkv,
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = rr * 4 + e;
-            const float pr = (!diag || kv <= q0 + ql + e) ? exp2f(sc[r] * sl2 - lv[e]) : 0.0f;
+            const float pr = (!diag || kv <= q0 + ql + e) ? exp2_hw(sc[r] * sl2 - lv[e]) : 0.0f;
             sc[r] = DK ? pr * (dp[r] - dv[e]) : pr;  // dS for dK, P for dV
           }
         }
