@@ -131,6 +131,8 @@ _SIGS = {
     "mt_host_cast_bf16": ([_P, _P, _I64, _I32], C.c_int),
     "mt_host_adamw": ([_P, _P, _P, _P, _P, _I64, C.POINTER(mt_adamw_hparams), _I64, _I32], C.c_int),
     "mt_host_accumulate": ([_P, _P, _I64, _I32, _I32], C.c_int),
+    "mt_host_adamw_slab": ([_P, _P, _P, _P, _P, _P, _I32, _I32, _I64, C.POINTER(mt_adamw_hparams),
+                            _I64, _I32], C.c_int),
     "mt_host_rope_table": ([_I32, _I32, _F, _P, _P], C.c_int),
     "mtk_gemm": ([C.POINTER(mt_gemm_args), _P], C.c_int),
     "mtk_rmsnorm_fwd": ([_P, _P, _P, _P, _I64, _I32, _F, _P], C.c_int),
@@ -275,6 +277,15 @@ def mt_host_cast_bf16(src: np.ndarray, dst: np.ndarray, threads: int = 0):
 def mt_host_adamw(master, grad, m, v, bf16_out, hp: mt_adamw_hparams, step: int, threads: int = 0):
     _check(_lib.mt_host_adamw(_ptr(master), _ptr(grad), _ptr(m), _ptr(v), _ptr(bf16_out),
                               master.size, C.byref(hp), step, threads), "mt_host_adamw")
+
+
+def mt_host_adamw_slab(master, grad, m, v, bf16_out, slab, accumulate: int,
+                       hp: mt_adamw_hparams, step: int, threads: int = 0):
+    """slab: uint16 (bf16 bits) or float32 array of master.size elements."""
+    sb = 1 if slab.dtype == np.uint16 else 0
+    _check(_lib.mt_host_adamw_slab(_ptr(master), _ptr(grad), _ptr(m), _ptr(v), _ptr(bf16_out),
+                                   _ptr(slab), sb, int(accumulate), master.size, C.byref(hp), step,
+                                   threads), "mt_host_adamw_slab")
 
 
 def mt_host_accumulate(grad, src, accumulate: int, threads: int = 0):

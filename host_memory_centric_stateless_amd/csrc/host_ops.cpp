@@ -301,6 +301,21 @@ extern "C" mt_status mt_host_adamw(float* master, const float* grad, float* m, f
   return MT_OK;
 }
 
+extern "C" mt_status mt_host_adamw_slab(float* master, float* grad, float* m, float* v,
+                                        uint16_t* bf16_out, const void* slab, int32_t slab_bf16,
+                                        int32_t accumulate_flag, int64_t n,
+                                        const mt_adamw_hparams* hp, int64_t step,
+                                        int32_t threads) {
+  if (n < 0 || !hp || step < 1) return MT_E_ARG;
+  if ((slab_bf16 != 0 && slab_bf16 != 1) || (accumulate_flag != 0 && accumulate_flag != 1))
+    return MT_E_ARG;
+  if (n > 0 && (!master || !grad || !m || !v || !slab)) return MT_E_ARG;
+  ThreadPool pool(nthreads(threads));
+  adamw_slab(pool, master, grad, m, v, bf16_out, slab, slab_bf16 != 0, accumulate_flag != 0, n,
+             *hp, step);
+  return MT_OK;
+}
+
 extern "C" mt_status mt_host_accumulate(float* grad, const float* src, int64_t n,
                                         int32_t accumulate_flag, int32_t threads) {
   if (n < 0 || (n > 0 && (!grad || !src))) return MT_E_ARG;

@@ -257,6 +257,14 @@ mt_status mt_host_cast_bf16(const float* src, uint16_t* dst, int64_t n, int32_t 
 mt_status mt_host_adamw(float* master, const float* grad, float* m, float* v, uint16_t* bf16_out,
                         int64_t n, const mt_adamw_hparams* hp, int64_t step, int32_t threads);
 
+/* The optimizer thread's pass for a unit's last gradient slab of a step:
+ * grad = (accumulate ? grad : 0) + slab, then one AdamW step on that gradient
+ * (as mt_host_accumulate followed by mt_host_adamw, bit for bit).  slab holds
+ * n bf16 values (slab_bf16 = 1) or n fp32 values (0). */
+mt_status mt_host_adamw_slab(float* master, float* grad, float* m, float* v, uint16_t* bf16_out,
+                             const void* slab, int32_t slab_bf16, int32_t accumulate, int64_t n,
+                             const mt_adamw_hparams* hp, int64_t step, int32_t threads);
+
 /* grad = src (accumulate = 0) or grad += src (accumulate = 1). */
 mt_status mt_host_accumulate(float* grad, const float* src, int64_t n, int32_t accumulate,
                              int32_t threads);

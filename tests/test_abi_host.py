@@ -141,6 +141,33 @@ def test_host_accumulate():
     np.testing.assert_array_equal(g, a + b)
 
 
+@pytest.mark.parametrize("slab_bf16", [True, False])
+@pytest.mark.parametrize("accumulate", [0, 1])
+def test_host_adamw_slab_equals_accumulate_then_adamw(slab_bf16, accumulate):
+    """The optimizer thread's fused pass (add the last slab, then AdamW) must
+    give bit for bit what the separate accumulate and AdamW give."""
+    rng = np.random.default_rng(7)
+    n = 1_000_003
+    master = rng.standard_normal(n).astype(np.float32) * np.float32(0.02)
+    grad0 = rng.standard_normal(n).astype(np.float32) * np.float32(1e-3)
+    m0 = rng.standard_normal(n).astype(np.float32) * np.float32(1e-4)
+    v0 = np.abs(rng.standard_normal(n)).astype(np.float32) * np.float32(1e-7)
+    g32 = rng.standard_normal(n).astype(np.float32) * np.float32(1e-3)
+    slab = ((g32.view(np.uint32) + np.uint32(0x8000)) >> np.uint32(16)).astype(np.uint16) \
+        if slab_bf16 else g32
+    slab_f32 = (slab.astype(np.uint32) << np.uint32(16)).view(np.float32) if slab_bf16 else slab
+    hp = mt.mt_adamw_hparams(1e-3, 0.9, 0.999, 1e-8, 0.01)
+    a = [x.copy() for x in (master, grad0, m0, v0)]
+    bf_a = np.zeros(n, np.uint16)
+    mt.mt_host_accumulate(a[1], slab_f32, accumulate, threads=3)
+    mt.mt_host_adamw(a[0], a[1], a[2], a[3], bf_a, hp, 2, threads=3)
+    b = [x.copy() for x in (master, grad0, m0, v0)]
+    bf_b = np.zeros(n, np.uint16)
+    mt.mt_host_adamw_slab(b[0], b[1], b[2], b[3], bf_b, slab, accumulate, hp, 2, threads=5)
+    for x, y, name in zip(a + [bf_a], b + [bf_b], ["master", "grad", "m", "v", "bf16"]):
+        np.testing.assert_array_equal(x, y, err_msg=name)
+
+
 @pytest.mark.parametrize("s,d", [(128, 64), (4096, 128), (131072, 128)])
 def test_rope_table_matches_oracle(s, d):
     c, sn = mt.mt_host_rope_table(s, d, 10000.0)
