@@ -22,12 +22,19 @@
 //     from its checkpoint, then runs its blocks backwards (zhichai design
 //     point 3; lqnn 三.4).
 //
-// MI355X choices (not from the pages): which buffer a load goes into is
-// decided ahead of time by simulating the two buffers over the whole
-// micro-batch (a unit still resident is reused instead of re-copied, e.g. the
-// last layers of a segment when its backward starts); the forward of the last
-// segment writes the window directly, so that segment is not recomputed; the
-// LM head is streamed through the same buffers in vocabulary chunks.
+// MI355X choices (not from the pages):
+//   * which buffer a load goes into is decided ahead of time by simulating the
+//     two buffers over the whole pass (a unit still resident is reused
+//     instead of re-copied, e.g. the last layers of a segment when its
+//     backward starts); the forward of the last segment writes the window
+//     directly, so that segment is not recomputed; the LM head is streamed
+//     through the same buffers in vocabulary chunks;
+//   * slabs drain through a small copy kernel writing pinned host memory;
+//   * with mt_backward_step, each unit's last slab of the step is added and
+//     stepped by AdamW in one host pass on the optimizer thread, units served
+//     in the order the next forward reads them;
+//   * optionally several micro-batches share one pass (layer-major gradient
+//     accumulation, mt_config.micro_batches_per_pass).
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
