@@ -32,6 +32,11 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
+// Word 3 of a raw (unformatted, unswizzled) buffer resource on gfx9-family
+// parts: 32-bit data format, no index stride.
+constexpr int BUF_FLAGS = 0x00020000;
+// log2 headroom of the forward's lazily updated running maximum
+constexpr float RESCALE_SLACK = 8.0f;
 
 __device__ inline bf16x8_t as_frag(u32x4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 __device__ inline bf16x8_t ld_frag(const uint16_t* p) {
@@ -49,6 +54,15 @@ __device__ inline void zero(f32x16_t& a) {
   for (int r = 0; r < 16; ++r) a[r] = 0.0f;
 }
 
+// Makes a value loaded before a loop count as used right here, so its load is
+// waited for once, ahead of the loop.  Otherwise the compiler sinks such loads
+// to the loop entry, and the wait counter, merged over the back edge, then has
+// every iteration wait for the next tile's prefetch as well.
+template <class T>
+__device__ inline void settle(const T& v) {
+  asm volatile("" ::"v"(v));
+}
+
 // LDS tiles are [ROWS][D] row-major copies of global rows (pitch PITCH
 // elements), read two ways: 16-byte row reads (MFMA operand with rows = tile
 // rows, k = d) and transpose reads (operand with rows = d, k = tile rows).
@@ -58,19 +72,33 @@ __device__ inline void zero(f32x16_t& a) {
 constexpr int PITCH = 152;
 
 // Global -> registers -> LDS copy of one [ROWS][D] tile by 256 threads, split
-// so that the global loads can be issued a tile ahead of the LDS stores.
+// so that the global loads can be issued a tile ahead of the LDS stores.  The
+// loads are buffer loads: a wave-uniform resource for the tile plus a 32-bit
+// per-lane byte offset fixed for the whole kernel, so no address register is
+// rewritten while a load is in flight and there is no per-tile 64-bit address
+// arithmetic.
 template <int ROWS, int D>
 struct TileCopy {
   static constexpr int VPR = D / 8;                // 16-byte vectors per row
   static constexpr int V = ROWS * VPR / 256;       // vectors per thread
   static_assert(V >= 1 && ROWS * VPR % 256 == 0, "tile does not split over 256 threads");
   u32x4 r[V];
-  __device__ inline void load(const uint16_t* src, int64_t ld, int tid) {
+  uint32_t off[V];
+  int span;  // bytes from the tile's first element to the end of its last row
+  __device__ inline TileCopy(int64_t ld, int tid) {
 #pragma unroll
     for (int i = 0; i < V; ++i) {
       const int idx = tid + 256 * i;
-      r[i] = *reinterpret_cast<const u32x4*>(src + (int64_t)(idx / VPR) * ld + (idx % VPR) * 8);
+      off[i] = (uint32_t)(((int64_t)(idx / VPR) * ld + (idx % VPR) * 8) * 2);
     }
+    span = (int)(((int64_t)(ROWS - 1) * ld + D) * 2);
+  }
+  __device__ inline void load(const uint16_t* src) {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(src), (short)0, span, BUF_FLAGS);
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+      r[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off[i], 0, 0));
   }
   __device__ inline void store(uint16_t* lds, int tid) const {
 #pragma unroll
@@ -120,7 +148,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BKV * PITCH];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BKV * PITCH];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, known uniform
   const int qb = gridDim.x - 1 - blockIdx.x;
   const int j = blockIdx.y, b = blockIdx.z;
   const int kvh = j / (nq / nkv);
@@ -142,19 +171,21 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
   for (int dd = 0; dd < DT; ++dd) zero(acc[dd]);
   float m_run = -INFINITY, l_run = 0.0f;
 
-  TileCopy<BKV, D> ck, cv;
+  TileCopy<BKV, D> ck(ld, tid), cv(ld, tid);
   const int nkb = (qb * 128 + 127) / BKV + 1;  // key tiles up to the block's last query
-  ck.load(Kp + row0 * ld, ld, tid);
-  cv.load(Vp + row0 * ld, ld, tid);
+  ck.load(Kp + row0 * ld);
+  cv.load(Vp + row0 * ld);
   ck.store(Ks[0], tid);
   cv.store(Vs[0], tid);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) settle(qf[ks]);
   __syncthreads();
   for (int kb = 0; kb < nkb; ++kb) {
     const int cur = kb & 1, kv0 = kb * BKV;
     const bool more = kb + 1 < nkb;
     if (more) {
-      ck.load(Kp + (row0 + kv0 + BKV) * ld, ld, tid);
-      cv.load(Vp + (row0 + kv0 + BKV) * ld, ld, tid);
+      ck.load(Kp + (row0 + kv0 + BKV) * ld);
+      cv.load(Vp + (row0 + kv0 + BKV) * ld);
     }
     if (kv0 <= q0 + 31) {
       const uint16_t* ks_t = Ks[cur];
@@ -166,31 +197,40 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) sc[i] = mfma(row_frag(ks_t, i * 32, ks * 16, lane), qf[ks], sc[i]);
       }
-      const bool diag = kv0 + BKV - 1 > q0;  // some keys of this tile lie after some queries
+      // causal mask only where some key of the tile lies after some query of
+      // the wave (wave-uniform branch)
+      if (kv0 + BKV - 1 > q0) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (kv0 + i * 32 + (r >> 2) * 8 + g * 4 + (r & 3) > q) sc[i][r] = -INFINITY;
+      }
       float mloc = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kv = kv0 + i * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-          const float v = (!diag || kv <= q) ? sc[i][r] * sl2 : -INFINITY;
-          sc[i][r] = v;
-          mloc = fmaxf(mloc, v);
-        }
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-      const float m_new = fmaxf(m_run, mloc);
-      const float alpha = exp2_hw(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
+        for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sc[i][r]);
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32)) * sl2;
+      // The running maximum only has to bound the exponents, not equal the
+      // row maximum: it moves (and the accumulator is rescaled) only when a
+      // row's maximum exceeds it by more than RESCALE_SLACK, so probabilities
+      // stay below 2^RESCALE_SLACK and most tiles skip the rescale.
+      const bool grow = mloc > m_run + RESCALE_SLACK;
+      if (__ballot(grow)) {
+        const float alpha = grow ? exp2_hw(m_run - mloc) : 1.0f;
+        m_run = grow ? mloc : m_run;
+        l_run *= alpha;
 #pragma unroll
-      for (int dd = 0; dd < DT; ++dd)
+        for (int dd = 0; dd < DT; ++dd)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[dd][r] *= alpha;
+          for (int r = 0; r < 16; ++r) acc[dd][r] *= alpha;
+      }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float pr = exp2_hw(sc[i][r] - m_new);
+          const float pr = exp2_hw(fmaf(sc[i][r], sl2, -m_run));
           sc[i][r] = pr;
           l_run += pr;
         }
@@ -266,7 +306,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BKV * PITCH];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BKV * PITCH];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, known uniform
   const int qb = gridDim.x - 1 - blockIdx.x;
   const int j = blockIdx.y, b = blockIdx.z;
   const int kvh = j / (nq / nkv);
@@ -293,19 +334,26 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
 #pragma unroll
   for (int dd = 0; dd < DT; ++dd) zero(acc[dd]);
 
-  TileCopy<BKV, D> ck, cv;
+  TileCopy<BKV, D> ck(ld, tid), cv(ld, tid);
   const int nkb = (qb * 128 + 127) / BKV + 1;
-  ck.load(Kp + row0 * ld, ld, tid);
-  cv.load(Vp + row0 * ld, ld, tid);
+  ck.load(Kp + row0 * ld);
+  cv.load(Vp + row0 * ld);
   ck.store(Ks[0], tid);
   cv.store(Vs[0], tid);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    settle(qf[ks]);
+    settle(df[ks]);
+  }
+  settle(lse2);
+  settle(dq_sum);
   __syncthreads();
   for (int kb = 0; kb < nkb; ++kb) {
     const int cur = kb & 1, kv0 = kb * BKV;
     const bool more = kb + 1 < nkb;
     if (more) {
-      ck.load(Kp + (row0 + kv0 + BKV) * ld, ld, tid);
-      cv.load(Vp + (row0 + kv0 + BKV) * ld, ld, tid);
+      ck.load(Kp + (row0 + kv0 + BKV) * ld);
+      cv.load(Vp + (row0 + kv0 + BKV) * ld);
     }
     if (kv0 <= q0 + 31) {
       const uint16_t* ks_t = Ks[cur];
@@ -323,12 +371,13 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
           sc = mfma(row_frag(ks_t, i * 32, ks * 16, lane), qf[ks], sc);
           dp = mfma(row_frag(vs_t, i * 32, ks * 16, lane), df[ks], dp);
         }
+        if (diag) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kv = kv0 + i * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-          const float pr = (!diag || kv <= q) ? exp2_hw(sc[r] * sl2 - lse2) : 0.0f;
-          sc[r] = pr * (dp[r] - dq_sum);
+          for (int r = 0; r < 16; ++r)
+            if (kv0 + i * 32 + (r >> 2) * 8 + g * 4 + (r & 3) > q) sc[r] = -INFINITY;
         }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[r] = exp2_hw(fmaf(sc[r], sl2, -lse2)) * (dp[r] - dq_sum);
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           const bf16x8_t sf = as_frag(u32x4{pack_bf2(sc[hh * 8 + 0], sc[hh * 8 + 1]),
@@ -381,7 +430,8 @@ __device__ __forceinline__ void dkdv_body(const uint16_t* __restrict__ qkv,
   __shared__ __attribute__((aligned(16))) float Ls[2][BQ];
   __shared__ __attribute__((aligned(16))) float Ds[2][BQ];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, known uniform
   const int kvb = gridDim.x - 1 - blockIdx.x;
   const int kvh = blockIdx.y, b = blockIdx.z;
   const int grp = nq / nkv;
@@ -406,28 +456,37 @@ __device__ __forceinline__ void dkdv_body(const uint16_t* __restrict__ qkv,
   const int qt0 = (kvb * 128) / BQ, nqt = seq / BQ;
   const int per_head = nqt - qt0, n_it = grp * per_head;
 
-  TileCopy<BQ, D> cq, co;
-  float stat = 0.0f;  // threads 0..63: LSE row, 64..127: D row of the tile
+  TileCopy<BQ, D> cq(ld, tid), co(ldo, tid);
+  // Each wave also reads one 64-row statistics vector of the tile (BQ is the
+  // wave size): wave 1 the D rows (dK only), every other wave the LSE rows;
+  // waves 0 and 1 keep theirs.
+  static_assert(BQ == 64, "one statistics row per lane");
+  const float* stat_src = (DK && w == 1) ? dsum : lse;
+  float stat = 0.0f;
   auto gload = [&](int it) {
     const int j = kvh * grp + it / per_head;
     const int q0 = (qt0 + it % per_head) * BQ;
-    cq.load(qkv + j * D + (row0 + q0) * ld, ld, tid);
-    co.load(dout + j * D + (row0 + q0) * ldo, ldo, tid);
-    if (tid < BQ)
-      stat = lse[(int64_t)j * T + row0 + q0 + tid] * LOG2E;
-    else if (DK && tid < 2 * BQ)
-      stat = dsum[(int64_t)j * T + row0 + q0 + tid - BQ];
+    cq.load(qkv + j * D + (row0 + q0) * ld);
+    co.load(dout + j * D + (row0 + q0) * ldo);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(stat_src + (int64_t)j * T + row0 + q0), (short)0, BQ * 4, BUF_FLAGS);
+    stat = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, lane * 4, 0, 0));
   };
   auto sstore = [&](int buf) {
     cq.store(Qs[buf], tid);
     co.store(Os[buf], tid);
-    if (tid < BQ)
-      Ls[buf][tid] = stat;
-    else if (DK && tid < 2 * BQ)
-      Ds[buf][tid - BQ] = stat;
+    if (w == 0)
+      Ls[buf][lane] = stat * LOG2E;
+    else if (DK && w == 1)
+      Ds[buf][lane] = stat;
   };
   gload(0);
   sstore(0);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    settle(kf[ks]);
+    if constexpr (DK) settle(vf[ks]);
+  }
   __syncthreads();
   for (int it = 0; it < n_it; ++it) {
     const int cur = it & 1;
@@ -460,10 +519,15 @@ __device__ __forceinline__ void dkdv_body(const uint16_t* __restrict__ qkv,
             const float4 d4 = *reinterpret_cast<const float4*>(&Ds[cur][ql]);
             dv[0] = d4.x; dv[1] = d4.y; dv[2] = d4.z; dv[3] = d4.w;
           }
+          if (diag) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (kv > q0 + ql + e) sc[rr * 4 + e] = -INFINITY;
+          }
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = rr * 4 + e;
-            const float pr = (!diag || kv <= q0 + ql + e) ? exp2_hw(sc[r] * sl2 - lv[e]) : 0.0f;
+            const float pr = exp2_hw(fmaf(sc[r], sl2, -lv[e]));
             sc[r] = DK ? pr * (dp[r] - dv[e]) : pr;  // dS for dK, P for dV
           }
         }

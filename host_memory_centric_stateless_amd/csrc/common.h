@@ -10,17 +10,22 @@
 namespace mt {
 
 // ---------------------------------------------------------------- bf16 bits
-// Round-to-nearest-even fp32 -> bf16; NaN stays a (quiet) NaN.
+// Round-to-nearest-even fp32 -> bf16; NaN stays a (quiet) NaN.  On the GPU
+// this is gfx950's conversion instruction (v_cvt_pk_bf16_f32, two values per
+// instruction), which rounds the same way; the host spells the rounding out.
+typedef __bf16 bf16x2_hw __attribute__((ext_vector_type(2)));
+typedef float f32x2_hw __attribute__((ext_vector_type(2)));
+
 __host__ __device__ inline uint16_t f2bf(float f) {
-  uint32_t u;
 #if defined(__HIP_DEVICE_COMPILE__)
-  u = __float_as_uint(f);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 #else
+  uint32_t u;
   __builtin_memcpy(&u, &f, 4);
-#endif
   if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
   u += 0x7fffu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
+#endif
 }
 
 __host__ __device__ inline float bf2f(uint16_t h) {
@@ -35,7 +40,11 @@ __host__ __device__ inline float bf2f(uint16_t h) {
 }
 
 __host__ __device__ inline uint32_t pack_bf2(float lo, float hi) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_hw){lo, hi}, bf16x2_hw));
+#else
   return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+#endif
 }
 
 // ---------------------------------------------------------------- launchers
