@@ -68,7 +68,7 @@ __global__ __launch_bounds__(NT) void rmsnorm_fwd_kernel(const float* __restrict
 // ------------------------------------------------------------- RMSNorm bwd
 // Workgroup b handles rows [b*R, (b+1)*R) in order and keeps per-column
 // partial sums of dn*xhat in registers; a second kernel adds the partials in
-// block order.
+// a fixed order.
 template <int MAXV>
 __global__ __launch_bounds__(NT) void rmsnorm_bwd_kernel(
     const float* __restrict__ dn, const float* __restrict__ x, const float* __restrict__ rstd,
@@ -144,21 +144,40 @@ __global__ __launch_bounds__(NT) void rmsnorm_bwd_kernel(
   }
 }
 
-__global__ void colsum_kernel(const float* __restrict__ partial, float* __restrict__ out,
-                              uint16_t* __restrict__ out16, int nblk, int h) {
-  const int c = blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= h) return;
-  float s = 0.0f;
-  for (int b = 0; b < nblk; ++b) s += partial[(int64_t)b * h + c];
+// Column sums of the [nblk][h] partials: a workgroup owns 64 columns; wave w
+// adds the block rows b = w (mod 4) in four interleaved chains, and the four
+// waves' sums are then added in wave order (a fixed order for any launch).
+__global__ __launch_bounds__(NT) void colsum_kernel(const float* __restrict__ partial,
+                                                    float* __restrict__ out,
+                                                    uint16_t* __restrict__ out16, int nblk, int h) {
+  __shared__ float sh[4][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c = blockIdx.x * 64 + lane;
+  float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (c < h) {
+    int b = w;
+    for (; b + 12 < nblk; b += 16)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) a[u] += partial[(int64_t)(b + 4 * u) * h + c];
+#pragma unroll
+    for (int u = 0; u < 3; ++u)
+      if (b + 4 * u < nblk) a[u] += partial[(int64_t)(b + 4 * u) * h + c];
+  }
+  sh[w][lane] = (a[0] + a[1]) + (a[2] + a[3]);
+  __syncthreads();
+  if (w != 0 || c >= h) return;
+  const float s = ((sh[0][lane] + sh[1][lane]) + sh[2][lane]) + sh[3][lane];
   if (out16)
     out16[c] = f2bf(s);
   else
     out[c] = s;
 }
 
+// Four rows per workgroup (up to 2048 workgroups), so that several
+// workgroups share each CU and their row loads overlap.
 int64_t bwd_blocks(int64_t T) {
-  int64_t nb = (T + 15) / 16;
-  return nb < 1024 ? nb : 1024;
+  int64_t nb = (T + 3) / 4;
+  return nb < 2048 ? nb : 2048;
 }
 
 // -------------------------------------------------------------------- RoPE
@@ -310,7 +329,7 @@ hipError_t launch_rmsnorm_bwd(const float* dn, const float* x, const float* rstd
   MT_BWD(1) MT_BWD(2) MT_BWD(4) MT_BWD(5) MT_BWD(8) MT_BWD(16)
 #undef MT_BWD
   if (!done) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(colsum_kernel, dim3((h + NT - 1) / NT), dim3(NT), 0, s, partial, dg, dg_bf16,
+  hipLaunchKernelGGL(colsum_kernel, dim3((h + 63) / 64), dim3(NT), 0, s, partial, dg, dg_bf16,
                      (int)nblk, h);
   return hipGetLastError();
 }
