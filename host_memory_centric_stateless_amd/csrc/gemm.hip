@@ -51,28 +51,60 @@ struct RowMap {
   }
 };
 
-// Operand stored [row][k] (k contiguous): R rows x 64 k, R/32 vectors of
-// 16 B per thread.  Out-of-range vectors are zeroed when written to LDS, not
-// when loaded, so no wait on the loads is needed until after the MFMAs.
+// Operand loads are raw buffer loads.  Each thread's byte offsets from the
+// tile's first row (or k-row) are fixed for the whole K loop, so a load is a
+// wave-uniform resource, rebuilt per tile in scalar registers, plus one
+// 32-bit VGPR that is never rewritten (no per-tile 64-bit address arithmetic,
+// and no address register that must outlive its load).  The resource ends
+// where the matrix ends: a read past it returns zeros instead of faulting.
+// Out-of-range vectors are zeroed when written to LDS, not when loaded, so no
+// wait on the loads is needed until after the MFMAs.
+constexpr int BUF_FLAGS = 0x00020000;  // word 3 of a raw buffer resource (gfx9 family)
+
+// Resource from element `off` of an operand to its end (`extent` bytes from
+// the operand's start).  The prefetch after the last tile starts past the end
+// (left <= 0): its resource is empty, so those loads return zeros and touch no
+// memory.  Offsets and extents are multiples of 16 bytes, so a 16-byte load
+// is either wholly inside or wholly outside.
+__device__ inline __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* base, int64_t off,
+                                                   int64_t extent) {
+  const int64_t left = extent - off * 2;
+  const uint32_t n = left <= 0 ? 0u : left > 0xffffffffLL ? 0xffffffffu : (uint32_t)left;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base + off), (short)0, (int)n,
+                                           BUF_FLAGS);
+}
+
+// Operand stored [row][k] (k contiguous): R rows x 64 k, R*8/NTH vectors of
+// 16 B per thread.  The tile's rows are fixed, so their offsets (out-of-range
+// rows clamped to the last valid one) are computed once.
 template <int R, int NTH>
 struct LoadK {
   static constexpr int V = R * 8 / NTH;
+  static_assert(NTH % 8 == 0, "a thread keeps one k chunk");
   u32x4 r[V];
-  uint32_t ok = 0;  // bit i: vector i is inside the matrix
+  uint32_t off[V];
+  uint32_t rok = 0;  // bit i: vector i's row is inside the matrix
+  uint32_t ok = 0;   // bit i: vector i of the current tile is inside the matrix
+  int64_t row_base = 0;
   template <class Map>
-  __device__ inline void load(const uint16_t* base, int64_t ld, const Map& rm, int64_t k0,
-                              int64_t K, int tid) {
-    ok = 0;
+  __device__ inline void init(int64_t ld, const Map& rm, int tid) {
+    row_base = rm.row0;
 #pragma unroll
     for (int i = 0; i < V; ++i) {
       const int idx = tid + NTH * i;
-      const int64_t k = k0 + (idx & 7) * 8;
-      bool rok;
-      const int64_t g = rm.map(idx >> 3, rok);
-      const bool in = rok && k < K;
-      ok |= (uint32_t)in << i;
-      r[i] = *reinterpret_cast<const u32x4*>(base + g * ld + (in ? k : 0));
+      bool in;
+      const int64_t g = rm.map(idx >> 3, in);
+      rok |= (uint32_t)in << i;
+      off[i] = (uint32_t)(((g - row_base) * ld + (idx & 7) * 8) * 2);
     }
+  }
+  __device__ inline void load(const uint16_t* base, int64_t ld, int64_t extent, int64_t k0,
+                              int64_t K, int tid) {
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(base, row_base * ld + k0, extent);
+    ok = (k0 + (tid & 7) * 8 < K) ? rok : 0u;
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+      r[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off[i], 0, 0));
   }
   __device__ inline void store(uint16_t* lds, int tid) const {
 #pragma unroll
@@ -95,20 +127,29 @@ struct LoadKT {
   static constexpr int VPR = R / 8;          // 16-byte vectors per k-row
   static constexpr int V = 64 * VPR / NTH;   // vectors per thread
   static constexpr int LDS_ELEMS = 64 * PT;
+  static_assert(NTH % VPR == 0, "a thread keeps one row chunk");
   u32x4 r[V];
-  uint32_t ok = 0;  // bit i: vector i is inside the matrix
-  // nrows is a multiple of 8, so a vector is wholly inside or outside.
-  __device__ inline void load(const uint16_t* base, int64_t ld, int64_t row0, int64_t nrows,
-                              int64_t k0, int64_t K, int tid) {
-    ok = 0;
+  uint32_t off[V];
+  bool rin = false;  // this thread's 8 rows are inside the matrix (nrows is a multiple of 8)
+  uint32_t ok = 0;
+  int64_t row0 = 0;
+  __device__ inline void init(int64_t ld, int64_t row0_, int64_t nrows, int tid) {
+    row0 = row0_;
+    rin = row0 + (tid % VPR) * 8 < nrows;
 #pragma unroll
     for (int i = 0; i < V; ++i) {
       const int idx = tid + NTH * i;
-      const int64_t k = k0 + idx / VPR;
-      const int64_t row = row0 + (idx % VPR) * 8;
-      const bool in = k < K && row < nrows;
-      ok |= (uint32_t)in << i;
-      r[i] = *reinterpret_cast<const u32x4*>(base + (in ? k * ld + row : 0));
+      off[i] = (uint32_t)(((int64_t)(idx / VPR) * ld + (idx % VPR) * 8) * 2);
+    }
+  }
+  __device__ inline void load(const uint16_t* base, int64_t ld, int64_t extent, int64_t k0,
+                              int64_t K, int tid) {
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(base, k0 * ld + row0, extent);
+    ok = 0;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      ok |= (uint32_t)(rin && k0 + (tid + NTH * i) / VPR < K) << i;
+      r[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off[i], 0, 0));
     }
   }
   __device__ inline void store(uint16_t* lds, int tid) const {
@@ -200,12 +241,18 @@ __global__ __launch_bounds__(64 * WVM * WVN) void gemm_kernel(mt_gemm_args p, in
 
   typename std::conditional<A_T, LoadKT<BM, NTH>, LoadK<BM, NTH>>::type la;
   typename std::conditional<B_T, LoadKT<BN, NTH>, LoadK<BN, NTH>>::type lb;
+  if constexpr (A_T) la.init(p.lda, m0, p.M, tid);
+  else la.init(p.lda, ra, tid);
+  if constexpr (B_T) lb.init(p.ldb, n0, p.N, tid);
+  else lb.init(p.ldb, rb, tid);
+  // bytes from each operand's start to the end of its last row
+  const int64_t ext_a = A_T ? ((K - 1) * p.lda + p.M) * 2 : ((p.M - 1) * p.lda + K) * 2;
+  const int64_t ext_b = B_T ? ((K - 1) * p.ldb + p.N) * 2
+                            : (((SWI ? p.ffn : 0) + p.N - 1) * p.ldb + K) * 2;
 
   auto load_tiles = [&](int64_t k0) {
-    if constexpr (A_T) la.load(A, p.lda, m0, p.M, k0, K, tid);
-    else la.load(A, p.lda, ra, k0, K, tid);
-    if constexpr (B_T) lb.load(B, p.ldb, n0, p.N, k0, K, tid);
-    else lb.load(B, p.ldb, rb, k0, K, tid);
+    la.load(A, p.lda, ext_a, k0, K, tid);
+    lb.load(B, p.ldb, ext_b, k0, K, tid);
   };
 
   f32x16_t acc[TM][TN];
