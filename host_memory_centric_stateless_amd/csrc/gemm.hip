@@ -310,6 +310,19 @@ __global__ __launch_bounds__(64 * WVM * WVN) void gemm_kernel(mt_gemm_args p, in
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j], acc[i][j], 0,
                                                             0, 0);
   };
+  // Within a k-step the next k-step's fragment reads are interleaved with
+  // this k-step's MFMAs (one MFMA, then RPM reads), all in the first half, so
+  // they have landed well before the next k-step needs them (group masks:
+  // 0x008 MFMA, 0x100 LDS read).
+  constexpr int NREAD = (A_T ? 2 : 1) * TM + (B_T ? 2 : 1) * TN;
+  constexpr int RPM = (NREAD + TM * TN / 2 - 1) / (TM * TN / 2);
+  auto interleave = [&]() {
+#pragma unroll
+    for (int j = 0; j < TM * TN; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);
+    }
+  };
   constexpr int KS = BK / 16;  // k-steps per tile (even, so slots alternate 0,1,0,1)
   static_assert(KS % 2 == 0, "k-steps per tile must be even");
 
@@ -329,13 +342,15 @@ __global__ __launch_bounds__(64 * WVM * WVN) void gemm_kernel(mt_gemm_args p, in
     for (int ks = 0; ks < KS - 1; ++ks) {
       read_frags(as, bs, ks + 1, (ks + 1) & 1);
       mfmas(ks & 1);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
     la.store(As[cur ^ 1], tid);
     lb.store(Bs[cur ^ 1], tid);
     __syncthreads();
     read_frags(As[cur ^ 1], Bs[cur ^ 1], 0, 0);
     mfmas((KS - 1) & 1);
+    interleave();
   }
 
   // ------------------------------------------------------------ epilogue
