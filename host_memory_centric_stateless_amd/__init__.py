@@ -140,6 +140,7 @@ _SIGS = {
     "mtk_rmsnorm_bwd": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _P], C.c_int),
     "mtk_rope": ([_P, _I64, _I32, _I32, _I32, _I32, _P, _P, _I32, _P], C.c_int),
     "mtk_attention_fwd": ([_P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P], C.c_int),
+    "mtk_attention_bwd_workspace": ([_I32, _I32, _I32, _I32, _I32], C.c_size_t),
     "mtk_attention_bwd": ([_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P], C.c_int),
     "mtk_cross_entropy": ([_P, _I64, _P, _I64, _I32, _F, _I64, _P, _I64, _P, _P, _P], C.c_int),
     "mtk_copy": ([_P, _P, C.c_size_t, _I32, _P], C.c_int),
@@ -333,9 +334,13 @@ def mtk_attention_fwd(qkv, o, lse, batch, seq_len, n_heads, n_kv_heads, head_dim
                                   n_kv_heads, head_dim, _stream(stream)), "mtk_attention_fwd")
 
 
-def mtk_attention_bwd(qkv, o, dout, lse, dsum_ws, dqkv, batch, seq_len, n_heads, n_kv_heads,
+def mtk_attention_bwd_workspace(batch, seq_len, n_heads, n_kv_heads, head_dim) -> int:
+    return _lib.mtk_attention_bwd_workspace(batch, seq_len, n_heads, n_kv_heads, head_dim)
+
+
+def mtk_attention_bwd(qkv, o, dout, lse, workspace, dqkv, batch, seq_len, n_heads, n_kv_heads,
                       head_dim, stream=None):
-    _check(_lib.mtk_attention_bwd(_ptr(qkv), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dsum_ws),
+    _check(_lib.mtk_attention_bwd(_ptr(qkv), _ptr(o), _ptr(dout), _ptr(lse), _ptr(workspace),
                                   _ptr(dqkv), batch, seq_len, n_heads, n_kv_heads, head_dim,
                                   _stream(stream)), "mtk_attention_bwd")
 

@@ -417,13 +417,13 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
 // dO^T and Q^T from the same tiles through transpose reads.  dK and dV are two
 // launches of this kernel (DK selects which): each then holds one accumulator
 // and fits two waves per SIMD, at the price of recomputing P in both.
-template <int D, bool DK>
+template <int D, bool DK, bool SPLIT>
 __device__ __forceinline__ void dkdv_body(const uint16_t* __restrict__ qkv,
                                           const uint16_t* __restrict__ dout,
                                           const float* __restrict__ lse,
                                           const float* __restrict__ dsum,
-                                          uint16_t* __restrict__ dqkv, int seq, int nq, int nkv,
-                                          int64_t T) {
+                                          uint16_t* __restrict__ dqkv, float* __restrict__ part,
+                                          int seq, int nq, int nkv, int64_t T) {
   constexpr int BQ = 64, KS = D / 16, DT = D / 32;
   __shared__ __attribute__((aligned(16))) uint16_t Qs[2][BQ * PITCH];
   __shared__ __attribute__((aligned(16))) uint16_t Os[2][BQ * PITCH];  // dO
@@ -433,8 +433,11 @@ __device__ __forceinline__ void dkdv_body(const uint16_t* __restrict__ qkv,
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, known uniform
   const int kvb = gridDim.x - 1 - blockIdx.x;
-  const int kvh = blockIdx.y, b = blockIdx.z;
+  const int b = blockIdx.z;
   const int grp = nq / nkv;
+  // SPLIT: one workgroup per query head (blockIdx.y), writing that head's
+  // fp32 share of dK or dV; otherwise one per kv head, walking its group.
+  const int kvh = SPLIT ? (int)blockIdx.y / grp : (int)blockIdx.y;
   const int64_t ld = (int64_t)(nq + 2 * nkv) * D;
   const int64_t ldo = (int64_t)nq * D;
   const int64_t row0 = (int64_t)b * seq;
@@ -454,7 +457,7 @@ __device__ __forceinline__ void dkdv_body(const uint16_t* __restrict__ qkv,
 #pragma unroll
   for (int dd = 0; dd < DT; ++dd) zero(acc[dd]);
   const int qt0 = (kvb * 128) / BQ, nqt = seq / BQ;
-  const int per_head = nqt - qt0, n_it = grp * per_head;
+  const int per_head = nqt - qt0, n_it = SPLIT ? per_head : grp * per_head;
 
   TileCopy<BQ, D> cq(ld, tid), co(ldo, tid);
   // Each wave also reads one 64-row statistics vector of the tile (BQ is the
@@ -464,8 +467,8 @@ __device__ __forceinline__ void dkdv_body(const uint16_t* __restrict__ qkv,
   const float* stat_src = (DK && w == 1) ? dsum : lse;
   float stat = 0.0f;
   auto gload = [&](int it) {
-    const int j = kvh * grp + it / per_head;
-    const int q0 = (qt0 + it % per_head) * BQ;
+    const int j = SPLIT ? (int)blockIdx.y : kvh * grp + it / per_head;
+    const int q0 = (qt0 + (SPLIT ? it : it % per_head)) * BQ;
     cq.load(qkv + j * D + (row0 + q0) * ld);
     co.load(dout + j * D + (row0 + q0) * ldo);
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -490,7 +493,7 @@ __device__ __forceinline__ void dkdv_body(const uint16_t* __restrict__ qkv,
   __syncthreads();
   for (int it = 0; it < n_it; ++it) {
     const int cur = it & 1;
-    const int q0 = (qt0 + it % per_head) * BQ;
+    const int q0 = (qt0 + (SPLIT ? it : it % per_head)) * BQ;
     const bool more = it + 1 < n_it;
     if (more) gload(it + 1);
     if (q0 + BQ - 1 >= kw0) {
@@ -546,17 +549,56 @@ __device__ __forceinline__ void dkdv_body(const uint16_t* __restrict__ qkv,
     if (more) sstore(cur ^ 1);
     __syncthreads();
   }
-  const float scale = DK ? 1.0f / sqrtf((float)D) : 1.0f;
-  uint16_t* dst = dqkv + (row0 + kv) * ld + (int64_t)(DK ? nq : nq + nkv) * D + kvh * D;
+  if constexpr (SPLIT) {
+    // unscaled fp32 share of query head blockIdx.y: part [nq][T][D]
+    float* dst = part + ((int64_t)blockIdx.y * T + row0 + kv) * D;
 #pragma unroll
-  for (int dd = 0; dd < DT; ++dd)
+    for (int dd = 0; dd < DT; ++dd)
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int d = dd * 32 + rr * 8 + g * 4;
-      u32x2 v2{pack_bf2(acc[dd][rr * 4 + 0] * scale, acc[dd][rr * 4 + 1] * scale),
-               pack_bf2(acc[dd][rr * 4 + 2] * scale, acc[dd][rr * 4 + 3] * scale)};
-      *reinterpret_cast<u32x2*>(dst + d) = v2;
-    }
+      for (int rr = 0; rr < 4; ++rr)
+        *reinterpret_cast<float4*>(dst + dd * 32 + rr * 8 + g * 4) =
+            make_float4(acc[dd][rr * 4 + 0], acc[dd][rr * 4 + 1], acc[dd][rr * 4 + 2],
+                        acc[dd][rr * 4 + 3]);
+  } else {
+    const float scale = DK ? 1.0f / sqrtf((float)D) : 1.0f;
+    uint16_t* dst = dqkv + (row0 + kv) * ld + (int64_t)(DK ? nq : nq + nkv) * D + kvh * D;
+#pragma unroll
+    for (int dd = 0; dd < DT; ++dd)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int d = dd * 32 + rr * 8 + g * 4;
+        u32x2 v2{pack_bf2(acc[dd][rr * 4 + 0] * scale, acc[dd][rr * 4 + 1] * scale),
+                 pack_bf2(acc[dd][rr * 4 + 2] * scale, acc[dd][rr * 4 + 3] * scale)};
+        *reinterpret_cast<u32x2*>(dst + d) = v2;
+      }
+  }
+}
+
+// dK or dV of a grouped kv head from its query heads' fp32 shares, added in
+// query-head order (fixed for any launch), scaled, rounded to bf16 into the
+// column block starting at head col0 of dqkv.  One thread per
+// four consecutive d of one (row, kv head).
+template <int D>
+__global__ __launch_bounds__(256) void attn_gqa_reduce_kernel(const float* __restrict__ part,
+                                                              uint16_t* __restrict__ dqkv,
+                                                              int64_t T, int nq, int nkv,
+                                                              int col0, float scale) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t per_row = (int64_t)nkv * (D / 4);
+  if (i >= T * per_row) return;
+  const int64_t row = i / per_row;
+  const int kvh = (int)((i % per_row) / (D / 4));
+  const int d = (int)(i % (D / 4)) * 4;
+  const int grp = nq / nkv;
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int g = 0; g < grp; ++g) {
+    const float4 v =
+        *reinterpret_cast<const float4*>(part + ((int64_t)(kvh * grp + g) * T + row) * D + d);
+    a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
+  }
+  const int64_t ld = (int64_t)(nq + 2 * nkv) * D;
+  *reinterpret_cast<u32x2*>(dqkv + row * ld + (int64_t)(col0 + kvh) * D + d) =
+      u32x2{pack_bf2(a.x * scale, a.y * scale), pack_bf2(a.z * scale, a.w * scale)};
 }
 
 // dK holds both K and V fragments: at two waves per SIMD a few registers
@@ -566,20 +608,20 @@ __device__ __forceinline__ void dkdv_body(const uint16_t* __restrict__ qkv,
 #define MT_DK_WAVES_PER_SIMD 2
 #endif
 
-template <int D>
+template <int D, bool SPLIT>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dv_kernel(
     const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ dsum, uint16_t* __restrict__ dqkv,
-    int seq, int nq, int nkv, int64_t T) {
-  dkdv_body<D, false>(qkv, dout, lse, dsum, dqkv, seq, nq, nkv, T);
+    float* __restrict__ part, int seq, int nq, int nkv, int64_t T) {
+  dkdv_body<D, false, SPLIT>(qkv, dout, lse, dsum, dqkv, part, seq, nq, nkv, T);
 }
 
-template <int D>
+template <int D, bool SPLIT>
 __global__ __launch_bounds__(256, MT_DK_WAVES_PER_SIMD) void attn_bwd_dk_kernel(
     const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ dsum, uint16_t* __restrict__ dqkv,
-    int seq, int nq, int nkv, int64_t T) {
-  dkdv_body<D, true>(qkv, dout, lse, dsum, dqkv, seq, nq, nkv, T);
+    float* __restrict__ part, int seq, int nq, int nkv, int64_t T) {
+  dkdv_body<D, true, SPLIT>(qkv, dout, lse, dsum, dqkv, part, seq, nq, nkv, T);
 }
 
 template <int D>
@@ -591,17 +633,34 @@ hipError_t fwd_d(const uint16_t* qkv, uint16_t* o, float* lse, int batch, int se
   return hipGetLastError();
 }
 
+// With grouped heads the dK/dV launches run one workgroup per query head (nq
+// instead of nkv workgroups per key block, so the grid fills the chip) and
+// the group's shares are added by attn_gqa_reduce_kernel.
 template <int D>
 hipError_t bwd_d(const uint16_t* qkv, const uint16_t* o, const uint16_t* dout, const float* lse,
-                 float* dsum, uint16_t* dqkv, int batch, int seq, int nq, int nkv, hipStream_t s) {
+                 float* dsum, float* part, uint16_t* dqkv, int batch, int seq, int nq, int nkv,
+                 hipStream_t s) {
   const int64_t T = (int64_t)batch * seq;
   const int64_t n = T * nq;
   hipLaunchKernelGGL(attn_dsum_kernel<D>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, o,
                      dout, dsum, nq, T);
-  hipLaunchKernelGGL(attn_bwd_dv_kernel<D>, dim3(seq / 128, nkv, batch), dim3(256), 0, s, qkv,
-                     dout, lse, dsum, dqkv, seq, nq, nkv, T);
-  hipLaunchKernelGGL(attn_bwd_dk_kernel<D>, dim3(seq / 128, nkv, batch), dim3(256), 0, s, qkv,
-                     dout, lse, dsum, dqkv, seq, nq, nkv, T);
+  if (nq == nkv) {
+    hipLaunchKernelGGL((attn_bwd_dv_kernel<D, false>), dim3(seq / 128, nkv, batch), dim3(256), 0,
+                       s, qkv, dout, lse, dsum, dqkv, nullptr, seq, nq, nkv, T);
+    hipLaunchKernelGGL((attn_bwd_dk_kernel<D, false>), dim3(seq / 128, nkv, batch), dim3(256), 0,
+                       s, qkv, dout, lse, dsum, dqkv, nullptr, seq, nq, nkv, T);
+  } else {
+    const int64_t nr = T * nkv * (D / 4);
+    const dim3 rgrid((unsigned)((nr + 255) / 256));
+    hipLaunchKernelGGL((attn_bwd_dv_kernel<D, true>), dim3(seq / 128, nq, batch), dim3(256), 0, s,
+                       qkv, dout, lse, dsum, dqkv, part, seq, nq, nkv, T);
+    hipLaunchKernelGGL(attn_gqa_reduce_kernel<D>, rgrid, dim3(256), 0, s, part, dqkv, T, nq, nkv,
+                       nq + nkv, 1.0f);
+    hipLaunchKernelGGL((attn_bwd_dk_kernel<D, true>), dim3(seq / 128, nq, batch), dim3(256), 0, s,
+                       qkv, dout, lse, dsum, dqkv, part, seq, nq, nkv, T);
+    hipLaunchKernelGGL(attn_gqa_reduce_kernel<D>, rgrid, dim3(256), 0, s, part, dqkv, T, nq, nkv,
+                       nq, 1.0f / sqrtf((float)D));
+  }
   hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, dim3(seq / 128, nq, batch), dim3(256), 0, s, qkv,
                      dout, lse, dsum, dqkv, seq, nq, nkv, T);
   return hipGetLastError();
@@ -616,11 +675,23 @@ hipError_t launch_attn_fwd(const uint16_t* qkv, uint16_t* o, float* lse, int bat
   return hipErrorInvalidValue;
 }
 
+// Workspace: the D rows (fp32 [nq, T]), then with grouped heads the
+// per-query-head dK/dV shares (fp32 [nq, T, d]).
+static size_t dsum_bytes(int64_t T, int nq) { return ((size_t)T * nq * 4 + 255) / 256 * 256; }
+
+size_t attn_bwd_workspace_bytes(int batch, int seq, int nq, int nkv, int d) {
+  const int64_t T = (int64_t)batch * seq;
+  return dsum_bytes(T, nq) + (nq != nkv ? (size_t)T * nq * d * 4 : 0);
+}
+
 hipError_t launch_attn_bwd(const uint16_t* qkv, const uint16_t* o, const uint16_t* dout,
-                           const float* lse, float* dsum, uint16_t* dqkv, int batch, int seq,
+                           const float* lse, void* workspace, uint16_t* dqkv, int batch, int seq,
                            int nq, int nkv, int d, hipStream_t s) {
-  if (d == 128) return bwd_d<128>(qkv, o, dout, lse, dsum, dqkv, batch, seq, nq, nkv, s);
-  if (d == 64) return bwd_d<64>(qkv, o, dout, lse, dsum, dqkv, batch, seq, nq, nkv, s);
+  float* dsum = static_cast<float*>(workspace);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                         dsum_bytes((int64_t)batch * seq, nq));
+  if (d == 128) return bwd_d<128>(qkv, o, dout, lse, dsum, part, dqkv, batch, seq, nq, nkv, s);
+  if (d == 64) return bwd_d<64>(qkv, o, dout, lse, dsum, part, dqkv, batch, seq, nq, nkv, s);
   return hipErrorInvalidValue;
 }
 

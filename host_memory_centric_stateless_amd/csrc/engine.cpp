@@ -427,7 +427,7 @@ hipError_t block_backward(mt_ctx* c, const uint16_t* W, const Acts& a, const flo
   CK(gemm(c, s, MT_GEMM_TN, wepi, h, p.qd, T, dh1b, h, a.o, p.qd, slab(T_WO), p.qd));
   {
     KScope k(c, s, "attn_bwd", 10.0 * g.head_dim * attn_pairs(g), 0);
-    CK(launch_attn_bwd(a.qkv, a.o, dout, a.lse, c->wsp<float>(p.ws.dsum), dqkv, (int)(T / g.seq_len),
+    CK(launch_attn_bwd(a.qkv, a.o, dout, a.lse, c->wsp<char>(p.ws.dsum), dqkv, (int)(T / g.seq_len),
                        g.seq_len, g.n_heads, g.n_kv_heads, g.head_dim, s));
   }
   {

@@ -59,15 +59,21 @@ extern "C" mt_status mtk_attention_fwd(const uint16_t* qkv, uint16_t* o, float* 
                                     (hipStream_t)stream));
 }
 
+extern "C" size_t mtk_attention_bwd_workspace(int32_t batch, int32_t seq_len, int32_t n_heads,
+                                              int32_t n_kv_heads, int32_t head_dim) {
+  if (!attn_ok(batch, seq_len, n_heads, n_kv_heads, head_dim)) return 0;
+  return attn_bwd_workspace_bytes(batch, seq_len, n_heads, n_kv_heads, head_dim);
+}
+
 extern "C" mt_status mtk_attention_bwd(const uint16_t* qkv, const uint16_t* o,
-                                       const uint16_t* dout, const float* lse, float* dsum_ws,
+                                       const uint16_t* dout, const float* lse, void* workspace,
                                        uint16_t* dqkv, int32_t batch, int32_t seq_len,
                                        int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
                                        void* stream) {
-  if (!qkv || !o || !dout || !lse || !dsum_ws || !dqkv ||
+  if (!qkv || !o || !dout || !lse || !workspace || !dqkv ||
       !attn_ok(batch, seq_len, n_heads, n_kv_heads, head_dim))
     return MT_E_ARG;
-  return hip_status(launch_attn_bwd(qkv, o, dout, lse, dsum_ws, dqkv, batch, seq_len, n_heads,
+  return hip_status(launch_attn_bwd(qkv, o, dout, lse, workspace, dqkv, batch, seq_len, n_heads,
                                     n_kv_heads, head_dim, (hipStream_t)stream));
 }
 

@@ -135,7 +135,8 @@ std::string make_plan(const mt_config& c, Plan* p) {
   w.dh1 = take(T * h * 4);
   w.dh1b = take(T * h * 2);
   w.dout = take(T * p->qd * 2);
-  w.dsum = take((size_t)c.n_heads * T * 4);
+  w.dsum = take(attn_bwd_workspace_bytes((int)(p->T / c.seq_len), c.seq_len, c.n_heads,
+                                         c.n_kv_heads, c.head_dim));
   w.dqkv = take(T * p->ldq * 2);
   w.partial = take(rmsnorm_bwd_partial_bytes(p->T, (int)h));
   w.cos_t = take((size_t)c.seq_len * (c.head_dim / 2) * 4);

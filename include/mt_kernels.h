@@ -85,12 +85,20 @@ mt_status mtk_attention_fwd(const uint16_t* qkv, uint16_t* o, float* lse, int32_
                             int32_t seq_len, int32_t n_heads, int32_t n_kv_heads,
                             int32_t head_dim, void* stream);
 
+/* Bytes of device scratch mtk_attention_bwd needs for these sizes (0 for sizes
+ * it rejects): fp32 [nq, T] row statistics, plus, when n_kv_heads < n_heads,
+ * fp32 [nq, T, d] per-query-head shares of dK and dV. */
+size_t mtk_attention_bwd_workspace(int32_t batch, int32_t seq_len, int32_t n_heads,
+                                   int32_t n_kv_heads, int32_t head_dim);
+
 /* Flash attention backward.  dout bf16 [T, nq d]; writes dq, dk, dv into the
- * matching column blocks of dqkv (same layout as qkv).  dsum_ws: fp32 [nq, T]
- * scratch.  Deterministic (no float atomics; dk/dv summed over the query heads
- * of a group in fixed order). */
+ * matching column blocks of dqkv (same layout as qkv).  workspace: device
+ * scratch of mtk_attention_bwd_workspace(...) bytes, owned by the caller, no
+ * contents kept between calls.  Deterministic (no float atomics; dk/dv summed
+ * over the query heads of a group in fixed order).  MT_E_ARG for null
+ * pointers or sizes attention_fwd rejects. */
 mt_status mtk_attention_bwd(const uint16_t* qkv, const uint16_t* o, const uint16_t* dout,
-                            const float* lse, float* dsum_ws, uint16_t* dqkv, int32_t batch,
+                            const float* lse, void* workspace, uint16_t* dqkv, int32_t batch,
                             int32_t seq_len, int32_t n_heads, int32_t n_kv_heads,
                             int32_t head_dim, void* stream);
 

@@ -175,8 +175,9 @@ def test_attention_backward(b, s, nq, nkv, d):
     lse = torch.empty((nq, T), dtype=torch.float32, device=dev())
     mt.mtk_attention_fwd(qd, o, lse, b, s, nq, nkv, d)
     dq = torch.zeros((T, (nq + 2 * nkv) * d), dtype=torch.bfloat16, device=dev())
-    dsum = torch.empty((nq, T), dtype=torch.float32, device=dev())
-    mt.mtk_attention_bwd(qd, o, bf16_dev(dO), lse, dsum, dq, b, s, nq, nkv, d)
+    ws = torch.empty(mt.mtk_attention_bwd_workspace(b, s, nq, nkv, d), dtype=torch.uint8,
+                     device=dev())
+    mt.mtk_attention_bwd(qd, o, bf16_dev(dO), lse, ws, dq, b, s, nq, nkv, d)
     rq, rk, rv = OM.attention_bwd(q, k, v, bf16_round(dO).reshape(b, s, nq, d))
     got = host(dq)
     assert rel_max(got[:, :nq * d], rq.reshape(T, -1)) < 2e-2

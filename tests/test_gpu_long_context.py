@@ -56,8 +56,9 @@ def test_attention_full_length_sampled_rows():
     dO = random_array((S, nq * d), seed=22)
     dOb = bf16_round(dO).reshape(S, nq, d)
     dqkv = torch.zeros((S, (nq + 2 * nkv) * d), dtype=torch.bfloat16, device=dev())
-    dsum = torch.empty((nq, S), dtype=torch.float32, device=dev())
-    mt.mtk_attention_bwd(qd, o, bf16_dev(dO), lse, dsum, dqkv, 1, S, nq, nkv, d)
+    ws = torch.empty(mt.mtk_attention_bwd_workspace(1, S, nq, nkv, d), dtype=torch.uint8,
+                     device=dev())
+    mt.mtk_attention_bwd(qd, o, bf16_dev(dO), lse, ws, dqkv, 1, S, nq, nkv, d)
     g = host(dqkv)
     scale = 1.0 / math.sqrt(d)
     for j in range(nq):  # row 0 attends to itself only: its dq is exactly zero
