@@ -242,9 +242,12 @@ def measured_traffic(kernel: str, cfg_name: str, default_shape: bool):
     except OSError:
         return None
     fields = dict(l.split(": ", 1) for l in text.splitlines() if ": " in l and not l.startswith(" "))
-    src = os.path.join(ROOT, "host_memory_centric_stateless_amd", "csrc", "gemm.hip")
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if fields.get("gemm_source_sha256", "").strip() != sha:
+    # the kernel's source and the device helpers it includes
+    h = hashlib.sha256()
+    for name in ("gemm.hip", "common.h"):
+        with open(os.path.join(ROOT, "host_memory_centric_stateless_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    if fields.get("gemm_source_sha256", "").split()[0:1] != [h.hexdigest()]:
         return None
     return float(fields["traffic_bytes_per_launch"])
 

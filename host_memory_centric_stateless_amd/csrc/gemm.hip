@@ -311,11 +311,16 @@ __global__ __launch_bounds__(64 * WVM * WVN) void gemm_kernel(mt_gemm_args p, in
                                                             0, 0);
   };
   // Within a k-step the next k-step's fragment reads are interleaved with
-  // this k-step's MFMAs (one MFMA, then RPM reads), all in the first half, so
-  // they have landed well before the next k-step needs them (group masks:
-  // 0x008 MFMA, 0x100 LDS read).
+  // this k-step's MFMAs (one MFMA, then RPM reads), so the LDS reads are
+  // spread over the matrix work instead of bunched just ahead of the MFMAs
+  // that use them (group masks: 0x008 MFMA, 0x100 LDS read).  Spreading them
+  // over all of the k-step rather than its first half keeps every 256 x 256
+  // instance at most 248 VGPRs: two waves per SIMD then still leave room for
+  // a wave of the gradient-drain copy kernel, so a GEMM workgroup can still
+  // start on a CU that the drain occupies (at 256 VGPRs a 256-tile product
+  // lost those CUs and ran a second round).
   constexpr int NREAD = (A_T ? 2 : 1) * TM + (B_T ? 2 : 1) * TN;
-  constexpr int RPM = (NREAD + TM * TN / 2 - 1) / (TM * TN / 2);
+  constexpr int RPM = (NREAD + TM * TN - 1) / (TM * TN);
   auto interleave = [&]() {
 #pragma unroll
     for (int j = 0; j < TM * TN; ++j) {
@@ -355,57 +360,135 @@ __global__ __launch_bounds__(64 * WVM * WVN) void gemm_kernel(mt_gemm_args p, in
 
   // ------------------------------------------------------------ epilogue
   // acc[i][j][r] is C[row, col] with row = 8*(r/4) + 4*(lane/32) + r%4 and
-  // col = lane%32 inside the 32x32 sub-tile (i, j).
+  // col = lane%32 inside the 32x32 sub-tile (i, j): one column per lane.  Each
+  // sub-tile is turned around through a wave-private LDS block so that a lane
+  // holds 16 consecutive columns of one row (row = lane/2, columns
+  // 16*(lane%2)..+15), and every global access of the epilogue is a 16-byte
+  // vector (N and the leading dimensions are multiples of 8, so each 8-column
+  // half is wholly inside or outside the matrix).
+  __syncthreads();  // the K loop's last fragment reads are done in every wave
+  constexpr int TP = 40;  // floats per LDS row: lanes l and l+32 write disjoint banks
+  static_assert(NTH / 64 * 32 * TP * 4 <= (int)sizeof(As), "epilogue scratch");
+  float* tb = reinterpret_cast<float*>(&As[0][0]) + (tid >> 6) * 32 * TP;
   const int g4 = (lane >> 5) * 4;
+  // The block is private to the wave, and LDS executes one wave's accesses in
+  // issue order, so a compiler-only barrier is enough between its writes and
+  // the reads of other lanes' values.  (A memory fence would also wait for
+  // the wave's outstanding global stores.)
+  auto lds_order = []() {
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+  };
+  auto turn = [&](const f32x16_t& v, float (&out)[16]) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) tb[(8 * (r >> 2) + g4 + (r & 3)) * TP + (lane & 31)] = v[r];
+    lds_order();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 x = *reinterpret_cast<const float4*>(tb + (lane >> 1) * TP + (lane & 1) * 16 + 4 * q);
+      out[4 * q + 0] = x.x; out[4 * q + 1] = x.y; out[4 * q + 2] = x.z; out[4 * q + 3] = x.w;
+    }
+    lds_order();
+  };
+  auto pack8 = [](const float* v) {
+    return u32x4{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]), pack_bf2(v[4], v[5]),
+                 pack_bf2(v[6], v[7])};
+  };
+  auto unpack8 = [](const u32x4 w, float* v) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] = bf2f((uint16_t)(w[e] & 0xffffu));
+      v[2 * e + 1] = bf2f((uint16_t)(w[e] >> 16));
+    }
+  };
   if constexpr (SWI) {
     uint16_t* C = static_cast<uint16_t*>(p.C);
 #pragma unroll
-    for (int j = 0; j < TN / 2; ++j) {
-      const int64_t f = n0 + wn * (WN / 2) + j * 32 + (lane & 31);
-      if (f >= p.N) continue;
+    for (int j = 0; j < TN / 2; ++j)
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+      for (int i = 0; i < TM; ++i) {
+        float a[16], u[16];
+        turn(acc[i][j], a);
+        turn(acc[i][j + TN / 2], u);
+        const int64_t row = m0 + wm * WM + i * 32 + (lane >> 1);
+        const int64_t f0 = n0 + wn * (WN / 2) + j * 32 + (lane & 1) * 16;
+        if (row >= p.M) continue;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t row = m0 + wm * WM + i * 32 + (r >> 2) * 8 + g4 + (r & 3);
-          if (row < p.M) {
-            const float a = acc[i][j][r], u = acc[i][j + TN / 2][r];
-            p.gu[row * p.ldgu + f] = f2bf(a);
-            p.gu[row * p.ldgu + p.ffn + f] = f2bf(u);
-            C[row * p.ldc + f] = f2bf(silu_f(a) * u);
-          }
+        for (int h = 0; h < 2; ++h) {
+          const int64_t f = f0 + 8 * h;
+          if (f >= p.N) continue;
+          float y[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) y[e] = silu_f(a[8 * h + e]) * u[8 * h + e];
+          *reinterpret_cast<u32x4*>(p.gu + row * p.ldgu + f) = pack8(a + 8 * h);
+          *reinterpret_cast<u32x4*>(p.gu + row * p.ldgu + p.ffn + f) = pack8(u + 8 * h);
+          *reinterpret_cast<u32x4*>(C + row * p.ldc + f) = pack8(y);
         }
-    }
+      }
   } else {
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int64_t col = n0 + wn * WN + j * 32 + (lane & 31);
-      if (col >= p.N) continue;
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+      for (int i = 0; i < TM; ++i) {
+        float v[16];
+        turn(acc[i][j], v);
+        const int64_t row = m0 + wm * WM + i * 32 + (lane >> 1);
+        const int64_t c0 = n0 + wn * WN + j * 32 + (lane & 1) * 16;
+        if (row >= p.M) continue;
+        const bool in[2] = {c0 < p.N, c0 + 8 < p.N};
+        // every load of the sub-tile is issued before its first store, so the
+        // loads overlap (C may alias R, which forbids moving a load past a store)
+        if constexpr (EPI == MT_EPI_BF16) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t row = m0 + wm * WM + i * 32 + (r >> 2) * 8 + g4 + (r & 3);
-          if (row >= p.M) continue;
-          const float v = acc[i][j][r];
-          if constexpr (EPI == MT_EPI_BF16) {
-            static_cast<uint16_t*>(p.C)[row * p.ldc + col] = f2bf(v);
-          } else if constexpr (EPI == MT_EPI_F32) {
-            static_cast<float*>(p.C)[row * p.ldc + col] = v;
-          } else if constexpr (EPI == MT_EPI_F32_RESID) {
-            static_cast<float*>(p.C)[row * p.ldc + col] = p.R[row * p.ldr + col] + v;
-          } else if constexpr (EPI == MT_EPI_F32_ACCUM) {
-            static_cast<float*>(p.C)[row * p.ldc + col] += v;
-          } else if constexpr (EPI == MT_EPI_SWIGLU_BWD) {
-            const float a = bf2f(p.gu[row * p.ldgu + col]);
-            const float u = bf2f(p.gu[row * p.ldgu + p.ffn + col]);
-            const float s = 1.0f / (1.0f + expf(-a));
-            uint16_t* C = static_cast<uint16_t*>(p.C);
-            C[row * p.ldc + col] = f2bf(v * u * s * (1.0f + a * (1.0f - s)));
-            C[row * p.ldc + p.ffn + col] = f2bf(v * a * s);
+          for (int h = 0; h < 2; ++h)
+            if (in[h])
+              *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.C) + row * p.ldc + c0 + 8 * h) =
+                  pack8(v + 8 * h);
+        } else if constexpr (EPI == MT_EPI_SWIGLU_BWD) {
+          u32x4 ga[2], gu_[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            if (in[h]) {
+              ga[h] = *reinterpret_cast<const u32x4*>(p.gu + row * p.ldgu + c0 + 8 * h);
+              gu_[h] = *reinterpret_cast<const u32x4*>(p.gu + row * p.ldgu + p.ffn + c0 + 8 * h);
+            }
+          uint16_t* C = static_cast<uint16_t*>(p.C);
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            if (!in[h]) continue;
+            float a[8], u[8], d0[8], d1[8];
+            unpack8(ga[h], a);
+            unpack8(gu_[h], u);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float x = v[8 * h + e];
+              const float sg = 1.0f / (1.0f + expf(-a[e]));
+              d0[e] = x * u[e] * sg * (1.0f + a[e] * (1.0f - sg));
+              d1[e] = x * a[e] * sg;
+            }
+            *reinterpret_cast<u32x4*>(C + row * p.ldc + c0 + 8 * h) = pack8(d0);
+            *reinterpret_cast<u32x4*>(C + row * p.ldc + p.ffn + c0 + 8 * h) = pack8(d1);
           }
+        } else {
+          float* C = static_cast<float*>(p.C) + row * p.ldc + c0;
+          float4 add[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            add[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if constexpr (EPI == MT_EPI_F32_RESID) {
+              if (in[q >> 1]) add[q] = *reinterpret_cast<const float4*>(p.R + row * p.ldr + c0 + 4 * q);
+            } else if constexpr (EPI == MT_EPI_F32_ACCUM) {
+              if (in[q >> 1]) add[q] = *reinterpret_cast<const float4*>(C + 4 * q);
+            }
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (in[q >> 1])
+              *reinterpret_cast<float4*>(C + 4 * q) =
+                  make_float4(v[4 * q] + add[q].x, v[4 * q + 1] + add[q].y, v[4 * q + 2] + add[q].z,
+                              v[4 * q + 3] + add[q].w);
         }
-    }
+      }
   }
 }
 
@@ -440,6 +523,9 @@ bool gemm_shape_ok(const mt_gemm_args& a, const char** why) {
   if ((a.M / 128 + 1) * (a.N / 64 + 1) >= (1LL << 31)) return bad("too many tiles");
   if (!a.A || !a.B || !a.C) return bad("null operand");
   if (a.lda % 8 || a.ldb % 8) return bad("lda/ldb must be multiples of 8");
+  if (a.ldc % 8 || a.ldr % 4 || a.ldgu % 8) return bad("ldc, ldgu must be multiples of 8, ldr of 4");
+  if (((uintptr_t)a.C | (uintptr_t)a.R | (uintptr_t)a.gu) & 15)
+    return bad("C, R and gu must be 16-byte aligned");
   const bool at = a.layout == MT_GEMM_TN, bt = a.layout != MT_GEMM_NT;
   if ((at ? a.lda < a.M : a.lda < a.K) || (bt ? a.ldb < a.N : a.ldb < a.K)) return bad("lda/ldb");
   if (a.epilogue == MT_EPI_SWIGLU) {

@@ -43,6 +43,9 @@ enum { MT_GEMM_NT = 0, MT_GEMM_NN = 1, MT_GEMM_TN = 2 };
 enum { MT_EPI_BF16 = 0, MT_EPI_F32 = 1, MT_EPI_F32_RESID = 2, MT_EPI_F32_ACCUM = 3,
        MT_EPI_SWIGLU = 4, MT_EPI_SWIGLU_BWD = 5 };
 
+/* Requirements (MT_E_ARG otherwise): M, N, K, lda, ldb, ldc, ldgu multiples of
+ * 8, ldr a multiple of 4; C, R and gu 16-byte aligned (the epilogue moves
+ * 16-byte vectors); the operands readable over their whole extent. */
 typedef struct mt_gemm_args {
   int32_t layout, epilogue;
   int64_t M, N, K;          /* all multiples of 8                                 */
