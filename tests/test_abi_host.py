@@ -218,3 +218,62 @@ def test_kernel_entry_points_reject_bad_shapes():
         mt.mtk_attention_fwd(1 << 30, 1 << 30, 1 << 30, 1, 128, 4, 3, 64, stream=0)
     with pytest.raises(mt.MtError):
         mt.mtk_rmsnorm_fwd(1 << 30, 1 << 30, 1 << 30, 1 << 30, 4, 6, 1e-5, stream=0)
+
+
+def _kernel_metadata():
+    """(name, vgpr_count, vgpr spills, scratch bytes) of every gfx950 kernel in
+    the built libmt.so, read from the code objects' metadata notes."""
+    import shutil
+    import subprocess
+    import tempfile
+    llvm = "/opt/rocm/llvm/bin"
+    tools = [shutil.which("objcopy"), os.path.join(llvm, "clang-offload-bundler"),
+             os.path.join(llvm, "llvm-readelf")]
+    if not all(t and os.path.exists(t) for t in tools):
+        pytest.skip("binutils / ROCm LLVM tools not found")
+    so = os.path.join(os.path.dirname(mt.__file__), "libmt.so")
+    out = []
+    with tempfile.TemporaryDirectory() as d:
+        fb = os.path.join(d, "fatbin")
+        subprocess.run([tools[0], "--dump-section", f".hip_fatbin={fb}", so, os.path.join(d, "x")],
+                       check=True, capture_output=True)
+        data = open(fb, "rb").read()
+        magic = b"__CLANG_OFFLOAD_BUNDLE__"
+        starts = [m.start() for m in re.finditer(re.escape(magic), data)]
+        for n, s in enumerate(starts):
+            part = os.path.join(d, f"b{n}")
+            with open(part, "wb") as f:
+                f.write(data[s:starts[n + 1] if n + 1 < len(starts) else len(data)])
+            co = part + ".co"
+            subprocess.run([tools[1], "--type=o", "--unbundle", f"--input={part}", f"--output={co}",
+                            "--targets=hipv4-amdgcn-amd-amdhsa--gfx950"], check=True,
+                           capture_output=True)
+            notes = subprocess.run([tools[2], "--notes", co], check=True, capture_output=True,
+                                   text=True).stdout
+            for blk in notes.split("  - .agpr_count")[1:]:
+                def field(k):
+                    m = re.search(r"\." + k + r":\s+(\S+)", blk)
+                    return m.group(1) if m else None
+                out.append((field("name"), int(field("vgpr_count")),
+                            int(field("vgpr_spill_count")),
+                            int(field("private_segment_fixed_size"))))
+    assert out, "no kernel metadata found"
+    return out
+
+
+def test_kernel_register_budget():
+    """Two waves per SIMD of the 256 x 256 GEMM (8 waves) and of the attention
+    kernels (2 workgroups of 4 waves per CU) must leave room for one wave of
+    the 4-workgroup gradient-drain copy kernel, which runs beside them for the
+    whole backward: 2 x 248 + 16 <= 512 VGPRs per lane (granule 8).  Otherwise
+    a product of exactly 256 tiles loses the drain's CUs and runs a second
+    round.  No kernel may spill or use scratch."""
+    meta = _kernel_metadata()
+    names = [m[0] for m in meta]
+    assert any("gemm_kernel" in n for n in names) and any("attn_fwd" in n for n in names)
+    for name, vgpr, spill, scratch in meta:
+        assert spill == 0 and scratch == 0, (name, spill, scratch)
+        if ("gemm_kernel" in name and "256ELi256" in name) or "attn_" in name:
+            assert vgpr <= 248, (name, vgpr)
+        if "copy16" in name:
+            assert vgpr <= 16, (name, vgpr)
