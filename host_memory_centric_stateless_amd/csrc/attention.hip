@@ -114,6 +114,22 @@ __device__ inline bf16x8_t row_frag(const uint16_t* t, int row0, int d0, int lan
   return ld_frag(t + (row0 + (lane & 31)) * PITCH + d0 + (lane >> 5) * 8);
 }
 
+// One score block: acc += sum over k-steps of (tile rows row0.., k-step ks)
+// x b[ks], for the k-steps [K0, K0 + G).  The G fragment reads are all issued
+// before the first MFMA, so their LDS latencies overlap; left to itself the
+// compiler issues each read just ahead of its MFMA, and the dependent chain
+// then waits on LDS at every step.
+template <int G, int K0, int N>
+__device__ inline void score_group(f32x16_t& acc, const uint16_t* t, int row0,
+                                   const bf16x8_t (&b)[N], int lane) {
+  bf16x8_t a[G];
+#pragma unroll
+  for (int k = 0; k < G; ++k) a[k] = row_frag(t, row0, (K0 + k) * 16, lane);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int k = 0; k < G; ++k) acc = mfma(a[k], b[K0 + k], acc);
+}
+
 // Transpose-read fragment: rows d = d0 + lane%32 of a [rows][d] tile, with
 // the eight k values (tile rows) in the order the probabilities use as the B
 // operand: k = r0 + 8*(e/4) + 4*(lane/32) + e%4 for element e.  One
@@ -194,8 +210,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         zero(sc[i]);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) sc[i] = mfma(row_frag(ks_t, i * 32, ks * 16, lane), qf[ks], sc[i]);
+        score_group<KS, 0>(sc[i], ks_t, i * 32, qf, lane);
       }
       // causal mask only where some key of the tile lies after some query of
       // the wave (wave-uniform branch)
@@ -366,11 +381,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
         f32x16_t sc, dp;
         zero(sc);
         zero(dp);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          sc = mfma(row_frag(ks_t, i * 32, ks * 16, lane), qf[ks], sc);
-          dp = mfma(row_frag(vs_t, i * 32, ks * 16, lane), df[ks], dp);
-        }
+        score_group<KS / 2, 0>(sc, ks_t, i * 32, qf, lane);
+        score_group<KS / 2, 0>(dp, vs_t, i * 32, df, lane);
+        score_group<KS / 2, KS / 2>(sc, ks_t, i * 32, qf, lane);
+        score_group<KS / 2, KS / 2>(dp, vs_t, i * 32, df, lane);
         if (diag) {
 #pragma unroll
           for (int r = 0; r < 16; ++r)
@@ -507,10 +521,16 @@ __device__ __forceinline__ void dkdv_body(const uint16_t* __restrict__ qkv,
         f32x16_t sc, dp;
         zero(sc);
         if constexpr (DK) zero(dp);
+        if constexpr (DK) {
+          // two chains; batching their reads would take dK past the register
+          // budget that lets a drain wave share its CU
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          sc = mfma(row_frag(qs_t, i * 32, ks * 16, lane), kf[ks], sc);
-          if constexpr (DK) dp = mfma(row_frag(os_t, i * 32, ks * 16, lane), vf[ks], dp);
+          for (int ks = 0; ks < KS; ++ks) {
+            sc = mfma(row_frag(qs_t, i * 32, ks * 16, lane), kf[ks], sc);
+            dp = mfma(row_frag(os_t, i * 32, ks * 16, lane), vf[ks], dp);
+          }
+        } else {
+          score_group<KS, 0>(sc, qs_t, i * 32, kf, lane);
         }
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
@@ -601,9 +621,9 @@ __global__ __launch_bounds__(256) void attn_gqa_reduce_kernel(const float* __res
       u32x2{pack_bf2(a.x * scale, a.y * scale), pack_bf2(a.z * scale, a.w * scale)};
 }
 
-// dK holds both K and V fragments: at two waves per SIMD a few registers
-// spill, which still beats one wave per SIMD (7B shape: backward 1.76 ms
-// against 2.12 ms).
+// dK holds both K and V fragments and two score chains: 248 VGPRs, two waves
+// per SIMD (one wave per SIMD was slower: 7B shape, backward 2.12 ms against
+// 1.76 ms when this was chosen).
 #ifndef MT_DK_WAVES_PER_SIMD
 #define MT_DK_WAVES_PER_SIMD 2
 #endif
