@@ -19,6 +19,7 @@ the run's copy activity (default: whole trace).
 from __future__ import annotations
 
 import argparse
+import bisect
 import csv
 from collections import defaultdict
 from typing import List, Tuple
@@ -106,6 +107,21 @@ def summarize(prefix: str, t0: int = None, t1: int = None) -> str:
     if drain:
         dt = sum(b - a for a, b in clip(drain, lo, hi))
         lines.append(f"drain kernels: n={len(drain)} total {dt / 1e6:.1f} ms")
+    # Compute time with no copy in flight, by kernel: what keeps the overlap below 1.
+    lone = defaultdict(int)
+    cends = [e for _, e in C]
+    for a, b, n in kern:
+        i, covered = bisect.bisect_right(cends, a), 0
+        while i < len(C) and C[i][0] < b:
+            covered += min(b, C[i][1]) - max(a, C[i][0])
+            i += 1
+        lone[n] += (b - a) - covered
+    lone_tot = sum(lone.values())
+    if lone_tot:
+        lines.append(f"kernel time with no copy in flight: {lone_tot / 1e6:.1f} ms (sum over launches)")
+        for n, t in sorted(lone.items(), key=lambda kv: -kv[1])[:8]:
+            short = n.replace("mt::(anonymous namespace)::", "").split("(")[0][:60]
+            lines.append(f"  {short:60s} {t / 1e6:8.1f} ms")
     lines.append("")
     lines.append(f"{'kernel':70s} {'calls':>6s} {'total ms':>10s} {'avg us':>10s} {'share':>6s}")
     for n, (c, t) in sorted(per.items(), key=lambda kv: -kv[1][1]):
