@@ -122,6 +122,7 @@ _SIGS = {
     "mt_backward": ([_P, _I32], C.c_int),
     "mt_backward_step": ([_P, _I32, C.POINTER(mt_adamw_hparams), _I64], C.c_int),
     "mt_flush_grads": ([_P], C.c_int),
+    "mt_sync_loss": ([_P], C.c_int),
     "mt_adamw_step": ([_P, C.POINTER(mt_adamw_hparams), _I64], C.c_int),
     "mt_get_stats": ([_P, C.POINTER(mt_stats)], C.c_int),
     "mt_last_error": ([_P], C.c_char_p),
@@ -238,6 +239,10 @@ def mt_backward_step(ctx, accumulate: int, hp: mt_adamw_hparams, step: int):
 
 def mt_flush_grads(ctx):
     _check(_lib.mt_flush_grads(ctx), "mt_flush_grads", ctx)
+
+
+def mt_sync_loss(ctx):
+    _check(_lib.mt_sync_loss(ctx), "mt_sync_loss", ctx)
 
 
 def mt_adamw_step(ctx, hp: mt_adamw_hparams, step: int):

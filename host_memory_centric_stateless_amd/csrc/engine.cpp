@@ -129,6 +129,7 @@ struct mt_ctx {
 
   hipEvent_t ev_ready[2] = {}, ev_free[2] = {}, ev_x0[2] = {}, ev_bwd_done[2] = {};
   hipEvent_t ev_written[64] = {}, ev_copied[64] = {}, ev_dx0[2] = {}, ev_dx0_copied[2] = {};
+  hipEvent_t ev_loss = nullptr;  // after the last forward's loss copy to the pinned ring
   bool x0_used[2] = {false, false}, bwd_used[2] = {false, false};
 
   int buf_unit[2] = {-1, -1};
@@ -968,6 +969,7 @@ extern "C" mt_status mt_create(const mt_config* cfg, const mt_device_arena* a, m
   }
   for (int i = 0; i < c->nslab; ++i)
     if (ev(&c->ev_written[i]) || ev(&c->ev_copied[i])) return MT_E_HIP;
+  if (ev(&c->ev_loss)) return MT_E_HIP;
 
   const size_t T = (size_t)p.T, h = (size_t)cfg->hidden;
   for (int i = 0; i < c->nslab; ++i)
@@ -1033,6 +1035,7 @@ extern "C" void mt_destroy(mt_ctx* c) {
   for (auto* e : evs)
     for (int i = 0; i < 2; ++i)
       if (e[i]) (void)hipEventDestroy(e[i]);
+  if (c->ev_loss) (void)hipEventDestroy(c->ev_loss);
   for (auto& r : c->krec) {
     c->ev_pool.push_back(r.a);
     c->ev_pool.push_back(r.b);
@@ -1143,6 +1146,7 @@ extern "C" mt_status mt_forward(mt_ctx* c, const int32_t* tokens, const int32_t*
   const int slot = c->loss_next;
   c->loss_next = (c->loss_next + 1) % mt_ctx::kLossRing;
   MT_HIP(c, hipMemcpyAsync(c->loss_pin + slot, c->ws + p.ws.loss, 4, hipMemcpyDeviceToHost, c->sc));
+  MT_HIP(c, hipEventRecord(c->ev_loss, c->sc));
   if (loss_out) c->pending_loss.emplace_back(loss_out, slot);
   c->state = ST_FWD;
   return MT_OK;
@@ -1200,6 +1204,17 @@ extern "C" mt_status mt_flush_grads(mt_ctx* c) {
   for (auto& pl : c->pending_loss) *pl.first = c->loss_pin[pl.second];
   c->pending_loss.clear();
   if (c->state == ST_BWD) c->state = ST_FLUSHED;
+  return MT_OK;
+}
+
+extern "C" mt_status mt_sync_loss(mt_ctx* c) {
+  mt_status r = check_live(c);
+  if (r != MT_OK) return r;
+  if (c->pending_loss.empty()) return MT_OK;
+  // every loss copy is on the compute stream, so the last one's event covers them all
+  MT_HIP(c, hipEventSynchronize(c->ev_loss));
+  for (auto& pl : c->pending_loss) *pl.first = c->loss_pin[pl.second];
+  c->pending_loss.clear();
   return MT_OK;
 }
 

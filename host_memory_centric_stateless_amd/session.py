@@ -14,7 +14,8 @@ import torch
 
 from . import (DEFAULT_DRAIN_WORKGROUPS, MT_GROUP_EMBED, MT_GROUP_HEAD, make_config, mt_adamw_hparams, mt_adamw_step,
                mt_backward, mt_backward_step, mt_bind_layer, mt_create, mt_destroy, mt_device_arena,
-               mt_device_requirements, mt_flush_grads, mt_forward, mt_get_stats, mt_layout)
+               mt_device_requirements, mt_flush_grads, mt_forward, mt_get_stats, mt_layout,
+               mt_sync_loss)
 
 
 def aligned_zeros(n: int, align: int = 64) -> np.ndarray:
@@ -137,10 +138,13 @@ class Session:
         return acc // n, tok, lab
 
     def step(self, tokens: np.ndarray, labels: np.ndarray, step: int, lr: Optional[float] = None,
-             weight_decay: float = 0.01, overlap_optimizer: bool = True) -> float:
+             weight_decay: float = 0.01, overlap_optimizer: bool = True, flush: bool = True) -> float:
         """One optimizer step.  overlap_optimizer: run each group's AdamW on
         the CPU worker as soon as its gradient of the last micro-batch is in
-        (mt_backward_step) instead of after the flush (mt_adamw_step)."""
+        (mt_backward_step) instead of after the flush (mt_adamw_step).
+        flush=False (overlapped optimizer only): return once the step's loss
+        is known, leaving the host updates of this step to finish under the
+        next step's forward; call flush() before reading grads or weights."""
         hp = mt_adamw_hparams(lr if lr is not None else self.cfg.lr, 0.9, 0.999, 1e-8, weight_decay)
         if not overlap_optimizer:
             loss = self.forward_backward(tokens, labels)
@@ -156,9 +160,17 @@ class Session:
                     mt_backward(self.ctx, 1 if k > 0 else 0)
                 else:
                     mt_backward_step(self.ctx, 1 if k > 0 else 0, hp, step)
-            mt_flush_grads(self.ctx)
+            if flush:
+                mt_flush_grads(self.ctx)
+            else:
+                mt_sync_loss(self.ctx)
         self._losses = losses
         return float(losses.mean())
+
+    def flush(self) -> None:
+        """Wait for every gradient drain, host accumulation and update."""
+        with torch.cuda.device(self.device):
+            mt_flush_grads(self.ctx)
 
     def stats(self) -> dict:
         return mt_get_stats(self.ctx)

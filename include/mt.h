@@ -220,6 +220,16 @@ mt_status mt_backward_step(mt_ctx* ctx, int32_t accumulate, const mt_adamw_hpara
  * idle; writes pending losses. */
 mt_status mt_flush_grads(mt_ctx* ctx);
 
+/* Wait only until the loss of every enqueued forward has been computed and
+ * write the pending losses (the *loss_out pointers given to mt_forward).
+ * Unlike mt_flush_grads it does not wait for slab drains, host accumulation
+ * or the overlapped optimizer, so a training loop of mt_backward_step steps
+ * can read each step's loss while the host is still updating that step's
+ * units (the next mt_forward waits per unit for its update).  Gradients and
+ * master weights may be read only after mt_flush_grads.  MT_E_ABORTED on a
+ * poisoned context; MT_E_HIP if the wait fails. */
+mt_status mt_sync_loss(mt_ctx* ctx);
+
 /* AdamW on every bound group (decoupled weight decay, bias correction, step is
  * 1-based), then refresh the pinned bf16 working copies.  Allowed only after
  * mt_flush_grads. */

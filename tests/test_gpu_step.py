@@ -226,6 +226,37 @@ def test_overlapped_optimizer_bit_exact(acc, slab_bf16, per_pass):
             np.testing.assert_array_equal(a, b, err_msg=f"group {g}")
 
 
+def test_steps_without_flush_bit_exact():
+    """Overlapped-optimizer steps that return at mt_sync_loss (no flush between
+    steps, so a step's host updates run under the next forward, which waits
+    per unit for them) must give the same losses and exactly the weights,
+    moments, gradients and working copies of flushing after every step.  The
+    worker is delayed so that the host really lags the GPU."""
+    cfg = PRESETS["C1"].replace(grad_accum=2)
+    runs = []
+    for flush in (True, False):
+        os.environ["MT_TEST_WORKER_DELAY_US"] = "3000"
+        try:
+            sess = _session(cfg)
+        finally:
+            del os.environ["MT_TEST_WORKER_DELAY_US"]
+        try:
+            losses = []
+            for step in (1, 2, 3):
+                tok, lab = make_batch(cfg, step)
+                losses.append(sess.step(tok, lab, step, flush=flush))
+            sess.flush()
+            runs.append((losses, {g: (sess.master[g].copy(), sess.m[g].copy(), sess.v[g].copy(),
+                                      sess.grad[g].copy()) for g in sess.groups}))
+            print("flush", flush, losses, sess.stats(), flush=True)
+        finally:
+            sess.close()
+    assert runs[0][0] == runs[1][0]
+    for g in runs[0][1]:
+        for a, b in zip(runs[0][1][g], runs[1][1][g]):
+            np.testing.assert_array_equal(a, b, err_msg=f"group {g}")
+
+
 def test_call_order_state_machine():
     from host_memory_centric_stateless_amd import (MT_E_STATE, MtError, mt_adamw_hparams,
                                                    mt_adamw_step, mt_backward, mt_flush_grads,
