@@ -200,11 +200,23 @@ def probe(cfg, reps: int = 2):
     return out
 
 
+CPU_SAMPLE_TOKENS = 4096
+
+
 def cpu_baseline(cfg, budget_s: float = 30.0):
-    """The oracle (fp32 NumPy) on one decoder layer at the same shape:
-    forward + recompute forward + backward, on this host's cores."""
+    """The oracle (fp32 NumPy) on one decoder layer of the same width:
+    forward + recompute forward + backward, on this host's cores.  The sample
+    holds at most CPU_SAMPLE_TOKENS tokens (one sequence of that length when
+    the configuration's sequences are longer): the oracle's attention keeps
+    the whole score matrix, which at 131,072 tokens would not fit in host
+    memory.  tokens/s is the sample's model TFLOP/s at the full
+    configuration's model flop per token."""
     from oracle import model as OM
     from synth_inputs import make_batch, tensor_specs
+    full = cfg
+    if cfg.micro_batch * cfg.seq_len > CPU_SAMPLE_TOKENS:
+        seq = min(cfg.seq_len, CPU_SAMPLE_TOKENS)
+        cfg = cfg.replace(seq_len=seq, micro_batch=max(1, CPU_SAMPLE_TOKENS // seq))
     rng = np.random.default_rng(0)
     T = cfg.micro_batch * cfg.seq_len
     W = {}
@@ -221,10 +233,11 @@ def cpu_baseline(cfg, budget_s: float = 30.0):
     per_layer_model = (model_flops_per_token(cfg.replace(n_layers=1, vocab=0)))
     tflops = per_layer_model * T / dt / 1e12
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    tok_s = tflops * 1e12 / model_flops_per_token(full)
     return {"value": tflops, "unit": "model TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"1 decoder layer ({cfg.name}) forward + recompute + backward on "
-                      f"{T} tokens, fp32 NumPy, {dt:.1f} s; tokens/s equivalent "
-                      f"{T / dt / cfg.n_layers:.1f}"}
+            "sample": f"1 decoder layer of {full.name} (hidden {cfg.hidden}) forward + recompute + "
+                      f"backward on {cfg.micro_batch} x {cfg.seq_len} tokens, fp32 NumPy, {dt:.1f} s; "
+                      f"tokens/s equivalent for the whole model {tok_s:.1f}"}
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_tn_bf16_7b_shape_traffic.txt")
