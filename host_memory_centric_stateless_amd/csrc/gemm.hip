@@ -207,6 +207,141 @@ __device__ inline bool tile_of(int bid, int nm, int nn, int& tm, int& tn) {
   return true;
 }
 
+// Epilogue of a BM x BN tile: acc[i][j][r] is C[row, col] with
+// row = 8*(r/4) + 4*(lane/32) + r%4 and col = lane%32 inside the 32x32
+// sub-tile (i, j).  tb: this wave's 32 x EPI_TP floats of LDS scratch.
+constexpr int EPI_TP = 40;  // floats per LDS row: lanes l and l+32 write disjoint banks
+
+template <int EPI, int BM, int BN, int WVM, int WVN>
+__device__ __forceinline__ void store_tile(const mt_gemm_args& p,
+                                           f32x16_t (&acc)[BM / WVM / 32][BN / WVN / 32],
+                                           int64_t m0, int64_t n0, int wm, int wn, int lane,
+                                           float* tb) {
+  constexpr bool SWI = (EPI == MT_EPI_SWIGLU);
+  constexpr int WM = BM / WVM, WN = BN / WVN, TM = WM / 32, TN = WN / 32;
+  constexpr int TP = EPI_TP;
+  const int g4 = (lane >> 5) * 4;
+  // The block is private to the wave, and LDS executes one wave's accesses in
+  // issue order, so a compiler-only barrier is enough between its writes and
+  // the reads of other lanes' values.  (A memory fence would also wait for
+  // the wave's outstanding global stores.)
+  auto lds_order = []() {
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+  };
+  auto turn = [&](const f32x16_t& v, float (&out)[16]) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) tb[(8 * (r >> 2) + g4 + (r & 3)) * TP + (lane & 31)] = v[r];
+    lds_order();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 x = *reinterpret_cast<const float4*>(tb + (lane >> 1) * TP + (lane & 1) * 16 + 4 * q);
+      out[4 * q + 0] = x.x; out[4 * q + 1] = x.y; out[4 * q + 2] = x.z; out[4 * q + 3] = x.w;
+    }
+    lds_order();
+  };
+  auto pack8 = [](const float* v) {
+    return u32x4{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]), pack_bf2(v[4], v[5]),
+                 pack_bf2(v[6], v[7])};
+  };
+  auto unpack8 = [](const u32x4 w, float* v) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] = bf2f((uint16_t)(w[e] & 0xffffu));
+      v[2 * e + 1] = bf2f((uint16_t)(w[e] >> 16));
+    }
+  };
+  if constexpr (SWI) {
+    uint16_t* C = static_cast<uint16_t*>(p.C);
+#pragma unroll
+    for (int j = 0; j < TN / 2; ++j)
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        float a[16], u[16];
+        turn(acc[i][j], a);
+        turn(acc[i][j + TN / 2], u);
+        const int64_t row = m0 + wm * WM + i * 32 + (lane >> 1);
+        const int64_t f0 = n0 + wn * (WN / 2) + j * 32 + (lane & 1) * 16;
+        if (row >= p.M) continue;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int64_t f = f0 + 8 * h;
+          if (f >= p.N) continue;
+          float y[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) y[e] = silu_f(a[8 * h + e]) * u[8 * h + e];
+          *reinterpret_cast<u32x4*>(p.gu + row * p.ldgu + f) = pack8(a + 8 * h);
+          *reinterpret_cast<u32x4*>(p.gu + row * p.ldgu + p.ffn + f) = pack8(u + 8 * h);
+          *reinterpret_cast<u32x4*>(C + row * p.ldc + f) = pack8(y);
+        }
+      }
+  } else {
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        float v[16];
+        turn(acc[i][j], v);
+        const int64_t row = m0 + wm * WM + i * 32 + (lane >> 1);
+        const int64_t c0 = n0 + wn * WN + j * 32 + (lane & 1) * 16;
+        if (row >= p.M) continue;
+        const bool in[2] = {c0 < p.N, c0 + 8 < p.N};
+        // every load of the sub-tile is issued before its first store, so the
+        // loads overlap (C may alias R, which forbids moving a load past a store)
+        if constexpr (EPI == MT_EPI_BF16) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            if (in[h])
+              *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.C) + row * p.ldc + c0 + 8 * h) =
+                  pack8(v + 8 * h);
+        } else if constexpr (EPI == MT_EPI_SWIGLU_BWD) {
+          u32x4 ga[2], gu_[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            if (in[h]) {
+              ga[h] = *reinterpret_cast<const u32x4*>(p.gu + row * p.ldgu + c0 + 8 * h);
+              gu_[h] = *reinterpret_cast<const u32x4*>(p.gu + row * p.ldgu + p.ffn + c0 + 8 * h);
+            }
+          uint16_t* C = static_cast<uint16_t*>(p.C);
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            if (!in[h]) continue;
+            float a[8], u[8], d0[8], d1[8];
+            unpack8(ga[h], a);
+            unpack8(gu_[h], u);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float x = v[8 * h + e];
+              const float sg = 1.0f / (1.0f + expf(-a[e]));
+              d0[e] = x * u[e] * sg * (1.0f + a[e] * (1.0f - sg));
+              d1[e] = x * a[e] * sg;
+            }
+            *reinterpret_cast<u32x4*>(C + row * p.ldc + c0 + 8 * h) = pack8(d0);
+            *reinterpret_cast<u32x4*>(C + row * p.ldc + p.ffn + c0 + 8 * h) = pack8(d1);
+          }
+        } else {
+          float* C = static_cast<float*>(p.C) + row * p.ldc + c0;
+          float4 add[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            add[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if constexpr (EPI == MT_EPI_F32_RESID) {
+              if (in[q >> 1]) add[q] = *reinterpret_cast<const float4*>(p.R + row * p.ldr + c0 + 4 * q);
+            } else if constexpr (EPI == MT_EPI_F32_ACCUM) {
+              if (in[q >> 1]) add[q] = *reinterpret_cast<const float4*>(C + 4 * q);
+            }
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (in[q >> 1])
+              *reinterpret_cast<float4*>(C + 4 * q) =
+                  make_float4(v[4 * q] + add[q].x, v[4 * q + 1] + add[q].y, v[4 * q + 2] + add[q].z,
+                              v[4 * q + 3] + add[q].w);
+        }
+      }
+  }
+}
+
 // BM x BN output tile per workgroup; each of the 4 waves owns a
 // (BM/2) x (BN/2) quadrant = TM x TN tiles of 32 x 32.  Larger tiles issue
 // fewer LDS fragment reads per MFMA (TM + TN reads feed TM * TN MFMAs).
@@ -377,129 +512,243 @@ __global__ __launch_bounds__(64 * WVM * WVN) void gemm_kernel(mt_gemm_args p, in
   // vector (N and the leading dimensions are multiples of 8, so each 8-column
   // half is wholly inside or outside the matrix).
   __syncthreads();  // the K loop's last fragment reads are done in every wave
-  constexpr int TP = 40;  // floats per LDS row: lanes l and l+32 write disjoint banks
-  static_assert(NTH / 64 * 32 * TP * 4 <= (int)sizeof(As), "epilogue scratch");
-  float* tb = reinterpret_cast<float*>(&As[0][0]) + (tid >> 6) * 32 * TP;
-  const int g4 = (lane >> 5) * 4;
-  // The block is private to the wave, and LDS executes one wave's accesses in
-  // issue order, so a compiler-only barrier is enough between its writes and
-  // the reads of other lanes' values.  (A memory fence would also wait for
-  // the wave's outstanding global stores.)
-  auto lds_order = []() {
-    __builtin_amdgcn_wave_barrier();
-    asm volatile("" ::: "memory");
-  };
-  auto turn = [&](const f32x16_t& v, float (&out)[16]) {
+  static_assert(NTH / 64 * 32 * EPI_TP * 4 <= (int)sizeof(As), "epilogue scratch");
+  store_tile<EPI, BM, BN, WVM, WVN>(p, acc, m0, n0, wm, wn, lane,
+                                    reinterpret_cast<float*>(&As[0][0]) + (tid >> 6) * 32 * EPI_TP);
+}
+
+// ------------------------------------------------- direct-to-LDS variant
+// The 256 x 256 tile when K is a multiple of 128 (every product of the model
+// shapes).  Operand tiles go from global memory straight into LDS with
+// buffer_load_dwordx4 ... lds: no VGPR staging and no ds_write, which in
+// timing probes of the register-staged kernel cost about a third of its time.
+// One such load moves 64 lanes x 16 bytes into 1 KB of LDS in lane order, so
+// the LDS tiles are unpadded and conflict-free fragment reads come from an
+// XOR swizzle of 16-byte chunks chosen on the global side.  The two stages
+// are separate LDS arrays and the K loop is unrolled by two, so that the
+// compiler can tell a DMA into one stage from fragment reads of the other.
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ inline void dma16(__amdgpu_buffer_rsrc_t rs, uint16_t* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds, 16, voff, 0, 0, 0);
+}
+
+// [row][k] operand, R rows x 64 k: LDS row r holds its eight 16-byte k
+// chunks with chunk c at slot c ^ ((r >> 1) & 7).  Load i of wave w fills
+// rows 8 (w V + i) .. +7; lane l writes row 8 (w V + i) + l/8, slot l%8.
+template <int R, int NTH>
+struct DLoadK {
+  static constexpr int V = R * 8 / NTH;  // loads per wave and tile
+  uint32_t off[V];
+  int64_t row_base = 0;
+  template <class Map>
+  __device__ inline void init(int64_t ld, const Map& rm, int wave, int lane) {
+    row_base = rm.row0;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) tb[(8 * (r >> 2) + g4 + (r & 3)) * TP + (lane & 31)] = v[r];
-    lds_order();
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float4 x = *reinterpret_cast<const float4*>(tb + (lane >> 1) * TP + (lane & 1) * 16 + 4 * q);
-      out[4 * q + 0] = x.x; out[4 * q + 1] = x.y; out[4 * q + 2] = x.z; out[4 * q + 3] = x.w;
+    for (int i = 0; i < V; ++i) {
+      const int r = 8 * (wave * V + i) + (lane >> 3);
+      const int c = (lane & 7) ^ ((r >> 1) & 7);
+      bool in;
+      const int64_t g = rm.map(r, in);  // out-of-range rows read a valid row; their results are not stored
+      off[i] = (uint32_t)(((g - row_base) * ld + c * 8) * 2);
     }
-    lds_order();
-  };
-  auto pack8 = [](const float* v) {
-    return u32x4{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]), pack_bf2(v[4], v[5]),
-                 pack_bf2(v[6], v[7])};
-  };
-  auto unpack8 = [](const u32x4 w, float* v) {
+  }
+  __device__ inline void load(const uint16_t* base, int64_t ld, int64_t extent, int64_t k0,
+                              uint16_t* lds, int wave) const {
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(base, row_base * ld + k0, extent);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      v[2 * e] = bf2f((uint16_t)(w[e] & 0xffffu));
-      v[2 * e + 1] = bf2f((uint16_t)(w[e] >> 16));
+    for (int i = 0; i < V; ++i) dma16(rs, lds + (wave * V + i) * 512, off[i]);
+  }
+};
+
+// [k][row] operand, 64 k x R rows (R = 256: two k-rows per load): LDS k-row
+// k holds its R/8 row chunks with chunk c at slot c ^ (2 (k & 3)), so the four
+// k-rows one transpose read touches fall on distinct banks.
+template <int R, int NTH>
+struct DLoadKT {
+  static constexpr int VPR = R / 8;            // chunks per k-row
+  static constexpr int V = 64 * VPR / NTH;     // loads per wave and tile
+  static_assert(512 % R == 0 && 64 % VPR == 0, "whole k-rows per load");
+  uint32_t off[V];
+  int64_t row0 = 0;
+  __device__ inline void init(int64_t ld, int64_t row0_, int wave, int lane) {
+    row0 = row0_;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const int e = 64 * (wave * V + i) + lane;  // chunk index in the tile
+      const int k = e / VPR;
+      const int c = (e % VPR) ^ (2 * (k & 3));
+      off[i] = (uint32_t)(((int64_t)k * ld + c * 8) * 2);
     }
-  };
-  if constexpr (SWI) {
-    uint16_t* C = static_cast<uint16_t*>(p.C);
+  }
+  __device__ inline void load(const uint16_t* base, int64_t ld, int64_t extent, int64_t k0,
+                              uint16_t* lds, int wave) const {
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(base, k0 * ld + row0, extent);
 #pragma unroll
-    for (int j = 0; j < TN / 2; ++j)
+    for (int i = 0; i < V; ++i) dma16(rs, lds + (wave * V + i) * 512, off[i]);
+  }
+};
+
+// MFMA fragment (rows row..row+31 over the lanes, k-step ks) of a swizzled
+// [row][64] tile.
+__device__ inline bf16x8_t frag_sw(const uint16_t* lds, int row, int ks, int lane) {
+  const int kc = ks * 2 + (lane >> 5);
+  return frag(lds + row * 64 + ((kc ^ ((row >> 1) & 7)) << 3));
+}
+
+// As frag_t, from a swizzled [64][R] tile.
+template <int R>
+__device__ inline bf16x8_t frag_tsw(const uint16_t* lds, int row_base, int ks, int lane) {
+  typedef short s4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s4 lds_s4;
+  const int g = lane >> 4, sl = lane & 15;
+  const int k = ks * 16 + 8 * (g >> 1) + (sl >> 2);
+  const int row = row_base + 16 * (g & 1) + 4 * (sl & 3);
+  const uint16_t* q = lds + k * R + ((((row >> 3) ^ (2 * (k & 3))) << 3) | (row & 7));
+  const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)q);
+  const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(q + 4 * R));  // k + 4: same swizzle
+  const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+  return __builtin_bit_cast(bf16x8_t, u32x4{a[0], a[1], b[0], b[1]});
+}
+
+template <int LAYOUT, int EPI>
+__global__ __launch_bounds__(512) void gemm_direct_kernel(mt_gemm_args p, int nm, int nn) {
+  constexpr int BM = 256, BN = 256, WVM = 2, WVN = 4, NTH = 512;
+  constexpr bool A_T = (LAYOUT == MT_GEMM_TN);
+  constexpr bool B_T = (LAYOUT != MT_GEMM_NT);
+  constexpr bool SWI = (EPI == MT_EPI_SWIGLU);
+  static_assert(!(SWI && B_T), "the SwiGLU product takes B as [rows][k]");
+  constexpr int WM = BM / WVM, WN = BN / WVN, TM = WM / 32, TN = WN / 32;
+  constexpr int HALF = BN / 2;
+  constexpr int TILE = 256 * 64;  // elements of one operand tile
+  __shared__ __attribute__((aligned(16))) uint16_t A0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t A1[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t B0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t B1[TILE];
+
+  int tm, tn;
+  if (!tile_of(blockIdx.x, nm, nn, tm, tn)) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WVN, wn = wave % WVN;
+  const int64_t m0 = (int64_t)tm * BM;
+  const int64_t n0 = (int64_t)tn * (SWI ? HALF : BN);
+  const int64_t K = p.K;
+  const uint16_t* A = p.A;
+  const uint16_t* B = p.B;
+
+  RowMap<BM, false> ra{m0, p.M, 0};
+  RowMap<HALF, SWI> rb{n0, p.N, SWI ? p.ffn : 0};
+  typename std::conditional<A_T, DLoadKT<BM, NTH>, DLoadK<BM, NTH>>::type la;
+  typename std::conditional<B_T, DLoadKT<BN, NTH>, DLoadK<BN, NTH>>::type lb;
+  if constexpr (A_T) la.init(p.lda, m0, wave, lane);
+  else la.init(p.lda, ra, wave, lane);
+  if constexpr (B_T) lb.init(p.ldb, n0, wave, lane);
+  else lb.init(p.ldb, rb, wave, lane);
+  const int64_t ext_a = A_T ? ((K - 1) * p.lda + p.M) * 2 : ((p.M - 1) * p.lda + K) * 2;
+  const int64_t ext_b = B_T ? ((K - 1) * p.ldb + p.N) * 2
+                            : (((SWI ? p.ffn : 0) + p.N - 1) * p.ldb + K) * 2;
+
+  f32x16_t acc[TM][TN];
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        float a[16], u[16];
-        turn(acc[i][j], a);
-        turn(acc[i][j + TN / 2], u);
-        const int64_t row = m0 + wm * WM + i * 32 + (lane >> 1);
-        const int64_t f0 = n0 + wn * (WN / 2) + j * 32 + (lane & 1) * 16;
-        if (row >= p.M) continue;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int64_t f = f0 + 8 * h;
-          if (f >= p.N) continue;
-          float y[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) y[e] = silu_f(a[8 * h + e]) * u[8 * h + e];
-          *reinterpret_cast<u32x4*>(p.gu + row * p.ldgu + f) = pack8(a + 8 * h);
-          *reinterpret_cast<u32x4*>(p.gu + row * p.ldgu + p.ffn + f) = pack8(u + 8 * h);
-          *reinterpret_cast<u32x4*>(C + row * p.ldc + f) = pack8(y);
-        }
-      }
-  } else {
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        float v[16];
-        turn(acc[i][j], v);
-        const int64_t row = m0 + wm * WM + i * 32 + (lane >> 1);
-        const int64_t c0 = n0 + wn * WN + j * 32 + (lane & 1) * 16;
-        if (row >= p.M) continue;
-        const bool in[2] = {c0 < p.N, c0 + 8 < p.N};
-        // every load of the sub-tile is issued before its first store, so the
-        // loads overlap (C may alias R, which forbids moving a load past a store)
-        if constexpr (EPI == MT_EPI_BF16) {
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  auto brow = [&](int j) {
+    if constexpr (SWI)
+      return (j < TN / 2) ? wn * (WN / 2) + j * 32 : HALF + wn * (WN / 2) + (j - TN / 2) * 32;
+    else
+      return wn * WN + j * 32;
+  };
+  const int arow = wm * WM + (lane & 31);
+
+  bf16x8_t fa[2][TM], fb[2][TN];
+  auto read_frags = [&](const uint16_t* as, const uint16_t* bs, int ks, int slot) {
 #pragma unroll
-          for (int h = 0; h < 2; ++h)
-            if (in[h])
-              *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.C) + row * p.ldc + c0 + 8 * h) =
-                  pack8(v + 8 * h);
-        } else if constexpr (EPI == MT_EPI_SWIGLU_BWD) {
-          u32x4 ga[2], gu_[2];
+    for (int i = 0; i < TM; ++i) {
+      if constexpr (A_T)
+        fa[slot][i] = frag_tsw<BM>(as, wm * WM + i * 32, ks, lane);
+      else
+        fa[slot][i] = frag_sw(as, arow + i * 32, ks, lane);
+    }
 #pragma unroll
-          for (int h = 0; h < 2; ++h)
-            if (in[h]) {
-              ga[h] = *reinterpret_cast<const u32x4*>(p.gu + row * p.ldgu + c0 + 8 * h);
-              gu_[h] = *reinterpret_cast<const u32x4*>(p.gu + row * p.ldgu + p.ffn + c0 + 8 * h);
-            }
-          uint16_t* C = static_cast<uint16_t*>(p.C);
+    for (int j = 0; j < TN; ++j) {
+      if constexpr (B_T)
+        fb[slot][j] = frag_tsw<BN>(bs, wn * WN + j * 32, ks, lane);
+      else
+        fb[slot][j] = frag_sw(bs, brow(j) + (lane & 31), ks, lane);
+    }
+  };
+  auto mfmas = [&](int slot) {
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            if (!in[h]) continue;
-            float a[8], u[8], d0[8], d1[8];
-            unpack8(ga[h], a);
-            unpack8(gu_[h], u);
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float x = v[8 * h + e];
-              const float sg = 1.0f / (1.0f + expf(-a[e]));
-              d0[e] = x * u[e] * sg * (1.0f + a[e] * (1.0f - sg));
-              d1[e] = x * a[e] * sg;
-            }
-            *reinterpret_cast<u32x4*>(C + row * p.ldc + c0 + 8 * h) = pack8(d0);
-            *reinterpret_cast<u32x4*>(C + row * p.ldc + p.ffn + c0 + 8 * h) = pack8(d1);
-          }
-        } else {
-          float* C = static_cast<float*>(p.C) + row * p.ldc + c0;
-          float4 add[4];
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j], acc[i][j], 0,
+                                                            0, 0);
+  };
+  constexpr int NREAD = (A_T ? 2 : 1) * TM + (B_T ? 2 : 1) * TN;
+  constexpr int RPM = (NREAD + TM * TN - 1) / (TM * TN);
+  auto interleave = [&]() {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            add[q] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if constexpr (EPI == MT_EPI_F32_RESID) {
-              if (in[q >> 1]) add[q] = *reinterpret_cast<const float4*>(p.R + row * p.ldr + c0 + 4 * q);
-            } else if constexpr (EPI == MT_EPI_F32_ACCUM) {
-              if (in[q >> 1]) add[q] = *reinterpret_cast<const float4*>(C + 4 * q);
-            }
-          }
+    for (int j = 0; j < TM * TN; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);
+    }
+  };
+  constexpr int KS = BK / 16;
+  // this wave's loads into LDS are complete (the barrier then covers every wave's)
+  auto wait_dma = []() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+
+  // One tile: the k-steps of the tile in (ca, cb) while the next tile's loads
+  // fill (na, nb); the last k-step runs after the barrier, under the reads of
+  // the next tile's first fragments (as in gemm_kernel).
+  auto tile = [&](const uint16_t* ca, const uint16_t* cb, uint16_t* na, uint16_t* nb,
+                  int64_t knext) {
+    la.load(A, p.lda, ext_a, knext, na, wave);
+    lb.load(B, p.ldb, ext_b, knext, nb, wave);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if (in[q >> 1])
-              *reinterpret_cast<float4*>(C + 4 * q) =
-                  make_float4(v[4 * q] + add[q].x, v[4 * q + 1] + add[q].y, v[4 * q + 2] + add[q].z,
-                              v[4 * q + 3] + add[q].w);
-        }
-      }
+    for (int ks = 0; ks < KS - 1; ++ks) {
+      __builtin_amdgcn_s_setprio(1);
+      read_frags(ca, cb, ks + 1, (ks + 1) & 1);
+      mfmas(ks & 1);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(0);
+    }
+    wait_dma();
+    __syncthreads();
+    __builtin_amdgcn_s_setprio(1);
+    read_frags(na, nb, 0, 0);
+    mfmas((KS - 1) & 1);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  const int nk = (int)(K / BK);  // even: K is a multiple of 128
+  la.load(A, p.lda, ext_a, 0, A0, wave);
+  lb.load(B, p.ldb, ext_b, 0, B0, wave);
+  wait_dma();
+  __syncthreads();
+  read_frags(A0, B0, 0, 0);
+  for (int kt = 0; kt < nk; kt += 2) {
+    tile(A0, B0, A1, B1, (int64_t)(kt + 1) * BK);
+    tile(A1, B1, A0, B0, (int64_t)(kt + 2) * BK);  // past the end: empty resource, zeros
   }
+
+  __syncthreads();  // the K loop's last fragment reads are done in every wave
+  // 8 waves x 32 x EPI_TP floats of scratch: waves 0..5 in A0, 6..7 in B0
+  static_assert(6 * 32 * EPI_TP * 4 <= (int)sizeof(A0) && 2 * 32 * EPI_TP * 4 <= (int)sizeof(B0),
+                "epilogue scratch");
+  float* tb = wave < 6 ? reinterpret_cast<float*>(A0) + wave * 32 * EPI_TP
+                       : reinterpret_cast<float*>(B0) + (wave - 6) * 32 * EPI_TP;
+  store_tile<EPI, BM, BN, WVM, WVN>(p, acc, m0, n0, wm, wn, lane, tb);
 }
 
 template <int LAYOUT, int EPI, int BM, int BN, int WVM, int WVN>
@@ -515,10 +764,22 @@ hipError_t launch_tiles(const mt_gemm_args& a, hipStream_t s) {
 // 256 x 256 tiles (8 waves of 128 x 64: two waves per SIMD) when the product
 // has enough of them to fill the chip, 128 x 128 (4 waves) otherwise.
 template <int LAYOUT, int EPI>
+hipError_t launch_direct(const mt_gemm_args& a, hipStream_t s) {
+  const int nn = (int)((EPI == MT_EPI_SWIGLU) ? (a.N + 127) / 128 : (a.N + 255) / 256);
+  const int nm = (int)((a.M + 255) / 256);
+  const int per = (nm * nn + NXCD - 1) / NXCD;
+  hipLaunchKernelGGL((gemm_direct_kernel<LAYOUT, EPI>), dim3((unsigned)(per * NXCD)), dim3(512), 0,
+                     s, a, nm, nn);
+  return hipGetLastError();
+}
+
+template <int LAYOUT, int EPI>
 hipError_t launch_one(const mt_gemm_args& a, hipStream_t s) {
   const int64_t nbig = ((a.M + 255) / 256) * ((a.N + 255) / 256);
-  if (a.M >= 1024 && a.N >= 1024 && nbig >= 128)
+  if (a.M >= 1024 && a.N >= 1024 && nbig >= 128) {
+    if (a.K % 128 == 0) return launch_direct<LAYOUT, EPI>(a, s);
     return launch_tiles<LAYOUT, EPI, 256, 256, 2, 4>(a, s);
+  }
   return launch_tiles<LAYOUT, EPI, 128, 128, 2, 2>(a, s);
 }
 

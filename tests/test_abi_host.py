@@ -271,9 +271,10 @@ def test_kernel_register_budget():
     meta = _kernel_metadata()
     names = [m[0] for m in meta]
     assert any("gemm_kernel" in n for n in names) and any("attn_fwd" in n for n in names)
+    assert any("gemm_direct_kernel" in n for n in names)
     for name, vgpr, spill, scratch in meta:
         assert spill == 0 and scratch == 0, (name, spill, scratch)
-        if ("gemm_kernel" in name and "256ELi256" in name) or "attn_" in name:
+        if ("gemm_kernel" in name and "256ELi256" in name) or "gemm_direct" in name or "attn_" in name:
             assert vgpr <= 248, (name, vgpr)
         if "copy16" in name:
             assert vgpr <= 16, (name, vgpr)

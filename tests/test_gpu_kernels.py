@@ -30,7 +30,10 @@ def _gemm_ref(layout, A, B):
 
 @pytest.mark.parametrize("layout", [mt.MT_GEMM_NT, mt.MT_GEMM_NN, mt.MT_GEMM_TN])
 @pytest.mark.parametrize("shape", [(200, 136, 88), (264, 392, 520), (512, 256, 4096),
-                                   (2056, 1288, 200), (4096, 4096, 256)])
+                                   (2056, 1288, 200), (4096, 4096, 256),
+                                   # 256 x 256 tiles with row and column tails: direct-to-LDS
+                                   # loads (K a multiple of 128), then register-staged (K tail)
+                                   (4104, 3080, 384), (4104, 3080, 328)])
 def test_gemm_layouts_f32_bf16(layout, shape):
     M, N, K = shape
     print(f"gemm layout={layout} shape={shape}", flush=True)
@@ -60,7 +63,8 @@ def test_gemm_layouts_f32_bf16(layout, shape):
     assert rel_max(host(Ca), ref + R[:, :N]) < 2e-5
 
 
-@pytest.mark.parametrize("T,h,F", [(136, 256, 688), (304, 512, 1408), (1032, 256, 1048)])
+@pytest.mark.parametrize("T,h,F", [(136, 256, 688), (304, 512, 1408), (1032, 256, 1048),
+                                   (4104, 256, 2056)])  # the last on 256 x 256 direct-to-LDS tiles
 def test_gemm_swiglu_forward_and_backward(T, h, F):
     print(f"swiglu T={T} h={h} F={F}", flush=True)
     n2 = random_array((T, h), seed=4)
