@@ -562,13 +562,15 @@ struct DLoadK {
 };
 
 // [k][row] operand, 64 k x R rows (R = 256: two k-rows per load): LDS k-row
-// k holds its R/8 row chunks with chunk c at slot c ^ (2 (k & 3)), so the four
-// k-rows one transpose read touches fall on distinct banks.
+// k holds its R/8 row chunks with chunk c at slot c ^ (4 (k & 3)).  Half a
+// wave's transpose read touches four k-rows (k & 3 = 0..3, same bank offset:
+// a k-row is 512 bytes) times four consecutive chunks (c & 3 = 0..3), and
+// the swizzle sends these 16 chunks to 16 distinct 16-byte bank groups.
 template <int R, int NTH>
 struct DLoadKT {
   static constexpr int VPR = R / 8;            // chunks per k-row
   static constexpr int V = 64 * VPR / NTH;     // loads per wave and tile
-  static_assert(512 % R == 0 && 64 % VPR == 0, "whole k-rows per load");
+  static_assert(512 % R == 0 && 64 % VPR == 0 && VPR >= 16, "whole k-rows per load");
   uint32_t off[V];
   int64_t row0 = 0;
   __device__ inline void init(int64_t ld, int64_t row0_, int wave, int lane) {
@@ -577,7 +579,7 @@ struct DLoadKT {
     for (int i = 0; i < V; ++i) {
       const int e = 64 * (wave * V + i) + lane;  // chunk index in the tile
       const int k = e / VPR;
-      const int c = (e % VPR) ^ (2 * (k & 3));
+      const int c = (e % VPR) ^ (4 * (k & 3));
       off[i] = (uint32_t)(((int64_t)k * ld + c * 8) * 2);
     }
   }
@@ -604,7 +606,7 @@ __device__ inline bf16x8_t frag_tsw(const uint16_t* lds, int row_base, int ks, i
   const int g = lane >> 4, sl = lane & 15;
   const int k = ks * 16 + 8 * (g >> 1) + (sl >> 2);
   const int row = row_base + 16 * (g & 1) + 4 * (sl & 3);
-  const uint16_t* q = lds + k * R + ((((row >> 3) ^ (2 * (k & 3))) << 3) | (row & 7));
+  const uint16_t* q = lds + k * R + ((((row >> 3) ^ (4 * (k & 3))) << 3) | (row & 7));
   const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)q);
   const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(q + 4 * R));  // k + 4: same swizzle
   const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
