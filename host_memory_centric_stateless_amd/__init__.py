@@ -91,7 +91,8 @@ class mt_stats(C.Structure):
                 ("layer_forwards", C.c_int64), ("layer_backwards", C.c_int64),
                 ("slab_waits", C.c_int64), ("slab_wait_s", C.c_double),
                 ("accumulate_s", C.c_double), ("adamw_s", C.c_double),
-                ("microbatches", C.c_int64)]
+                ("microbatches", C.c_int64), ("timed_copy_ms", C.c_double),
+                ("timed_kernel_ms", C.c_double), ("timed_overlap_ms", C.c_double)]
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}

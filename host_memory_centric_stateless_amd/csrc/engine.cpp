@@ -130,6 +130,7 @@ struct mt_ctx {
   hipEvent_t ev_ready[2] = {}, ev_free[2] = {}, ev_x0[2] = {}, ev_bwd_done[2] = {};
   hipEvent_t ev_written[64] = {}, ev_copied[64] = {}, ev_dx0[2] = {}, ev_dx0_copied[2] = {};
   hipEvent_t ev_loss = nullptr;  // after the last forward's loss copy to the pinned ring
+  hipEvent_t ev_origin = nullptr;  // timing origin, recorded when kernel timing is enabled
   bool x0_used[2] = {false, false}, bwd_used[2] = {false, false};
 
   int buf_unit[2] = {-1, -1};
@@ -192,7 +193,54 @@ struct mt_ctx {
     if (hipEventCreate(&e) != hipSuccess) return nullptr;
     return e;
   }
+  // Timed intervals of one flush: host-link copies and compute kernels, as
+  // [start, end) in ms from ev_origin; their union measures and the measure
+  // of their intersection go into the stats.
+  static bool is_copy(const char* n) {
+    return !strcmp(n, "h2d_load") || !strcmp(n, "h2d_input") || !strcmp(n, "drain_d2h");
+  }
+  static std::vector<std::pair<double, double>> union_of(std::vector<std::pair<double, double>> v) {
+    std::sort(v.begin(), v.end());
+    std::vector<std::pair<double, double>> u;
+    for (auto& x : v) {
+      if (!u.empty() && x.first <= u.back().second)
+        u.back().second = std::max(u.back().second, x.second);
+      else
+        u.push_back(x);
+    }
+    return u;
+  }
+  static double measure(const std::vector<std::pair<double, double>>& u) {
+    double m = 0;
+    for (auto& x : u) m += x.second - x.first;
+    return m;
+  }
+  hipError_t collect_overlap() {
+    std::vector<std::pair<double, double>> cp, kn;
+    for (auto& r : krec) {
+      float a = 0.0f, b = 0.0f;
+      hipError_t e = hipEventElapsedTime(&a, ev_origin, r.a);
+      if (e == hipSuccess) e = hipEventElapsedTime(&b, ev_origin, r.b);
+      if (e != hipSuccess) return e;
+      (is_copy(r.name) ? cp : kn).emplace_back(a, b);
+    }
+    const auto uc = union_of(cp), uk = union_of(kn);
+    double both = 0;
+    for (size_t i = 0, j = 0; i < uc.size() && j < uk.size();) {
+      const double lo = std::max(uc[i].first, uk[j].first), hi = std::min(uc[i].second, uk[j].second);
+      if (lo < hi) both += hi - lo;
+      if (uc[i].second < uk[j].second) ++i; else ++j;
+    }
+    st.timed_copy_ms += measure(uc);
+    st.timed_kernel_ms += measure(uk);
+    st.timed_overlap_ms += both;
+    return hipSuccess;
+  }
   hipError_t collect_kernel_times() {
+    if (!krec.empty()) {
+      hipError_t e = collect_overlap();
+      if (e != hipSuccess) return e;
+    }
     for (auto& r : krec) {
       float ms = 0.0f;
       hipError_t e = hipEventElapsedTime(&ms, r.a, r.b);
@@ -553,7 +601,10 @@ mt_status issue_load(mt_ctx* c, const Load& ld) {
     if (c->poisoned) return MT_E_ABORTED;
   }
   MT_HIP(c, hipStreamWaitEvent(c->sp, c->ev_free[ld.buf], 0));
-  MT_HIP(c, hipMemcpyAsync(c->wbuf[ld.buf], src, (size_t)n * 2, hipMemcpyHostToDevice, c->sp));
+  {
+    KScope k(c, c->sp, "h2d_load", 0, (double)n * 2);
+    MT_HIP(c, hipMemcpyAsync(c->wbuf[ld.buf], src, (size_t)n * 2, hipMemcpyHostToDevice, c->sp));
+  }
   MT_HIP(c, hipEventRecord(c->ev_ready[ld.buf], c->sp));
   c->st.h2d_bytes += n * 2;
   c->st.weight_loads += 1;
@@ -853,7 +904,10 @@ mt_status run_step(mt_ctx* c, const Step& s) {
       float* dx0 = c->wsp<float>(c->dy_idx ? p.ws.dy1 : p.ws.dy0);
       MT_HIP(c, hipEventRecord(c->ev_dx0[par], cs));
       MT_HIP(c, hipStreamWaitEvent(c->so, c->ev_dx0[par], 0));
-      MT_HIP(c, drain(c, c->dx0_stage[par], dx0, (size_t)T * h * 4));
+      {
+        KScope k(c, c->so, "drain_d2h", 0, (double)T * h * 4);
+        MT_HIP(c, drain(c, c->dx0_stage[par], dx0, (size_t)T * h * 4));
+      }
       MT_HIP(c, hipEventRecord(c->ev_dx0_copied[par], c->so));
       c->st.d2h_bytes += T * h * 4;
       Job j;
@@ -970,6 +1024,7 @@ extern "C" mt_status mt_create(const mt_config* cfg, const mt_device_arena* a, m
   for (int i = 0; i < c->nslab; ++i)
     if (ev(&c->ev_written[i]) || ev(&c->ev_copied[i])) return MT_E_HIP;
   if (ev(&c->ev_loss)) return MT_E_HIP;
+  if (hipEventCreate(&c->ev_origin) != hipSuccess) return MT_E_HIP;
 
   const size_t T = (size_t)p.T, h = (size_t)cfg->hidden;
   for (int i = 0; i < c->nslab; ++i)
@@ -1036,6 +1091,7 @@ extern "C" void mt_destroy(mt_ctx* c) {
     for (int i = 0; i < 2; ++i)
       if (e[i]) (void)hipEventDestroy(e[i]);
   if (c->ev_loss) (void)hipEventDestroy(c->ev_loss);
+  if (c->ev_origin) (void)hipEventDestroy(c->ev_origin);
   for (auto& r : c->krec) {
     c->ev_pool.push_back(r.a);
     c->ev_pool.push_back(r.b);
@@ -1129,10 +1185,13 @@ extern "C" mt_status mt_forward(mt_ctx* c, const int32_t* tokens, const int32_t*
   // the device copies of x0 / labels of two micro-batches ago are free once
   // that micro-batch's backward has finished
   if (c->bwd_used[par]) MT_HIP(c, hipStreamWaitEvent(c->sp, c->ev_bwd_done[par], 0));
-  MT_HIP(c, hipMemcpyAsync(c->ws + p.ws.x0[par], c->x0_stage[par], (size_t)T * h * 4,
-                           hipMemcpyHostToDevice, c->sp));
-  MT_HIP(c, hipMemcpyAsync(c->ws + p.ws.labels[par], c->lab_stage[par], (size_t)T * 4,
-                           hipMemcpyHostToDevice, c->sp));
+  {
+    KScope k(c, c->sp, "h2d_input", 0, (double)T * (h + 1) * 4);
+    MT_HIP(c, hipMemcpyAsync(c->ws + p.ws.x0[par], c->x0_stage[par], (size_t)T * h * 4,
+                             hipMemcpyHostToDevice, c->sp));
+    MT_HIP(c, hipMemcpyAsync(c->ws + p.ws.labels[par], c->lab_stage[par], (size_t)T * 4,
+                             hipMemcpyHostToDevice, c->sp));
+  }
   MT_HIP(c, hipEventRecord(c->ev_x0[par], c->sp));
   c->x0_used[par] = true;
   MT_HIP(c, hipStreamWaitEvent(c->sc, c->ev_x0[par], 0));
@@ -1253,6 +1312,7 @@ extern "C" mt_status mt_kernel_timing(mt_ctx* c, int32_t enable) {
       c->ev_pool.push_back(k.b);
     }
     c->krec.clear();
+    MT_HIP(c, hipEventRecord(c->ev_origin, c->sc));
   }
   c->ktiming = enable != 0;
   return MT_OK;

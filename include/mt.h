@@ -147,6 +147,13 @@ typedef struct mt_stats {
   double accumulate_s;        /* worker seconds adding slabs into host grads   */
   double adamw_s;             /* seconds in mt_adamw_step                      */
   int64_t microbatches;
+  /* While mt_kernel_timing is enabled, from the same HIP timing events, added
+   * up at each mt_flush_grads: device time with a host-link copy in flight
+   * (weight and input loads, gradient and dx0 drains), with a compute kernel
+   * running, and with both at once (union measures, milliseconds). */
+  double timed_copy_ms;
+  double timed_kernel_ms;
+  double timed_overlap_ms;
 } mt_stats;
 
 typedef struct mt_ctx mt_ctx;

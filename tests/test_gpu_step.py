@@ -257,6 +257,35 @@ def test_steps_without_flush_bit_exact():
             np.testing.assert_array_equal(a, b, err_msg=f"group {g}")
 
 
+def test_timed_overlap_stats():
+    """With kernel timing on, the flush adds up device time with a host-link
+    copy in flight, with a kernel running and with both; the weight loads
+    appear as their own timed kind with their bytes."""
+    from host_memory_centric_stateless_amd import mt_get_kernel_times, mt_kernel_timing
+    cfg = PRESETS["C1"].replace(grad_accum=2)
+    sess = _session(cfg)
+    try:
+        mt_kernel_timing(sess.ctx, True)
+        s0 = sess.stats()
+        for step in (1, 2):
+            tok, lab = make_batch(cfg, step)
+            sess.step(tok, lab, step)
+        s1 = sess.stats()
+        kinds = {k["name"]: k for k in mt_get_kernel_times(sess.ctx)}
+    finally:
+        sess.close()
+    c = s1["timed_copy_ms"] - s0["timed_copy_ms"]
+    k = s1["timed_kernel_ms"] - s0["timed_kernel_ms"]
+    both = s1["timed_overlap_ms"] - s0["timed_overlap_ms"]
+    print("copy", c, "kernel", k, "both", both, flush=True)
+    assert c > 0 and k > 0 and 0 <= both <= min(c, k) + 1e-6
+    loads = s1["weight_loads"] - s0["weight_loads"]
+    unit = sum(n for _, _, _, n in OL.group_layout(cfg, 0)[0])  # a block's elements (no padding at C1)
+    assert kinds["h2d_load"]["launches"] == loads
+    assert kinds["h2d_load"]["bytes"] >= loads * unit * 2 * 0.5
+    assert "drain_d2h" in kinds and "h2d_input" in kinds
+
+
 def test_call_order_state_machine():
     from host_memory_centric_stateless_amd import (MT_E_STATE, MtError, mt_adamw_hparams,
                                                    mt_adamw_step, mt_backward, mt_flush_grads,
