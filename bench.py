@@ -265,6 +265,20 @@ def measured_traffic(kernel: str, cfg_name: str, default_shape: bool):
     return float(fields["traffic_bytes_per_launch"])
 
 
+def host_roofline(n: int = 1 << 28, reps: int = 5):
+    """Host-memory bandwidth of a STREAM-style triad (a = b + s c, 12 bytes per
+    element counted) on the library's default thread count: the roofline of
+    the host AdamW and slab accumulation."""
+    import host_memory_centric_stateless_amd as mt
+    from host_memory_centric_stateless_amd.session import aligned_zeros
+    a, b, c = aligned_zeros(n), aligned_zeros(n), aligned_zeros(n)
+    b += 1.0
+    c += 2.0
+    t = mt.mt_host_triad(a, b, c, 3.0, reps=reps)
+    del a, b, c
+    return {"triad_GBps": 12.0 * n / t / 1e9, "bytes": 12 * n, "threads": "library default (<= 16)"}
+
+
 def overlap(s0, s1):
     """Copy/compute overlap over the timed steps, from the library's HIP timing
     events: |copies AND kernels| / min(|copies|, |kernels|) (union measures;
@@ -385,6 +399,14 @@ def main():
 
     gemm = time_dominant_gemm(sess)
     link = link_roofline(sess.req.weight_buf)
+    host = host_roofline()
+    # host bytes per parameter and step: the last micro-batch's fused add + AdamW +
+    # bf16 recast (32 B, or 36 B when it adds to an earlier micro-batch's gradient);
+    # the other micro-batches' bf16 slab accumulation (6 B for the first, 10 B after)
+    n_params = sum(sess.layout[g][1] for g in sess.groups)
+    adamw_bpp = 36 if cfg.grad_accum > 1 else 32
+    acc_bpp = (6 + 10 * (cfg.grad_accum - 2)) if cfg.grad_accum > 1 else 0
+    acc_s = (s1["accumulate_s"] - s0["accumulate_s"]) / args.steps
     step_no = 1 + args.warmup + args.steps
     kernels = []
     for k in ktimes:
@@ -477,6 +499,13 @@ def main():
                        else f"copy kernel, {sess.c.drain_workgroups} workgroups"),
         "mfma_frac_end_to_end": model_tflops / MFMA_BF16_PEAK_TFLOPS,
         "h2d_GBps": h2d, "d2h_GBps": d2h, "adamw_s_per_step": adamw_s,
+        "host_roofline": host,
+        "host_adamw": {"GBps": n_params * adamw_bpp / adamw_s / 1e9 if adamw_s > 0 else None,
+                       "bytes_per_param": adamw_bpp, "params": n_params,
+                       "frac_of_triad": (n_params * adamw_bpp / adamw_s / 1e9) / host["triad_GBps"]
+                       if adamw_s > 0 else None},
+        "host_accumulate": {"GBps": n_params * acc_bpp / acc_s / 1e9 if acc_s > 0 else None,
+                            "bytes_per_param_per_step": acc_bpp},
         "loss_last": losses[-1],
         "link_roofline": link,
         "h2d_frac_of_link": h2d / link["h2d_GBps"],

@@ -136,6 +136,7 @@ _SIGS = {
     "mt_host_adamw_slab": ([_P, _P, _P, _P, _P, _P, _I32, _I32, _I64, C.POINTER(mt_adamw_hparams),
                             _I64, _I32], C.c_int),
     "mt_host_rope_table": ([_I32, _I32, _F, _P, _P], C.c_int),
+    "mt_host_triad": ([_P, _P, _P, _F, _I64, _I32, _I32, C.POINTER(C.c_double)], C.c_int),
     "mtk_gemm": ([C.POINTER(mt_gemm_args), _P], C.c_int),
     "mtk_rmsnorm_fwd": ([_P, _P, _P, _P, _I64, _I32, _F, _P], C.c_int),
     "mtk_rmsnorm_bwd_workspace": ([_I64, _I32], C.c_size_t),
@@ -298,6 +299,14 @@ def mt_host_adamw_slab(master, grad, m, v, bf16_out, slab, accumulate: int,
 def mt_host_accumulate(grad, src, accumulate: int, threads: int = 0):
     _check(_lib.mt_host_accumulate(_ptr(grad), _ptr(src), grad.size, accumulate, threads),
            "mt_host_accumulate")
+
+
+def mt_host_triad(a, b, c, s: float, reps: int = 5, threads: int = 0) -> float:
+    """Fastest of `reps` passes of a = b + s c (host float32 arrays), seconds."""
+    t = C.c_double()
+    _check(_lib.mt_host_triad(_ptr(a), _ptr(b), _ptr(c), s, a.size, reps, threads, C.byref(t)),
+           "mt_host_triad")
+    return t.value
 
 
 def mt_host_rope_table(seq_len: int, head_dim: int, base: float):

@@ -15,6 +15,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <chrono>
 
 namespace mt {
 
@@ -321,6 +322,25 @@ extern "C" mt_status mt_host_accumulate(float* grad, const float* src, int64_t n
   if (n < 0 || (n > 0 && (!grad || !src))) return MT_E_ARG;
   ThreadPool pool(nthreads(threads));
   accumulate(pool, grad, src, n, accumulate_flag != 0);
+  return MT_OK;
+}
+
+extern "C" mt_status mt_host_triad(float* a, const float* b, const float* c, float s, int64_t n,
+                                   int32_t reps, int32_t threads, double* best_s) {
+  if (n < 1 || reps < 1 || !a || !b || !c || !best_s) return MT_E_ARG;
+  ThreadPool pool(nthreads(threads));
+  double best = 1e30;
+  for (int32_t r = 0; r < reps; ++r) {
+    const auto t0 = std::chrono::steady_clock::now();
+    chunked(pool, n, [&](int64_t lo, int64_t hi) {
+      float* __restrict x = a;
+      const float* __restrict y = b;
+      const float* __restrict z = c;
+      for (int64_t i = lo; i < hi; ++i) x[i] = y[i] + s * z[i];
+    });
+    best = std::min(best, std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count());
+  }
+  *best_s = best;
   return MT_OK;
 }
 

@@ -286,6 +286,15 @@ mt_status mt_host_adamw_slab(float* master, float* grad, float* m, float* v, uin
 mt_status mt_host_accumulate(float* grad, const float* src, int64_t n, int32_t accumulate,
                              int32_t threads);
 
+/* Host-memory bandwidth probe, the roofline of the host optimizer and
+ * accumulation loops: a[i] = b[i] + s * c[i] for i < n (the STREAM triad), reps
+ * passes on `threads` threads (0: the library's default count, as for its
+ * own pools).  Writes the fastest pass's seconds to *best_s.  MT_E_ARG for
+ * n < 1, reps < 1 or a NULL pointer.  Arrays are the caller's, 64-byte
+ * aligned for full speed. */
+mt_status mt_host_triad(float* a, const float* b, const float* c, float s, int64_t n, int32_t reps,
+                        int32_t threads, double* best_s);
+
 /* RoPE cos/sin tables [seq_len, head_dim/2] from float64 angles
  * pos * base^(-2i/head_dim), rounded to fp32. */
 mt_status mt_host_rope_table(int32_t seq_len, int32_t head_dim, float base, float* cos_out,

@@ -168,6 +168,20 @@ def test_host_adamw_slab_equals_accumulate_then_adamw(slab_bf16, accumulate):
         np.testing.assert_array_equal(x, y, err_msg=name)
 
 
+def test_host_triad_computes_and_times():
+    """The host-memory bandwidth probe computes a = b + s c and reports a
+    positive time; bad arguments are rejected."""
+    n = 1 << 16
+    rng = np.random.default_rng(3)
+    b = rng.standard_normal(n, dtype=np.float32)
+    c = rng.standard_normal(n, dtype=np.float32)
+    a = np.empty_like(b)
+    t = mt.mt_host_triad(a, b, c, 0.5, reps=2, threads=2)
+    assert t > 0
+    np.testing.assert_array_equal(a, b + np.float32(0.5) * c)
+    with pytest.raises(mt.MtError):
+        mt.mt_host_triad(a[:0], b[:0], c[:0], 0.5)
+
 @pytest.mark.parametrize("s,d", [(128, 64), (4096, 128), (131072, 128)])
 def test_rope_table_matches_oracle(s, d):
     c, sn = mt.mt_host_rope_table(s, d, 10000.0)
