@@ -45,12 +45,14 @@ def _sync_state(sess, st):
     sess.bind()
 
 
-def gradients_at_matched_weights(cfg, steps, report, **kw):
+def gradients_at_matched_weights(cfg, steps, report, weights=None, **kw):
     """Each step starts the GPU from the oracle's state, so the gradient
-    comparison measures the kernels, not the divergence of two trajectories."""
+    comparison measures the kernels, not the divergence of two trajectories.
+    weights: the (group, name, array) stream of initial masters (default: the
+    seeded N(0, 0.02) draw)."""
     sess = _session(cfg, **kw)
     st = HostState(cfg, np.float32)
-    st.load_weights(weight_stream(cfg, 0))
+    st.load_weights(weights if weights is not None else weight_stream(cfg, 0))
     worst = {"loss": 0.0, "grad": 0.0}
     try:
         for step in range(1, steps + 1):
