@@ -122,7 +122,9 @@ def test_rmsnorm_forward_backward(T, h):
     assert np.all(np.abs(host(dxb) - (dx_ref + resid)) <= BF16_REL * np.abs(dx_ref + resid) + 1e-5)
 
 
-@pytest.mark.parametrize("b,s,nq,nkv,d", [(2, 128, 4, 2, 64), (1, 256, 5, 1, 128)])
+@pytest.mark.parametrize("b,s,nq,nkv,d", [(2, 128, 4, 2, 64), (1, 256, 5, 1, 128),
+                                         (2, 128, 2, 2, 16),   # eight-pair kernel, one thread per head
+                                         (1, 128, 3, 1, 24)])  # d not a multiple of 16: one pair per thread
 def test_rope_forward_inverse(b, s, nq, nkv, d):
     T = b * s
     W = (nq + 2 * nkv) * d
