@@ -1201,7 +1201,14 @@ extern "C" mt_status mt_forward(mt_ctx* c, const int32_t* tokens, const int32_t*
   c->dy_idx = 0;
   r = run_until(c, c->split, n_valid, grad_scale);
   if (r != MT_OK) return r;
-  // loss -> pinned ring, resolved at flush
+  // loss -> pinned ring, resolved at flush or mt_sync_loss; if this forward's
+  // slot still holds an unresolved loss (a whole ring of forwards without
+  // either call), the pending losses are resolved first
+  if (!c->pending_loss.empty() && c->pending_loss.front().second == c->loss_next) {
+    MT_HIP(c, hipEventSynchronize(c->ev_loss));
+    for (auto& pl : c->pending_loss) *pl.first = c->loss_pin[pl.second];
+    c->pending_loss.clear();
+  }
   const int slot = c->loss_next;
   c->loss_next = (c->loss_next + 1) % mt_ctx::kLossRing;
   MT_HIP(c, hipMemcpyAsync(c->loss_pin + slot, c->ws + p.ws.loss, 4, hipMemcpyDeviceToHost, c->sc));

@@ -779,7 +779,9 @@ template <int LAYOUT, int EPI>
 hipError_t launch_one(const mt_gemm_args& a, hipStream_t s) {
   const int64_t nbig = ((a.M + 255) / 256) * ((a.N + 255) / 256);
   if (a.M >= 1024 && a.N >= 1024 && nbig >= 128) {
-    if (a.K % 128 == 0) return launch_direct<LAYOUT, EPI>(a, s);
+    // the direct loads move 16-byte chunks: operand bases must be 16-byte aligned
+    if (a.K % 128 == 0 && (((uintptr_t)a.A | (uintptr_t)a.B) & 15) == 0)
+      return launch_direct<LAYOUT, EPI>(a, s);
     return launch_tiles<LAYOUT, EPI, 256, 256, 2, 4>(a, s);
   }
   return launch_tiles<LAYOUT, EPI, 128, 128, 2, 2>(a, s);
