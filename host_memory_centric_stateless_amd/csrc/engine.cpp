@@ -1234,6 +1234,12 @@ static mt_status backward_impl(mt_ctx* c, int32_t accumulate_flag, const mt_adam
     c->hp = *hp;
     c->opt_step = step;
   }
+  // The previous micro-batch's embedding gradient may still be draining from
+  // dy0/dy1 on the offload stream; this backward overwrites both (the final
+  // norm's backward and the first block backward), so the compute stream
+  // waits for that drain first (write after read across streams).
+  if (c->bwd_used[c->parity ^ 1])
+    MT_HIP(c, hipStreamWaitEvent(c->sc, c->ev_dx0_copied[c->parity ^ 1], 0));
   r = run_until(c, c->steps.size(), nullptr, 0.0f);
   c->fused = false;
   if (r != MT_OK) return r;

@@ -81,3 +81,39 @@ def test_planted_mistake_is_caught(mutation):
             except Exception:
                 failed.append(name)
     assert failed, f"no pin caught {mutation}"
+
+
+# ------------------------------------------- accumulation and step loss
+import inspect
+import textwrap
+
+import oracle.train as TR
+import tests.test_oracle_accumulation as A
+
+TRAIN_MUTATIONS = {
+    "accumulation_not_scaled": ("scale = 1.0 / acc", "scale = 1.0"),
+    "step_loss_summed": ("np.mean(losses)", "np.sum(losses)"),
+}
+ACC_PINS = ["test_repeated_microbatch_equals_single_step",
+            "test_two_microbatches_average_their_gradients_and_losses"]
+
+
+@pytest.mark.parametrize("mutation", sorted(TRAIN_MUTATIONS))
+def test_planted_accumulation_mistake_is_caught(mutation):
+    old, new = TRAIN_MUTATIONS[mutation]
+    src = textwrap.dedent(inspect.getsource(TR.train_step))
+    assert src.count(old) == 1, "the planted slip no longer matches the oracle's source"
+    ns = dict(vars(TR))
+    exec(compile(src.replace(old, new), TR.__file__, "exec"), ns)
+    orig = TR.train_step
+    TR.train_step = ns["train_step"]
+    failed = []
+    try:
+        for name in ACC_PINS:
+            try:
+                getattr(A, name)()
+            except Exception:
+                failed.append(name)
+    finally:
+        TR.train_step = orig
+    assert failed, f"no pin caught {mutation}"
