@@ -37,7 +37,8 @@ if len(_hip_runtimes()) > 1:
 MT_OK, MT_E_ARG, MT_E_STATE, MT_E_HIP, MT_E_NOMEM, MT_E_UNBOUND, MT_E_ABORTED = 0, -1, -2, -3, -4, -5, -6
 MT_GROUP_EMBED, MT_GROUP_HEAD = -1, -2
 MT_GEMM_NT, MT_GEMM_NN, MT_GEMM_TN = 0, 1, 2
-MT_EPI_BF16, MT_EPI_F32, MT_EPI_F32_RESID, MT_EPI_F32_ACCUM, MT_EPI_SWIGLU, MT_EPI_SWIGLU_BWD = range(6)
+(MT_EPI_BF16, MT_EPI_F32, MT_EPI_F32_RESID, MT_EPI_F32_ACCUM, MT_EPI_SWIGLU, MT_EPI_SWIGLU_BWD,
+ MT_EPI_ROPE) = range(7)
 _STATUS = {0: "MT_OK", -1: "MT_E_ARG", -2: "MT_E_STATE", -3: "MT_E_HIP", -4: "MT_E_NOMEM",
            -5: "MT_E_UNBOUND", -6: "MT_E_ABORTED"}
 
@@ -108,7 +109,8 @@ class mt_gemm_args(C.Structure):
                 ("N", C.c_int64), ("K", C.c_int64), ("A", C.c_void_p), ("lda", C.c_int64),
                 ("B", C.c_void_p), ("ldb", C.c_int64), ("C", C.c_void_p), ("ldc", C.c_int64),
                 ("R", C.c_void_p), ("ldr", C.c_int64), ("gu", C.c_void_p), ("ldgu", C.c_int64),
-                ("ffn", C.c_int64)]
+                ("ffn", C.c_int64), ("rope_cos", C.c_void_p), ("rope_sin", C.c_void_p),
+                ("rope_cols", C.c_int64), ("rope_seq", C.c_int32), ("rope_dim", C.c_int32)]
 
 
 _P = C.c_void_p
@@ -145,6 +147,8 @@ _SIGS = {
     "mtk_attention_fwd": ([_P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P], C.c_int),
     "mtk_attention_bwd_workspace": ([_I32, _I32, _I32, _I32, _I32], C.c_size_t),
     "mtk_attention_bwd": ([_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P], C.c_int),
+    "mtk_attention_bwd_rope": ([_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P],
+                               C.c_int),
     "mtk_cross_entropy": ([_P, _I64, _P, _I64, _I32, _F, _I64, _P, _I64, _P, _P, _P], C.c_int),
     "mtk_copy": ([_P, _P, C.c_size_t, _I32, _P], C.c_int),
 }
@@ -318,9 +322,11 @@ def mt_host_rope_table(seq_len: int, head_dim: int, base: float):
 
 # -------------------------------------------------------- kernel entry points
 def mtk_gemm(layout, epilogue, M, N, K, A, lda, B, ldb, Cm, ldc, R=None, ldr=0, gu=None, ldgu=0,
-             ffn=0, stream=None):
+             ffn=0, stream=None, rope_cos=None, rope_sin=None, rope_cols=0, rope_seq=0,
+             rope_dim=0):
     a = mt_gemm_args(layout, epilogue, M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(Cm), ldc,
-                     _ptr(R), ldr, _ptr(gu), ldgu, ffn)
+                     _ptr(R), ldr, _ptr(gu), ldgu, ffn, _ptr(rope_cos), _ptr(rope_sin), rope_cols,
+                     rope_seq, rope_dim)
     _check(_lib.mtk_gemm(C.byref(a), _stream(stream)), "mtk_gemm")
 
 
@@ -358,6 +364,14 @@ def mtk_attention_bwd(qkv, o, dout, lse, workspace, dqkv, batch, seq_len, n_head
     _check(_lib.mtk_attention_bwd(_ptr(qkv), _ptr(o), _ptr(dout), _ptr(lse), _ptr(workspace),
                                   _ptr(dqkv), batch, seq_len, n_heads, n_kv_heads, head_dim,
                                   _stream(stream)), "mtk_attention_bwd")
+
+
+def mtk_attention_bwd_rope(qkv, o, dout, lse, workspace, dqkv, batch, seq_len, n_heads,
+                           n_kv_heads, head_dim, cos_t, sin_t, stream=None):
+    _check(_lib.mtk_attention_bwd_rope(_ptr(qkv), _ptr(o), _ptr(dout), _ptr(lse), _ptr(workspace),
+                                       _ptr(dqkv), batch, seq_len, n_heads, n_kv_heads, head_dim,
+                                       _ptr(cos_t), _ptr(sin_t), _stream(stream)),
+           "mtk_attention_bwd_rope")
 
 
 def mtk_cross_entropy(logits, ld, labels, T, V, grad_scale, n_valid, dlogits, ld_d, loss_rows,

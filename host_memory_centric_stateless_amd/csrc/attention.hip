@@ -16,10 +16,13 @@
 // reduction indices that the A operand (read from a transposed LDS tile with
 // two 8-byte reads) follows exactly, so the sum is unchanged.
 //
-// Backward is two deterministic kernels: dK/dV with the key block outer
-// (loops over every query head of the group and every later query tile, so
-// grouped heads are summed in a fixed order) and dQ with the query block
-// outer.  No floating-point atomics.
+// Backward is deterministic, with no floating-point atomics: D = rowsum(dO*O)
+// per query (attn_dsum_kernel); dV and dK, each its own launch with the key
+// block outer (one workgroup per kv head walking its group's query heads in
+// order, or with grouped heads one per query head writing fp32 shares that
+// attn_gqa_reduce_kernel adds in query-head order); dQ with the query block
+// outer.  Given RoPE tables, dQ and dK leave the kernels rotated back to the
+// pre-rotation q and k in fp32, so each is rounded to bf16 once.
 #include "common.h"
 
 namespace mt {
@@ -148,6 +151,49 @@ __device__ inline bf16x8_t tr_frag(const uint16_t* t, int r0, int d0, int lane) 
   const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(q + 8 * PITCH));
   const u32x2 x = __builtin_bit_cast(u32x2, lo), y = __builtin_bit_cast(u32x2, hi);
   return as_frag(u32x4{x[0], x[1], y[0], y[1]});
+}
+
+// Stores one lane's share of a transposed head row: acc[dd][4 rr + e] is
+// element d = 32 dd + 8 rr + 4 g + e of the row of this lane's query (or
+// key), g = lane / 32.  Values are scaled, then rounded once to bf16.  With
+// RoPE tables the row is a gradient with respect to rotated q or k, and it
+// is rotated back in fp32 first (the transpose of the forward rotation by the
+// angle of position pos): the pair (d, d + D/2) sits in accumulators dd and
+// dd + D/64 of the same lane.
+template <int D>
+__device__ inline void store_head_row(const f32x16_t (&acc)[D / 32], uint16_t* dst, float scale,
+                                      const float* cos_t, const float* sin_t, int pos, int g) {
+  constexpr int DT = D / 32, HD = D / 2;
+  if (cos_t) {
+#pragma unroll
+    for (int dd = 0; dd < DT / 2; ++dd)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int i = dd * 32 + rr * 8 + g * 4;
+        const float4 c4 = *reinterpret_cast<const float4*>(cos_t + (int64_t)pos * HD + i);
+        const float4 s4 = *reinterpret_cast<const float4*>(sin_t + (int64_t)pos * HD + i);
+        const float cs[4] = {c4.x, c4.y, c4.z, c4.w}, sn[4] = {s4.x, s4.y, s4.z, s4.w};
+        float a[4], b[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x = acc[dd][rr * 4 + e] * scale, y = acc[dd + DT / 2][rr * 4 + e] * scale;
+          a[e] = x * cs[e] + y * sn[e];
+          b[e] = y * cs[e] - x * sn[e];
+        }
+        *reinterpret_cast<u32x2*>(dst + i) = u32x2{pack_bf2(a[0], a[1]), pack_bf2(a[2], a[3])};
+        *reinterpret_cast<u32x2*>(dst + i + HD) = u32x2{pack_bf2(b[0], b[1]), pack_bf2(b[2], b[3])};
+      }
+  } else {
+#pragma unroll
+    for (int dd = 0; dd < DT; ++dd)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int d = dd * 32 + rr * 8 + g * 4;
+        *reinterpret_cast<u32x2*>(dst + d) =
+            u32x2{pack_bf2(acc[dd][rr * 4 + 0] * scale, acc[dd][rr * 4 + 1] * scale),
+                  pack_bf2(acc[dd][rr * 4 + 2] * scale, acc[dd][rr * 4 + 3] * scale)};
+      }
+  }
 }
 
 // --------------------------------------------------------------- forward
@@ -316,7 +362,8 @@ template <int D>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
     const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ dsum, uint16_t* __restrict__ dqkv,
-    int seq, int nq, int nkv, int64_t T) {
+    const float* __restrict__ cos_t, const float* __restrict__ sin_t, int seq, int nq, int nkv,
+    int64_t T) {
   constexpr int BKV = 64, KS = D / 16, DT = D / 32;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BKV * PITCH];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BKV * PITCH];
@@ -410,17 +457,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
     }
     __syncthreads();
   }
-  const float scale = 1.0f / sqrtf((float)D);
-  uint16_t* dq = dqkv + (row0 + q) * ld + j * D;
-#pragma unroll
-  for (int dd = 0; dd < DT; ++dd)
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int d = dd * 32 + rr * 8 + g * 4;
-      u32x2 v{pack_bf2(acc[dd][rr * 4 + 0] * scale, acc[dd][rr * 4 + 1] * scale),
-              pack_bf2(acc[dd][rr * 4 + 2] * scale, acc[dd][rr * 4 + 3] * scale)};
-      *reinterpret_cast<u32x2*>(dq + d) = v;
-    }
+  store_head_row<D>(acc, dqkv + (row0 + q) * ld + j * D, 1.0f / sqrtf((float)D), cos_t, sin_t, q,
+                    g);
 }
 
 // ---------------------------------------------------- backward: dK, dV
@@ -437,7 +475,9 @@ __device__ __forceinline__ void dkdv_body(const uint16_t* __restrict__ qkv,
                                           const float* __restrict__ lse,
                                           const float* __restrict__ dsum,
                                           uint16_t* __restrict__ dqkv, float* __restrict__ part,
-                                          int seq, int nq, int nkv, int64_t T) {
+                                          const float* __restrict__ cos_t,
+                                          const float* __restrict__ sin_t, int seq, int nq,
+                                          int nkv, int64_t T) {
   constexpr int BQ = 64, KS = D / 16, DT = D / 32;
   __shared__ __attribute__((aligned(16))) uint16_t Qs[2][BQ * PITCH];
   __shared__ __attribute__((aligned(16))) uint16_t Os[2][BQ * PITCH];  // dO
@@ -580,17 +620,10 @@ __device__ __forceinline__ void dkdv_body(const uint16_t* __restrict__ qkv,
             make_float4(acc[dd][rr * 4 + 0], acc[dd][rr * 4 + 1], acc[dd][rr * 4 + 2],
                         acc[dd][rr * 4 + 3]);
   } else {
-    const float scale = DK ? 1.0f / sqrtf((float)D) : 1.0f;
-    uint16_t* dst = dqkv + (row0 + kv) * ld + (int64_t)(DK ? nq : nq + nkv) * D + kvh * D;
-#pragma unroll
-    for (int dd = 0; dd < DT; ++dd)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int d = dd * 32 + rr * 8 + g * 4;
-        u32x2 v2{pack_bf2(acc[dd][rr * 4 + 0] * scale, acc[dd][rr * 4 + 1] * scale),
-                 pack_bf2(acc[dd][rr * 4 + 2] * scale, acc[dd][rr * 4 + 3] * scale)};
-        *reinterpret_cast<u32x2*>(dst + d) = v2;
-      }
+    // dK is a gradient with respect to rotated keys (rotated back here); dV is not
+    store_head_row<D>(acc, dqkv + (row0 + kv) * ld + (int64_t)(DK ? nq : nq + nkv) * D + kvh * D,
+                      DK ? 1.0f / sqrtf((float)D) : 1.0f, DK ? cos_t : nullptr,
+                      DK ? sin_t : nullptr, kv, g);
   }
 }
 
@@ -598,27 +631,56 @@ __device__ __forceinline__ void dkdv_body(const uint16_t* __restrict__ qkv,
 // query-head order (fixed for any launch), scaled, rounded to bf16 into the
 // column block starting at head col0 of dqkv.  One thread per
 // four consecutive d of one (row, kv head).
+// With RoPE tables (dK) a thread instead takes four d of the first half and
+// their rotation partners d + D/2, and rotates the scaled sums back in fp32
+// before the rounding.
 template <int D>
 __global__ __launch_bounds__(256) void attn_gqa_reduce_kernel(const float* __restrict__ part,
                                                               uint16_t* __restrict__ dqkv,
                                                               int64_t T, int nq, int nkv,
-                                                              int col0, float scale) {
+                                                              int col0, float scale,
+                                                              const float* __restrict__ cos_t,
+                                                              const float* __restrict__ sin_t,
+                                                              int seq) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t per_row = (int64_t)nkv * (D / 4);
+  const int per_head = cos_t ? D / 8 : D / 4;
+  const int64_t per_row = (int64_t)nkv * per_head;
   if (i >= T * per_row) return;
   const int64_t row = i / per_row;
-  const int kvh = (int)((i % per_row) / (D / 4));
-  const int d = (int)(i % (D / 4)) * 4;
+  const int kvh = (int)((i % per_row) / per_head);
+  const int d = (int)(i % per_head) * 4;
   const int grp = nq / nkv;
-  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int g = 0; g < grp; ++g) {
-    const float4 v =
-        *reinterpret_cast<const float4*>(part + ((int64_t)(kvh * grp + g) * T + row) * D + d);
-    a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
-  }
   const int64_t ld = (int64_t)(nq + 2 * nkv) * D;
-  *reinterpret_cast<u32x2*>(dqkv + row * ld + (int64_t)(col0 + kvh) * D + d) =
-      u32x2{pack_bf2(a.x * scale, a.y * scale), pack_bf2(a.z * scale, a.w * scale)};
+  uint16_t* dst = dqkv + row * ld + (int64_t)(col0 + kvh) * D;
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int g = 0; g < grp; ++g) {
+    const float* src = part + ((int64_t)(kvh * grp + g) * T + row) * D;
+    const float4 v = *reinterpret_cast<const float4*>(src + d);
+    a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
+    if (cos_t) {
+      const float4 w = *reinterpret_cast<const float4*>(src + d + D / 2);
+      b.x += w.x; b.y += w.y; b.z += w.z; b.w += w.w;
+    }
+  }
+  if (cos_t) {
+    const int64_t t = (row % seq) * (D / 2) + d;
+    const float4 c = *reinterpret_cast<const float4*>(cos_t + t);
+    const float4 s = *reinterpret_cast<const float4*>(sin_t + t);
+    const float x[4] = {a.x * scale, a.y * scale, a.z * scale, a.w * scale};
+    const float y[4] = {b.x * scale, b.y * scale, b.z * scale, b.w * scale};
+    const float cs[4] = {c.x, c.y, c.z, c.w}, sn[4] = {s.x, s.y, s.z, s.w};
+    float ra[4], rb[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ra[e] = x[e] * cs[e] + y[e] * sn[e];
+      rb[e] = y[e] * cs[e] - x[e] * sn[e];
+    }
+    *reinterpret_cast<u32x2*>(dst + d) = u32x2{pack_bf2(ra[0], ra[1]), pack_bf2(ra[2], ra[3])};
+    *reinterpret_cast<u32x2*>(dst + d + D / 2) = u32x2{pack_bf2(rb[0], rb[1]), pack_bf2(rb[2], rb[3])};
+  } else {
+    *reinterpret_cast<u32x2*>(dst + d) =
+        u32x2{pack_bf2(a.x * scale, a.y * scale), pack_bf2(a.z * scale, a.w * scale)};
+  }
 }
 
 // dK holds both K and V fragments and two score chains: 248 VGPRs, two waves
@@ -633,15 +695,16 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dv_kernel(
     const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ dsum, uint16_t* __restrict__ dqkv,
     float* __restrict__ part, int seq, int nq, int nkv, int64_t T) {
-  dkdv_body<D, false, SPLIT>(qkv, dout, lse, dsum, dqkv, part, seq, nq, nkv, T);
+  dkdv_body<D, false, SPLIT>(qkv, dout, lse, dsum, dqkv, part, nullptr, nullptr, seq, nq, nkv, T);
 }
 
 template <int D, bool SPLIT>
 __global__ __launch_bounds__(256, MT_DK_WAVES_PER_SIMD) void attn_bwd_dk_kernel(
     const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ dsum, uint16_t* __restrict__ dqkv,
-    float* __restrict__ part, int seq, int nq, int nkv, int64_t T) {
-  dkdv_body<D, true, SPLIT>(qkv, dout, lse, dsum, dqkv, part, seq, nq, nkv, T);
+    float* __restrict__ part, const float* __restrict__ cos_t, const float* __restrict__ sin_t,
+    int seq, int nq, int nkv, int64_t T) {
+  dkdv_body<D, true, SPLIT>(qkv, dout, lse, dsum, dqkv, part, cos_t, sin_t, seq, nq, nkv, T);
 }
 
 template <int D>
@@ -658,8 +721,8 @@ hipError_t fwd_d(const uint16_t* qkv, uint16_t* o, float* lse, int batch, int se
 // the group's shares are added by attn_gqa_reduce_kernel.
 template <int D>
 hipError_t bwd_d(const uint16_t* qkv, const uint16_t* o, const uint16_t* dout, const float* lse,
-                 float* dsum, float* part, uint16_t* dqkv, int batch, int seq, int nq, int nkv,
-                 hipStream_t s) {
+                 float* dsum, float* part, uint16_t* dqkv, const float* cos_t, const float* sin_t,
+                 int batch, int seq, int nq, int nkv, hipStream_t s) {
   const int64_t T = (int64_t)batch * seq;
   const int64_t n = T * nq;
   hipLaunchKernelGGL(attn_dsum_kernel<D>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, o,
@@ -668,21 +731,20 @@ hipError_t bwd_d(const uint16_t* qkv, const uint16_t* o, const uint16_t* dout, c
     hipLaunchKernelGGL((attn_bwd_dv_kernel<D, false>), dim3(seq / 128, nkv, batch), dim3(256), 0,
                        s, qkv, dout, lse, dsum, dqkv, nullptr, seq, nq, nkv, T);
     hipLaunchKernelGGL((attn_bwd_dk_kernel<D, false>), dim3(seq / 128, nkv, batch), dim3(256), 0,
-                       s, qkv, dout, lse, dsum, dqkv, nullptr, seq, nq, nkv, T);
+                       s, qkv, dout, lse, dsum, dqkv, nullptr, cos_t, sin_t, seq, nq, nkv, T);
   } else {
-    const int64_t nr = T * nkv * (D / 4);
-    const dim3 rgrid((unsigned)((nr + 255) / 256));
+    const int64_t nv = T * nkv * (D / 4), nk = T * nkv * (cos_t ? D / 8 : D / 4);
     hipLaunchKernelGGL((attn_bwd_dv_kernel<D, true>), dim3(seq / 128, nq, batch), dim3(256), 0, s,
                        qkv, dout, lse, dsum, dqkv, part, seq, nq, nkv, T);
-    hipLaunchKernelGGL(attn_gqa_reduce_kernel<D>, rgrid, dim3(256), 0, s, part, dqkv, T, nq, nkv,
-                       nq + nkv, 1.0f);
+    hipLaunchKernelGGL(attn_gqa_reduce_kernel<D>, dim3((unsigned)((nv + 255) / 256)), dim3(256), 0,
+                       s, part, dqkv, T, nq, nkv, nq + nkv, 1.0f, nullptr, nullptr, seq);
     hipLaunchKernelGGL((attn_bwd_dk_kernel<D, true>), dim3(seq / 128, nq, batch), dim3(256), 0, s,
-                       qkv, dout, lse, dsum, dqkv, part, seq, nq, nkv, T);
-    hipLaunchKernelGGL(attn_gqa_reduce_kernel<D>, rgrid, dim3(256), 0, s, part, dqkv, T, nq, nkv,
-                       nq, 1.0f / sqrtf((float)D));
+                       qkv, dout, lse, dsum, dqkv, part, nullptr, nullptr, seq, nq, nkv, T);
+    hipLaunchKernelGGL(attn_gqa_reduce_kernel<D>, dim3((unsigned)((nk + 255) / 256)), dim3(256), 0,
+                       s, part, dqkv, T, nq, nkv, nq, 1.0f / sqrtf((float)D), cos_t, sin_t, seq);
   }
   hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, dim3(seq / 128, nq, batch), dim3(256), 0, s, qkv,
-                     dout, lse, dsum, dqkv, seq, nq, nkv, T);
+                     dout, lse, dsum, dqkv, cos_t, sin_t, seq, nq, nkv, T);
   return hipGetLastError();
 }
 
@@ -706,12 +768,16 @@ size_t attn_bwd_workspace_bytes(int batch, int seq, int nq, int nkv, int d) {
 
 hipError_t launch_attn_bwd(const uint16_t* qkv, const uint16_t* o, const uint16_t* dout,
                            const float* lse, void* workspace, uint16_t* dqkv, int batch, int seq,
-                           int nq, int nkv, int d, hipStream_t s) {
+                           int nq, int nkv, int d, const float* cos_t, const float* sin_t,
+                           hipStream_t s) {
   float* dsum = static_cast<float*>(workspace);
   float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                          dsum_bytes((int64_t)batch * seq, nq));
-  if (d == 128) return bwd_d<128>(qkv, o, dout, lse, dsum, part, dqkv, batch, seq, nq, nkv, s);
-  if (d == 64) return bwd_d<64>(qkv, o, dout, lse, dsum, part, dqkv, batch, seq, nq, nkv, s);
+  if (!cos_t != !sin_t) return hipErrorInvalidValue;
+  if (d == 128)
+    return bwd_d<128>(qkv, o, dout, lse, dsum, part, dqkv, cos_t, sin_t, batch, seq, nq, nkv, s);
+  if (d == 64)
+    return bwd_d<64>(qkv, o, dout, lse, dsum, part, dqkv, cos_t, sin_t, batch, seq, nq, nkv, s);
   return hipErrorInvalidValue;
 }
 

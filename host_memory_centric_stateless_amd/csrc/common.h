@@ -64,9 +64,12 @@ hipError_t launch_rope(uint16_t* qkv, int64_t T, int seq, int nq, int nkv, int d
 hipError_t launch_attn_fwd(const uint16_t* qkv, uint16_t* o, float* lse, int batch, int seq,
                            int nq, int nkv, int d, hipStream_t s);
 size_t attn_bwd_workspace_bytes(int batch, int seq, int nq, int nkv, int d);
+// cos_t/sin_t (both or neither): RoPE tables [seq, d/2]; dq and dk are then
+// rotated back from the rotated q/k to the pre-rotation ones before rounding.
 hipError_t launch_attn_bwd(const uint16_t* qkv, const uint16_t* o, const uint16_t* dout,
                            const float* lse, void* workspace, uint16_t* dqkv, int batch, int seq,
-                           int nq, int nkv, int d, hipStream_t s);
+                           int nq, int nkv, int d, const float* cos_t, const float* sin_t,
+                           hipStream_t s);
 // out[0] = mean of v[0..n) (one workgroup, fixed order).
 hipError_t launch_mean(const float* v, int64_t n, float* out, hipStream_t s);
 hipError_t launch_cross_entropy(const float* logits, int64_t ld, const int32_t* labels, int64_t T,

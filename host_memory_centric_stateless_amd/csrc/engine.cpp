@@ -365,10 +365,13 @@ struct KScope {
 };
 
 const char* gemm_name(int layout, int epi) {
-  static const char* n[3][6] = {
-      {"gemm_nt_bf16", "gemm_nt_f32", "gemm_nt_resid", "gemm_nt_accum", "gemm_nt_swiglu", "gemm_nt_x"},
-      {"gemm_nn_bf16", "gemm_nn_f32", "gemm_nn_resid", "gemm_nn_accum", "gemm_nn_x", "gemm_nn_swiglu_bwd"},
-      {"gemm_tn_bf16", "gemm_tn_f32", "gemm_tn_resid", "gemm_tn_accum", "gemm_tn_x", "gemm_tn_x"}};
+  static const char* n[3][7] = {
+      {"gemm_nt_bf16", "gemm_nt_f32", "gemm_nt_resid", "gemm_nt_accum", "gemm_nt_swiglu", "gemm_nt_x",
+       "gemm_nt_rope"},
+      {"gemm_nn_bf16", "gemm_nn_f32", "gemm_nn_resid", "gemm_nn_accum", "gemm_nn_x", "gemm_nn_swiglu_bwd",
+       "gemm_nn_x"},
+      {"gemm_tn_bf16", "gemm_tn_f32", "gemm_tn_resid", "gemm_tn_accum", "gemm_tn_x", "gemm_tn_x",
+       "gemm_tn_x"}};
   return n[layout][epi];
 }
 
@@ -376,10 +379,25 @@ hipError_t gemm(mt_ctx* c, hipStream_t s, int layout, int epi, int64_t M, int64_
                 const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, void* C,
                 int64_t ldc, const float* R = nullptr, int64_t ldr = 0, uint16_t* gu = nullptr,
                 int64_t ldgu = 0, int64_t ffn = 0) {
-  mt_gemm_args a{layout, epi, M, N, K, A, lda, B, ldb, C, ldc, R, ldr, gu, ldgu, ffn};
+  mt_gemm_args a{layout, epi, M, N, K, A, lda, B, ldb, C, ldc, R, ldr, gu, ldgu, ffn,
+                 nullptr, nullptr, 0, 0, 0};
   // the SwiGLU product computes both the gate and the up projection
   const double nn = (epi == MT_EPI_SWIGLU) ? 2.0 * N : (double)N;
   KScope k(c, s, gemm_name(layout, epi), 2.0 * M * nn * K, 2.0 * (M * K + nn * K));
+  return launch_gemm(a, s);
+}
+
+// The fused QKV projection: qkv = n1 [Wq; Wk; Wv]^T with RoPE applied to the
+// q and k columns in fp32 in the epilogue, so q and k are rounded to bf16 once.
+hipError_t gemm_qkv_rope(mt_ctx* c, hipStream_t s, int64_t T, const uint16_t* n1,
+                         const uint16_t* Wqkv, uint16_t* qkv) {
+  const Plan& p = c->p;
+  const int64_t h = p.c.hidden;
+  mt_gemm_args a{MT_GEMM_NT, MT_EPI_ROPE, T, p.ldq, h, n1, h, Wqkv, h, qkv, p.ldq,
+                 nullptr, 0, nullptr, 0, 0,
+                 c->wsp<float>(p.ws.cos_t), c->wsp<float>(p.ws.sin_t), p.qd + p.kvd,
+                 p.c.seq_len, p.c.head_dim};
+  KScope k(c, s, "gemm_nt_rope", 2.0 * T * p.ldq * h, 2.0 * (T * h + (double)p.ldq * h));
   return launch_gemm(a, s);
 }
 
@@ -404,17 +422,11 @@ hipError_t block_forward(mt_ctx* c, const uint16_t* W, const Acts& a, float* y) 
   hipStream_t s = c->sc;
   const TensorOff* L = p.layer;
   const double nb_fwd = (double)T * h * 6 + h * 2 + T * 4;   // rmsnorm: x in, bf16 out
-  const double nb_rope = (double)T * (p.qd + p.kvd) * 4;      // q, k read + written
   {
     KScope k(c, s, "rmsnorm_fwd", 0, nb_fwd);
     CK(launch_rmsnorm_fwd(a.x, W + L[T_ATTN_NORM].off, a.n1, a.rstd1, T, (int)h, g.rms_eps, s));
   }
-  CK(gemm(c, s, MT_GEMM_NT, MT_EPI_BF16, T, p.ldq, h, a.n1, h, W + L[T_WQ].off, h, a.qkv, p.ldq));
-  {
-    KScope k(c, s, "rope", 0, nb_rope);
-    CK(launch_rope(a.qkv, T, g.seq_len, g.n_heads, g.n_kv_heads, g.head_dim,
-                   c->wsp<float>(p.ws.cos_t), c->wsp<float>(p.ws.sin_t), 0, s));
-  }
+  CK(gemm_qkv_rope(c, s, T, a.n1, W + L[T_WQ].off, a.qkv));
   {
     KScope k(c, s, "attn_fwd", 4.0 * g.head_dim * attn_pairs(g), 0);
     CK(launch_attn_fwd(a.qkv, a.o, a.lse, (int)(T / g.seq_len), g.seq_len, g.n_heads, g.n_kv_heads,
@@ -476,13 +488,10 @@ hipError_t block_backward(mt_ctx* c, const uint16_t* W, const Acts& a, const flo
   CK(gemm(c, s, MT_GEMM_TN, wepi, h, p.qd, T, dh1b, h, a.o, p.qd, slab(T_WO), p.qd));
   {
     KScope k(c, s, "attn_bwd", 10.0 * g.head_dim * attn_pairs(g), 0);
+    // dq and dk come out rotated back to the pre-RoPE q and k (inverse RoPE fused)
     CK(launch_attn_bwd(a.qkv, a.o, dout, a.lse, c->wsp<char>(p.ws.dsum), dqkv, (int)(T / g.seq_len),
-                       g.seq_len, g.n_heads, g.n_kv_heads, g.head_dim, s));
-  }
-  {
-    KScope k(c, s, "rope", 0, (double)T * (p.qd + p.kvd) * 4);
-    CK(launch_rope(dqkv, T, g.seq_len, g.n_heads, g.n_kv_heads, g.head_dim,
-                   c->wsp<float>(p.ws.cos_t), c->wsp<float>(p.ws.sin_t), 1, s));
+                       g.seq_len, g.n_heads, g.n_kv_heads, g.head_dim, c->wsp<float>(p.ws.cos_t),
+                       c->wsp<float>(p.ws.sin_t), s));
   }
   CK(gemm(c, s, MT_GEMM_TN, wepi, p.ldq, h, T, dqkv, p.ldq, a.n1, h, slab(T_WQ), h));
   CK(gemm(c, s, MT_GEMM_NN, MT_EPI_F32, T, h, p.ldq, dqkv, p.ldq, W + L[T_WQ].off, h, dn, h));

@@ -51,6 +51,25 @@ struct RowMap {
   }
 };
 
+// B rows of the RoPE product (the fused QKV projection).  Inside every head
+// of d rows the tile's local row l = 16 g + w (w < 16) holds head row
+// 8 g + w for w < 8 and d/2 + 8 g + w - 8 otherwise.  The epilogue gives a
+// lane 16 consecutive local columns, so it then holds eight whole rotation
+// pairs (i, i + d/2), i = 8 g .. 8 g + 7, and rotates them in fp32 before the
+// single bf16 rounding.  Heads never straddle a tile (tiles are 128 or 256
+// columns wide, d divides 128).
+struct RopeRowMap {
+  int64_t row0, nrows;
+  int d;
+  __device__ inline int64_t map(int r, bool& ok) const {
+    const int l = r % d, g = l >> 4, w = l & 15;
+    const int hr = (w < 8) ? 8 * g + w : (d >> 1) + 8 * g + (w - 8);
+    const int64_t gr = row0 + (r - l) + hr;
+    ok = gr < nrows;
+    return ok ? gr : nrows - 1;
+  }
+};
+
 // Operand loads are raw buffer loads.  Each thread's byte offsets from the
 // tile's first row (or k-row) are fixed for the whole K loop, so a load is a
 // wave-uniform resource, rebuilt per tile in scalar registers, plus one
@@ -294,6 +313,34 @@ __device__ __forceinline__ void store_tile(const mt_gemm_args& p,
             if (in[h])
               *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.C) + row * p.ldc + c0 + 8 * h) =
                   pack8(v + 8 * h);
+        } else if constexpr (EPI == MT_EPI_ROPE) {
+          // v[0..7] and v[8..15] are head columns i0.. and d/2 + i0.. (RopeRowMap);
+          // N is a multiple of d, so the 16 columns are all inside or all outside
+          if (!in[0]) continue;
+          const int hd = p.rope_dim >> 1;
+          const int64_t l = c0 % p.rope_dim;
+          const int i0 = (int)(l >> 1);
+          uint16_t* C = static_cast<uint16_t*>(p.C) + row * p.ldc + (c0 - l) + i0;
+          if (c0 < p.rope_cols) {
+            const int64_t t = (int64_t)(row % p.rope_seq) * hd + i0;
+            const float4 c4[2] = {*reinterpret_cast<const float4*>(p.rope_cos + t),
+                                  *reinterpret_cast<const float4*>(p.rope_cos + t + 4)};
+            const float4 s4[2] = {*reinterpret_cast<const float4*>(p.rope_sin + t),
+                                  *reinterpret_cast<const float4*>(p.rope_sin + t + 4)};
+            const float cs[8] = {c4[0].x, c4[0].y, c4[0].z, c4[0].w, c4[1].x, c4[1].y, c4[1].z, c4[1].w};
+            const float sn[8] = {s4[0].x, s4[0].y, s4[0].z, s4[0].w, s4[1].x, s4[1].y, s4[1].z, s4[1].w};
+            float a[8], b[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              a[e] = v[e] * cs[e] - v[8 + e] * sn[e];
+              b[e] = v[8 + e] * cs[e] + v[e] * sn[e];
+            }
+            *reinterpret_cast<u32x4*>(C) = pack8(a);
+            *reinterpret_cast<u32x4*>(C + hd) = pack8(b);
+          } else {
+            *reinterpret_cast<u32x4*>(C) = pack8(v);
+            *reinterpret_cast<u32x4*>(C + hd) = pack8(v + 8);
+          }
         } else if constexpr (EPI == MT_EPI_SWIGLU_BWD) {
           u32x4 ga[2], gu_[2];
 #pragma unroll
@@ -379,6 +426,7 @@ __global__ __launch_bounds__(64 * WVM * WVN) void gemm_kernel(mt_gemm_args p, in
   if constexpr (A_T) la.init(p.lda, m0, p.M, tid);
   else la.init(p.lda, ra, tid);
   if constexpr (B_T) lb.init(p.ldb, n0, p.N, tid);
+  else if constexpr (EPI == MT_EPI_ROPE) lb.init(p.ldb, RopeRowMap{n0, p.N, p.rope_dim}, tid);
   else lb.init(p.ldb, rb, tid);
   // bytes from each operand's start to the end of its last row
   const int64_t ext_a = A_T ? ((K - 1) * p.lda + p.M) * 2 : ((p.M - 1) * p.lda + K) * 2;
@@ -647,6 +695,7 @@ __global__ __launch_bounds__(512) void gemm_direct_kernel(mt_gemm_args p, int nm
   if constexpr (A_T) la.init(p.lda, m0, wave, lane);
   else la.init(p.lda, ra, wave, lane);
   if constexpr (B_T) lb.init(p.ldb, n0, wave, lane);
+  else if constexpr (EPI == MT_EPI_ROPE) lb.init(p.ldb, RopeRowMap{n0, p.N, p.rope_dim}, wave, lane);
   else lb.init(p.ldb, rb, wave, lane);
   const int64_t ext_a = A_T ? ((K - 1) * p.lda + p.M) * 2 : ((p.M - 1) * p.lda + K) * 2;
   const int64_t ext_b = B_T ? ((K - 1) * p.ldb + p.N) * 2
@@ -792,7 +841,7 @@ hipError_t launch_one(const mt_gemm_args& a, hipStream_t s) {
 bool gemm_shape_ok(const mt_gemm_args& a, const char** why) {
   auto bad = [&](const char* w) { if (why) *why = w; return false; };
   if (a.layout < 0 || a.layout > 2) return bad("layout");
-  if (a.epilogue < 0 || a.epilogue > 5) return bad("epilogue");
+  if (a.epilogue < 0 || a.epilogue > 6) return bad("epilogue");
   if (a.M <= 0 || a.N <= 0 || a.K <= 0) return bad("empty or negative dimension");
   if (a.M % 8 || a.N % 8 || a.K % 8) return bad("M, N, K must be multiples of 8");
   if ((a.M / 128 + 1) * (a.N / 64 + 1) >= (1LL << 31)) return bad("too many tiles");
@@ -812,6 +861,14 @@ bool gemm_shape_ok(const mt_gemm_args& a, const char** why) {
   } else {
     if (a.ldc < a.N) return bad("ldc");
     if (a.epilogue == MT_EPI_F32_RESID && (!a.R || a.ldr < a.N)) return bad("residual");
+    if (a.epilogue == MT_EPI_ROPE) {
+      if (a.layout != MT_GEMM_NT) return bad("ROPE needs the NT layout");
+      const int d = a.rope_dim;
+      if (!(d == 16 || d == 32 || d == 64 || d == 128)) return bad("rope_dim");
+      if (!a.rope_cos || !a.rope_sin || a.rope_seq < 1) return bad("rope tables");
+      if ((((uintptr_t)a.rope_cos | (uintptr_t)a.rope_sin) & 15)) return bad("rope table alignment");
+      if (a.N % d || a.rope_cols % d || a.rope_cols < 0 || a.rope_cols > a.N) return bad("rope_cols");
+    }
   }
   return true;
 }
@@ -824,6 +881,7 @@ hipError_t launch_gemm(const mt_gemm_args& a, hipStream_t s) {
   MT_GEMM_CASE(MT_GEMM_NT, MT_EPI_F32_RESID)
   MT_GEMM_CASE(MT_GEMM_NT, MT_EPI_F32_ACCUM)
   MT_GEMM_CASE(MT_GEMM_NT, MT_EPI_SWIGLU)
+  MT_GEMM_CASE(MT_GEMM_NT, MT_EPI_ROPE)
   MT_GEMM_CASE(MT_GEMM_NN, MT_EPI_BF16)
   MT_GEMM_CASE(MT_GEMM_NN, MT_EPI_F32)
   MT_GEMM_CASE(MT_GEMM_NN, MT_EPI_F32_RESID)

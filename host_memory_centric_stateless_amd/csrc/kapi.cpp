@@ -74,7 +74,21 @@ extern "C" mt_status mtk_attention_bwd(const uint16_t* qkv, const uint16_t* o,
       !attn_ok(batch, seq_len, n_heads, n_kv_heads, head_dim))
     return MT_E_ARG;
   return hip_status(launch_attn_bwd(qkv, o, dout, lse, workspace, dqkv, batch, seq_len, n_heads,
-                                    n_kv_heads, head_dim, (hipStream_t)stream));
+                                    n_kv_heads, head_dim, nullptr, nullptr, (hipStream_t)stream));
+}
+
+extern "C" mt_status mtk_attention_bwd_rope(const uint16_t* qkv, const uint16_t* o,
+                                            const uint16_t* dout, const float* lse,
+                                            void* workspace, uint16_t* dqkv, int32_t batch,
+                                            int32_t seq_len, int32_t n_heads, int32_t n_kv_heads,
+                                            int32_t head_dim, const float* cos_t,
+                                            const float* sin_t, void* stream) {
+  if (!qkv || !o || !dout || !lse || !workspace || !dqkv || !cos_t || !sin_t ||
+      (((uintptr_t)cos_t | (uintptr_t)sin_t) & 15) ||
+      !attn_ok(batch, seq_len, n_heads, n_kv_heads, head_dim))
+    return MT_E_ARG;
+  return hip_status(launch_attn_bwd(qkv, o, dout, lse, workspace, dqkv, batch, seq_len, n_heads,
+                                    n_kv_heads, head_dim, cos_t, sin_t, (hipStream_t)stream));
 }
 
 extern "C" mt_status mtk_cross_entropy(const float* logits, int64_t ld, const int32_t* labels,

@@ -39,9 +39,17 @@ enum { MT_GEMM_NT = 0, MT_GEMM_NN = 1, MT_GEMM_TN = 2 };
  *              C (bf16) [m, f] = silu(a) * u, a = gate acc, u = up acc.
  *   SWIGLU_BWD NN only.  acc = dm[m, f], N = ffn; reads a, u from gu;
  *              C (bf16) [m, f] = dm*u*s*(1+a*(1-s)),  C[m, ffn+f] = dm*a*s,
- *              s = sigmoid(a). */
+ *              s = sigmoid(a).
+ *   ROPE       NT only, the fused QKV projection.  C (bf16) = acc, except that
+ *              in the columns below rope_cols every head of rope_dim columns
+ *              is rotated in fp32 before its single bf16 rounding: the pair
+ *              (a, b) = (c0 + i, c0 + i + rope_dim/2) becomes
+ *              (a cos - b sin, b cos + a sin), cos/sin = rope_cos/rope_sin
+ *              [pos * rope_dim/2 + i], pos = m mod rope_seq (rotate-half RoPE
+ *              with a host-made fp32 table).  Requires rope_dim in {16, 32,
+ *              64, 128} and N, rope_cols multiples of rope_dim. */
 enum { MT_EPI_BF16 = 0, MT_EPI_F32 = 1, MT_EPI_F32_RESID = 2, MT_EPI_F32_ACCUM = 3,
-       MT_EPI_SWIGLU = 4, MT_EPI_SWIGLU_BWD = 5 };
+       MT_EPI_SWIGLU = 4, MT_EPI_SWIGLU_BWD = 5, MT_EPI_ROPE = 6 };
 
 /* Requirements (MT_E_ARG otherwise): M, N, K, lda, ldb, ldc, ldgu multiples of
  * 8, ldr a multiple of 4; C, R and gu 16-byte aligned (the epilogue moves
@@ -55,6 +63,10 @@ typedef struct mt_gemm_args {
   const float* R; int64_t ldr;
   uint16_t* gu; int64_t ldgu;
   int64_t ffn;
+  const float* rope_cos;    /* ROPE only: fp32 [rope_seq, rope_dim/2] tables      */
+  const float* rope_sin;
+  int64_t rope_cols;        /* ROPE only: columns [0, rope_cols) are rotated      */
+  int32_t rope_seq, rope_dim;
 } mt_gemm_args;
 
 mt_status mtk_gemm(const mt_gemm_args* args, void* stream);
@@ -104,6 +116,19 @@ mt_status mtk_attention_bwd(const uint16_t* qkv, const uint16_t* o, const uint16
                             const float* lse, void* workspace, uint16_t* dqkv, int32_t batch,
                             int32_t seq_len, int32_t n_heads, int32_t n_kv_heads,
                             int32_t head_dim, void* stream);
+
+/* mtk_attention_bwd for q and k that were rotated by RoPE after the
+ * projection (the MT_EPI_ROPE product): qkv holds the rotated q and k, and dq
+ * and dk are written as gradients with respect to the pre-rotation q and k,
+ * i.e. rotated back by -angle in fp32 before their single bf16 rounding.
+ * cos_t/sin_t: the fp32 [seq_len, head_dim/2] tables the forward used,
+ * 16-byte aligned.  The backward of RoPE is the transpose of a rotation (the
+ * oracle's RoPE reading: rotate-half pairs, angles from a float64 table). */
+mt_status mtk_attention_bwd_rope(const uint16_t* qkv, const uint16_t* o, const uint16_t* dout,
+                                 const float* lse, void* workspace, uint16_t* dqkv, int32_t batch,
+                                 int32_t seq_len, int32_t n_heads, int32_t n_kv_heads,
+                                 int32_t head_dim, const float* cos_t, const float* sin_t,
+                                 void* stream);
 
 /* Cross-entropy over fp32 logits [T, V] (row stride ld): loss_rows[t] =
  * lse_t - logits[t, label_t] (0 for label < 0); dlogits bf16 [T, V] (row stride

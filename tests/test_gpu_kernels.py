@@ -143,6 +143,33 @@ def test_rope_forward_inverse(b, s, nq, nkv, d):
     assert rel_max(back, xb) < 2e-2
 
 
+# (T, seq, nq, nkv, d, K): the fused QKV projection with RoPE in the epilogue.
+# The first two run on 128 x 128 tiles, the others on 256 x 256 direct-to-LDS
+# tiles (the last with a ragged row tail and T not a multiple of the sequence).
+@pytest.mark.parametrize("T,s,nq,nkv,d,K", [(256, 128, 4, 2, 64, 256), (384, 384, 10, 2, 128, 392),
+                                            (4096, 2048, 8, 8, 128, 256),
+                                            (4104, 1024, 16, 4, 64, 384)])
+def test_gemm_rope_epilogue(T, s, nq, nkv, d, K):
+    print(f"gemm rope T={T} s={s} nq={nq} nkv={nkv} d={d} K={K}", flush=True)
+    N = (nq + 2 * nkv) * d
+    A = random_array((T, K), seed=21)
+    B = random_array((N, K), seed=22, std=0.05)
+    cos, sin = mt.mt_host_rope_table(s, d, 10000.0)
+    out = torch.empty((T, N), dtype=torch.bfloat16, device=dev())
+    mt.mtk_gemm(mt.MT_GEMM_NT, mt.MT_EPI_ROPE, T, N, K, bf16_dev(A), K, bf16_dev(B), K, out, N,
+                rope_cos=f32_dev(cos), rope_sin=f32_dev(sin), rope_cols=(nq + nkv) * d,
+                rope_seq=s, rope_dim=d)
+    y = bf16_round(A) @ bf16_round(B).T          # the projection, float64
+    pos = np.arange(T) % s
+    ref = y.copy()
+    qk = y[:, :(nq + nkv) * d].reshape(1, T, nq + nkv, d)
+    ref[:, :(nq + nkv) * d] = OM.rope(qk, cos[pos].astype(np.float64),
+                                      sin[pos].astype(np.float64)).reshape(T, -1)
+    got = host(out)
+    # one rounding of the fp32 result (the rotation adds fp32 error only)
+    assert np.all(np.abs(got - ref) <= BF16_REL * np.abs(ref) + 3e-5 * np.max(np.abs(ref)))
+
+
 ATTN_CASES = [(2, 256, 4, 2, 64), (1, 384, 4, 4, 128), (1, 256, 10, 2, 128), (2, 128, 16, 16, 64)]
 
 
@@ -185,6 +212,33 @@ def test_attention_backward(b, s, nq, nkv, d):
                      device=dev())
     mt.mtk_attention_bwd(qd, o, bf16_dev(dO), lse, ws, dq, b, s, nq, nkv, d)
     rq, rk, rv = OM.attention_bwd(q, k, v, bf16_round(dO).reshape(b, s, nq, d))
+    got = host(dq)
+    assert rel_max(got[:, :nq * d], rq.reshape(T, -1)) < 2e-2
+    assert rel_max(got[:, nq * d:(nq + nkv) * d], rk.reshape(T, -1)) < 2e-2
+    assert rel_max(got[:, (nq + nkv) * d:], rv.reshape(T, -1)) < 2e-2
+
+
+@pytest.mark.parametrize("b,s,nq,nkv,d", ATTN_CASES)
+def test_attention_backward_rope(b, s, nq, nkv, d):
+    """dq and dk leave the kernels rotated back to the pre-RoPE q and k."""
+    print(f"attn bwd rope b={b} s={s} nq={nq} nkv={nkv} d={d}", flush=True)
+    T = b * s
+    qkv, q, k, v = _attn_inputs(b, s, nq, nkv, d, 24)
+    dO = random_array((T, nq * d), seed=25)
+    qd = bf16_dev(qkv)
+    o = torch.empty((T, nq * d), dtype=torch.bfloat16, device=dev())
+    lse = torch.empty((nq, T), dtype=torch.float32, device=dev())
+    mt.mtk_attention_fwd(qd, o, lse, b, s, nq, nkv, d)
+    cos, sin = mt.mt_host_rope_table(s, d, 10000.0)
+    dq = torch.zeros((T, (nq + 2 * nkv) * d), dtype=torch.bfloat16, device=dev())
+    ws = torch.empty(mt.mtk_attention_bwd_workspace(b, s, nq, nkv, d), dtype=torch.uint8,
+                     device=dev())
+    mt.mtk_attention_bwd_rope(qd, o, bf16_dev(dO), lse, ws, dq, b, s, nq, nkv, d, f32_dev(cos),
+                              f32_dev(sin))
+    rq, rk, rv = OM.attention_bwd(q, k, v, bf16_round(dO).reshape(b, s, nq, d))
+    c64, s64 = cos.astype(np.float64), sin.astype(np.float64)
+    rq = OM.rope(rq, c64, s64, inverse=True)
+    rk = OM.rope(rk, c64, s64, inverse=True)
     got = host(dq)
     assert rel_max(got[:, :nq * d], rq.reshape(T, -1)) < 2e-2
     assert rel_max(got[:, nq * d:(nq + nkv) * d], rk.reshape(T, -1)) < 2e-2
