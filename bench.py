@@ -232,12 +232,40 @@ def cpu_baseline(cfg, budget_s: float = 30.0):
     dt = time.perf_counter() - t0
     per_layer_model = (model_flops_per_token(cfg.replace(n_layers=1, vocab=0)))
     tflops = per_layer_model * T / dt / 1e12
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    blas = _blas_info()
     tok_s = tflops * 1e12 / model_flops_per_token(full)
-    return {"value": tflops, "unit": "model TFLOP/s", "cores": threads, "kind": "oracle",
+    return {"value": tflops, "unit": "model TFLOP/s", "cores": blas["threads"], "kind": "oracle",
+            "cpu_model": _cpu_model(), "blas": blas["library"], "blas_threads": blas["threads"],
+            "logical_cpus": os.cpu_count(),
             "sample": f"1 decoder layer of {full.name} (hidden {cfg.hidden}) forward + recompute + "
                       f"backward on {cfg.micro_batch} x {cfg.seq_len} tokens, fp32 NumPy, {dt:.1f} s; "
                       f"tokens/s equivalent for the whole model {tok_s:.1f}"}
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _blas_info() -> dict:
+    """The BLAS numpy calls and the size of its thread pool, as loaded in this
+    process (the pool the oracle's matrix products actually ran on)."""
+    try:
+        import threadpoolctl
+        for p in threadpoolctl.threadpool_info():
+            if p.get("user_api") == "blas":
+                return {"library": f"{p.get('internal_api')} {p.get('version')} "
+                                   f"({p.get('threading_layer')}, {p.get('architecture')})",
+                        "threads": int(p.get("num_threads"))}
+    except Exception:
+        pass
+    return {"library": "unknown", "threads": int(os.environ.get("OMP_NUM_THREADS", 1))}
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_tn_bf16_7b_shape_traffic.txt")
@@ -324,6 +352,8 @@ def main():
     ap.add_argument("--host-mem-gib", type=float, default=0.0,
                     help="host memory the run may use (default: MemAvailable); the run stops "
                          "before allocating if the host state and pinned buffers exceed it")
+    ap.add_argument("--no-fp32-slabs", action="store_true",
+                    help="skip the second measurement of the headline step with fp32 slabs")
     ap.add_argument("--probe", action="store_true",
                     help="only run each block GEMM at this shape and a calibration copy")
     args = ap.parse_args()
@@ -467,6 +497,7 @@ def main():
         lel = time.perf_counter() - t_start
         l1 = lm.stats()
         lm.close()
+        step_no += args.steps
         ltok = tokens_per_step * args.steps / lel
         layer_major = {
             "micro_batches_per_pass": cfg.grad_accum, "ms_per_step": 1e3 * lel / args.steps,
@@ -481,6 +512,44 @@ def main():
                     "weight residency"}
         print(f"[bench] layer-major pass: {layer_major['ms_per_step']:.0f} ms/step, "
               f"{ltok:.0f} tokens/s", file=sys.stderr, flush=True)
+    # The headline step again with fp32 gradient slabs (the plain reading of
+    # the pages: fp32 gradients to the host) instead of the default bf16 slabs.
+    fp32_slabs = None
+    if not args.no_fp32_slabs:
+        t0 = time.perf_counter()
+        fs = Session(cfg, host_threads=args.host_threads, drain_workgroups=args.drain_workgroups,
+                     micro_batches_per_pass=args.micro_batches_per_pass, slab_bf16=False,
+                     host_from=sess)
+        fs.bind()
+        print(f"[bench] fp32 slabs: init {time.perf_counter() - t0:.1f} s", file=sys.stderr,
+              flush=True)
+        for w in range(args.warmup):
+            tok, lab = make_batch(cfg, step_no)
+            fs.step(tok, lab, step_no)
+            step_no += 1
+        fb = [make_batch(cfg, step_no + k) for k in range(args.steps)]
+        f0 = fs.stats()
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for k in range(args.steps):
+            tok, lab = fb[k]
+            fs.step(tok, lab, step_no + k, flush=False)
+        fs.flush()
+        torch.cuda.synchronize()
+        fel = time.perf_counter() - t_start
+        f1 = fs.stats()
+        fs.close()
+        step_no += args.steps
+        ftok = tokens_per_step * args.steps / fel
+        fp32_slabs = {
+            "ms_per_step": 1e3 * fel / args.steps, "tokens_per_s": ftok,
+            "model_tflops": model_flops_per_token(cfg) * ftok / 1e12,
+            "d2h_GBps": (f1["d2h_bytes"] - f0["d2h_bytes"]) / fel / 1e9,
+            "h2d_GBps": (f1["h2d_bytes"] - f0["h2d_bytes"]) / fel / 1e9,
+            "note": "headline step with fp32 gradient slabs (4 bytes per gradient element "
+                    "device -> host instead of 2)"}
+        print(f"[bench] fp32 slabs: {fp32_slabs['ms_per_step']:.0f} ms/step", file=sys.stderr,
+              flush=True)
     base = None if args.no_cpu_baseline else cpu_baseline(cfg)
 
     out = {
@@ -516,6 +585,7 @@ def main():
         "roofline": roofline, "kernels": kernels,
         "isolated_swiglu_gemm": {"TFLOPs": gemm["tflops"], "ms": gemm["ms"], "shape_MNK": gemm["shape"]},
         "layer_major": layer_major,
+        "fp32_slabs": fp32_slabs,
         "cpu_baseline": base,
     }
     print(json.dumps(out))

@@ -126,6 +126,7 @@ _SIGS = {
     "mt_backward_step": ([_P, _I32, C.POINTER(mt_adamw_hparams), _I64], C.c_int),
     "mt_flush_grads": ([_P], C.c_int),
     "mt_sync_loss": ([_P], C.c_int),
+    "mt_step_loss": ([_P, C.POINTER(C.c_float)], C.c_int),
     "mt_adamw_step": ([_P, C.POINTER(mt_adamw_hparams), _I64], C.c_int),
     "mt_get_stats": ([_P, C.POINTER(mt_stats)], C.c_int),
     "mt_last_error": ([_P], C.c_char_p),
@@ -249,6 +250,12 @@ def mt_flush_grads(ctx):
 
 def mt_sync_loss(ctx):
     _check(_lib.mt_sync_loss(ctx), "mt_sync_loss", ctx)
+
+
+def mt_step_loss(ctx) -> float:
+    out = C.c_float()
+    _check(_lib.mt_step_loss(ctx, C.byref(out)), "mt_step_loss", ctx)
+    return out.value
 
 
 def mt_adamw_step(ctx, hp: mt_adamw_hparams, step: int):

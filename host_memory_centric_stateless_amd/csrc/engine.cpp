@@ -262,6 +262,9 @@ struct mt_ctx {
   std::atomic<bool> poisoned{false};
   std::vector<std::pair<float*, int>> pending_loss;
   int loss_next = 0;
+  // loss ring slots of the passes of the open optimizer step, and of the last
+  // completed one (mt_step_loss)
+  std::vector<int> step_slots, last_step_slots;
   mt_stats st{};
 
   void set_err(const char* fmt, ...) {
@@ -1223,6 +1226,7 @@ extern "C" mt_status mt_forward(mt_ctx* c, const int32_t* tokens, const int32_t*
   MT_HIP(c, hipMemcpyAsync(c->loss_pin + slot, c->ws + p.ws.loss, 4, hipMemcpyDeviceToHost, c->sc));
   MT_HIP(c, hipEventRecord(c->ev_loss, c->sc));
   if (loss_out) c->pending_loss.emplace_back(loss_out, slot);
+  c->step_slots.push_back(slot);
   c->state = ST_FWD;
   return MT_OK;
 }
@@ -1252,7 +1256,11 @@ static mt_status backward_impl(mt_ctx* c, int32_t accumulate_flag, const mt_adam
   r = run_until(c, c->steps.size(), nullptr, 0.0f);
   c->fused = false;
   if (r != MT_OK) return r;
-  if (hp) c->buf_unit[0] = c->buf_unit[1] = -1;  // working copies are being rewritten
+  if (hp) {
+    c->buf_unit[0] = c->buf_unit[1] = -1;  // working copies are being rewritten
+    c->last_step_slots.swap(c->step_slots);
+    c->step_slots.clear();
+  }
   c->mb += 1;
   c->st.microbatches += 1;
   c->state = hp ? ST_IDLE : ST_BWD;
@@ -1299,6 +1307,20 @@ extern "C" mt_status mt_sync_loss(mt_ctx* c) {
   return MT_OK;
 }
 
+extern "C" mt_status mt_step_loss(mt_ctx* c, float* loss_out) {
+  mt_status r = check_live(c);
+  if (r != MT_OK) return r;
+  if (!loss_out) return MT_E_ARG;
+  const std::vector<int>& sl = c->step_slots.empty() ? c->last_step_slots : c->step_slots;
+  if (sl.empty()) return MT_E_STATE;
+  // every loss copy is on the compute stream, so the last one's event covers them all
+  MT_HIP(c, hipEventSynchronize(c->ev_loss));
+  double sum = 0.0;
+  for (int s : sl) sum += (double)c->loss_pin[s];
+  *loss_out = (float)(sum / (double)sl.size());
+  return MT_OK;
+}
+
 extern "C" mt_status mt_adamw_step(mt_ctx* c, const mt_adamw_hparams* hp, int64_t step) {
   mt_status r = check_live(c);
   if (r != MT_OK) return r;
@@ -1311,6 +1333,8 @@ extern "C" mt_status mt_adamw_step(mt_ctx* c, const mt_adamw_hparams* hp, int64_
   adamw(*c->pool, c->head.master, c->head.grad, c->head.m, c->head.v, c->head.pinned, c->head.n,
         *hp, step);
   c->buf_unit[0] = c->buf_unit[1] = -1;  // working copies changed
+  c->last_step_slots.swap(c->step_slots);
+  c->step_slots.clear();
   c->st.adamw_s += now_s() - t0;
   c->state = ST_IDLE;
   return MT_OK;

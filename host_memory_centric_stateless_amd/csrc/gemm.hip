@@ -4,14 +4,19 @@
 // (the block's dedicated forward/backward replaces an autograd graph:
 // zhichai.net "MegaTrain：单卡训百亿大模型的突破与实践", design point 4).
 //
-// Tiling: 256x256 (large products) or 128x128 output tile per 256-thread
-// workgroup, 4 waves as 2x2 each owning a quadrant of 32x32
-// v_mfma_f32_32x32x16_bf16 tiles, K step 64, LDS double buffered.  LDS holds both operands as [row][k] (k contiguous, row stride 72
-// elements so 16-byte fragment reads are conflict-free).  Operands whose
-// reduction dimension is the slow one in memory (the transposed layouts of
-// the input- and weight-gradient products) are transposed in registers on the
-// way into LDS: each thread reads an 8(k) x 4(row) block with 8-byte loads and
-// writes four 16-byte rows.
+// Two kernels share one epilogue (store_tile):
+//   * gemm_direct_kernel: 256x256 output tiles, 8 waves of 128x64 (two waves
+//     per SIMD), K step 64 in two LDS stages.  Operand tiles go from global
+//     memory straight into LDS with buffer_load ... lds into unpadded,
+//     XOR-swizzled tiles; [k][row] operands (the transposed layouts of the
+//     gradient products) are read as MFMA fragments with ds_read_b64_tr_b16.
+//     Used for every product large enough to fill the chip whose K is a
+//     multiple of 128.
+//   * gemm_kernel: the same tiling staged through registers (128x128 tiles of
+//     4 waves for small products, or 256x256 when K has a tail).
+// v_mfma_f32_32x32x16_bf16 throughout; blockIdx -> tile is XCD-aware so that
+// neighbouring tiles share an L2.  Epilogues: bf16 / fp32 stores, residual
+// add, fp32 accumulate, SwiGLU forward and backward, and the fused QKV RoPE.
 #include "common.h"
 
 namespace mt {

@@ -15,7 +15,7 @@ import torch
 from . import (DEFAULT_DRAIN_WORKGROUPS, MT_GROUP_EMBED, MT_GROUP_HEAD, make_config, mt_adamw_hparams, mt_adamw_step,
                mt_backward, mt_backward_step, mt_bind_layer, mt_create, mt_destroy, mt_device_arena,
                mt_device_requirements, mt_flush_grads, mt_forward, mt_get_stats, mt_layout,
-               mt_sync_loss)
+               mt_step_loss, mt_sync_loss)
 
 
 def aligned_zeros(n: int, align: int = 64) -> np.ndarray:
@@ -124,8 +124,9 @@ class Session:
                 mt_forward(self.ctx, tok[k], lab[k], 1.0 / acc, out)
                 mt_backward(self.ctx, 1 if k > 0 else 0)
             mt_flush_grads(self.ctx)
+            loss = mt_step_loss(self.ctx)
         self._losses = losses  # keep the output buffer alive until flush wrote it
-        return float(losses.mean())
+        return loss
 
     def _passes(self, tokens: np.ndarray, labels: np.ndarray):
         """[acc, b, s] micro-batches -> passes of mb_per_pass micro-batches,
@@ -164,8 +165,9 @@ class Session:
                 mt_flush_grads(self.ctx)
             else:
                 mt_sync_loss(self.ctx)
+            loss = mt_step_loss(self.ctx)
         self._losses = losses
-        return float(losses.mean())
+        return loss
 
     def flush(self) -> None:
         """Wait for every gradient drain, host accumulation and update."""

@@ -167,18 +167,28 @@ typedef struct mt_ctx mt_ctx;
 mt_status mt_layout(const mt_config* cfg, int32_t group, mt_tensor_desc* out, int32_t cap,
                     int32_t* n_out, int64_t* flat_numel);
 
-/* Memory needed for cfg (pure, no GPU).  MT_E_ARG for an unsupported config. */
+/* Memory needed for cfg (pure, no GPU): the device holds only the two layer
+ * buffers, one checkpoint window of activations, the checkpoints and the slab
+ * pool, so device memory does not grow with depth (zhichai design point 2:
+ * only the current layer's parameters and gradients on the GPU; lqnn 三.4:
+ * one checkpoint window, "1-2 layers of weights plus a few activations").
+ * MT_E_ARG for an unsupported config. */
 mt_status mt_device_requirements(const mt_config* cfg, mt_device_req* out);
 
-/* Create a context on the current HIP device.  The arena must satisfy
+/* Create a context on the current HIP device (lqnn 三.1-三.3: one GPU context
+ * with its two flat layer buffers, three streams and the gradient slab pool;
+ * the slabs' CPU worker thread starts here).  The arena must satisfy
  * mt_device_requirements(cfg) (MT_E_NOMEM if a region is smaller); it is
  * borrowed, not freed, by the library.  Allocates pinned host slabs and
  * staging buffers, events and the worker threads.  The library allocates no
  * device memory. */
 mt_status mt_create(const mt_config* cfg, const mt_device_arena* arena, mt_ctx** out);
 
-/* Bind the host state of one group: fp32 master, grad, adam_m, adam_v flat
- * arrays of exactly mt_layout's flat_numel elements (64-byte aligned,
+/* Bind the host state of one group (lqnn 二: per parameter an fp32 master,
+ * its gradient and Adam m / v, all in host memory; lqnn 三.1: a pinned,
+ * pre-flattened copy per layer for the fastest DMA path): fp32 master, grad,
+ * adam_m, adam_v flat arrays of exactly mt_layout's flat_numel elements
+ * (64-byte aligned,
  * pageable memory is fine).  The caller keeps ownership; the arrays must
  * outlive the context.  For blocks and the head the library makes a pinned
  * bf16 working copy (round-to-nearest-even of master) that is what streams
@@ -189,7 +199,10 @@ mt_status mt_bind_layer(mt_ctx* ctx, int32_t group, float* master, float* grad, 
                         float* adam_v, int64_t numel);
 
 /* Enqueue the forward pass of one pass of micro_batches_per_pass
- * micro-batches: embedding gather on the host, streamed block forwards with a
+ * micro-batches (zhichai design point 2: each layer's parameters are
+ * prefetched, the layer runs and its buffer is released; design point 3: a
+ * checkpoint every K layers): embedding gather on the host, streamed block
+ * forwards with a
  * checkpoint every K layers, the LM head in vocabulary chunks, cross-entropy
  * and its gradient, scaled for each micro-batch by grad_scale / (labelled
  * tokens of that micro-batch).  tokens and labels are host int32 arrays of
@@ -201,10 +214,16 @@ mt_status mt_bind_layer(mt_ctx* ctx, int32_t group, float* master, float* grad, 
 mt_status mt_forward(mt_ctx* ctx, const int32_t* tokens, const int32_t* labels, float grad_scale,
                      float* loss_out);
 
-/* Enqueue the backward pass of the last forward: LM head gradients, then per
- * segment (last to first) recompute from the checkpoint and block backwards.
- * Each unit's fp32 gradient is written into a free slab, copied to pinned host
- * memory on the offload stream and added by the worker into the host grad:
+/* Enqueue the backward pass of the last forward (zhichai design point 2:
+ * backward streams like forward and each layer's gradients go back to host
+ * memory, never accumulated on the GPU; design point 3 / lqnn 三.4: each
+ * K-layer segment is recomputed from its checkpoint; lqnn 三.3: gradients land
+ * in a free slab of the pool and a CPU thread adds them into the fp32 master
+ * gradients): LM head gradients, then per segment (last to first) recompute
+ * from the checkpoint and block backwards.  Each unit's gradient is written
+ * into a free slab (bf16 or fp32, mt_config.slab_bf16), copied to pinned host
+ * memory on the offload stream and added in fp32 by the worker into the host
+ * grad:
  * accumulate = 0 sets grad = g, accumulate = 1 adds grad += g.  The embedding
  * gradient is scattered into the embedding grad on the host.  May block while
  * every slab is in flight. */
@@ -224,11 +243,15 @@ mt_status mt_backward_step(mt_ctx* ctx, int32_t accumulate, const mt_adamw_hpara
 
 /* Wait until every gradient of every enqueued backward is in the host grads
  * (and, after mt_backward_step, every group is updated) and all streams are
- * idle; writes pending losses. */
+ * idle; writes pending losses.  The end of lqnn 三.3's three-stage pipeline
+ * (GPU backward -> gradient copy -> CPU accumulation): its last stage drained. */
 mt_status mt_flush_grads(mt_ctx* ctx);
 
 /* Wait only until the loss of every enqueued forward has been computed and
- * write the pending losses (the *loss_out pointers given to mt_forward).
+ * write the pending losses (the *loss_out pointers given to mt_forward), so
+ * that the host optimizer of one step overlaps the next step's streaming
+ * (lqnn 二: the optimizer runs on the CPU where its state lives; 三.3: the
+ * stages are pipelined rather than serialised).
  * Unlike mt_flush_grads it does not wait for slab drains, host accumulation
  * or the overlapped optimizer, so a training loop of mt_backward_step steps
  * can read each step's loss while the host is still updating that step's
@@ -239,9 +262,15 @@ mt_status mt_sync_loss(mt_ctx* ctx);
 
 /* AdamW on every bound group (decoupled weight decay, bias correction, step is
  * 1-based), then refresh the pinned bf16 working copies.  Allowed only after
- * mt_flush_grads. */
+ * mt_flush_grads.  zhichai design point 1: the optimizer step runs on the
+ * CPU, so optimizer state never crosses to the GPU; lqnn 二: the in-memory
+ * fp32 master is updated and the GPU only ever sees a use-and-discard copy. */
 mt_status mt_adamw_step(mt_ctx* ctx, const mt_adamw_hparams* hp, int64_t step);
 
+/* Counters of the pipeline (bytes each way over the host link, loads, slab
+ * waits, host seconds), the quantities the pages' link-bound argument is about
+ * (zhichai design point 2 and 存储层次: the CPU-GPU link is the bottleneck).
+ * MT_E_ARG for null pointers. */
 mt_status mt_get_stats(mt_ctx* ctx, mt_stats* out);
 
 /* Live per-kernel timing.  While enabled, the library records a pair of HIP
@@ -261,16 +290,35 @@ typedef struct mt_kernel_time {
 mt_status mt_kernel_timing(mt_ctx* ctx, int32_t enable);
 /* Kinds seen since timing was enabled, by descending device time. */
 mt_status mt_get_kernel_times(mt_ctx* ctx, mt_kernel_time* out, int32_t cap, int32_t* n_out);
+
+/* The loss of an optimizer step built by gradient accumulation
+ * (travelaiplan 怎麼開始: the global batch is reached by accumulating
+ * micro-batches): the mean over the step's passes of the pass losses
+ * mt_forward computed (each the mean over its micro-batches), summed in
+ * float64 in pass order.  The step is the one still open (passes enqueued
+ * since the last mt_backward_step or mt_adamw_step), or, if none is open, the
+ * last one completed.  Waits for those losses on the GPU.  MT_E_STATE if no
+ * pass has run yet; MT_E_ARG for null pointers. */
+mt_status mt_step_loss(mt_ctx* ctx, float* loss_out);
+
+/* Message of the last error of the context (a string owned by it). */
 const char* mt_last_error(const mt_ctx* ctx);
+/* Waits for the streams, stops the worker threads and frees what the library
+ * allocated (pinned copies and slabs, events); the caller's arena and host
+ * state are untouched. */
 void mt_destroy(mt_ctx* ctx);
 
 /* ---- host kernels, usable without a GPU (the same code the context runs) ---- */
 
-/* fp32 -> bf16 round-to-nearest-even (NaN stays NaN), n elements. */
+/* fp32 -> bf16 round-to-nearest-even (NaN stays NaN), n elements: how the
+ * pinned working copy is made from the fp32 master (lqnn 二: the GPU only sees
+ * a use-and-discard copy; round-to-nearest-even is the reading taken, the
+ * pages fix no rounding). */
 mt_status mt_host_cast_bf16(const float* src, uint16_t* dst, int64_t n, int32_t threads);
 
-/* One AdamW step over n elements in place; bf16_out (may be NULL) receives
- * RNE(master) after the update. */
+/* One AdamW step over n elements in place (lqnn 二: the optimizer named is
+ * PyTorch AdamW, run on the CPU; decoupled decay, bias correction); bf16_out
+ * (may be NULL) receives RNE(master) after the update. */
 mt_status mt_host_adamw(float* master, const float* grad, float* m, float* v, uint16_t* bf16_out,
                         int64_t n, const mt_adamw_hparams* hp, int64_t step, int32_t threads);
 
@@ -282,7 +330,9 @@ mt_status mt_host_adamw_slab(float* master, float* grad, float* m, float* v, uin
                              const void* slab, int32_t slab_bf16, int32_t accumulate, int64_t n,
                              const mt_adamw_hparams* hp, int64_t step, int32_t threads);
 
-/* grad = src (accumulate = 0) or grad += src (accumulate = 1). */
+/* grad = src (accumulate = 0) or grad += src (accumulate = 1): the CPU
+ * worker's accumulation of a drained slab into the fp32 master gradient
+ * (lqnn 三.3). */
 mt_status mt_host_accumulate(float* grad, const float* src, int64_t n, int32_t accumulate,
                              int32_t threads);
 
@@ -296,7 +346,8 @@ mt_status mt_host_triad(float* a, const float* b, const float* c, float s, int64
                         int32_t threads, double* best_s);
 
 /* RoPE cos/sin tables [seq_len, head_dim/2] from float64 angles
- * pos * base^(-2i/head_dim), rounded to fp32. */
+ * pos * base^(-2i/head_dim), rounded to fp32 (the block's RoPE is a reading:
+ * the pages name "Llama" layers, lqnn 四, and give no formula). */
 mt_status mt_host_rope_table(int32_t seq_len, int32_t head_dim, float base, float* cos_out,
                              float* sin_out);
 
