@@ -144,6 +144,8 @@ _SIGS = {
     "mtk_rmsnorm_fwd": ([_P, _P, _P, _P, _I64, _I32, _F, _P], C.c_int),
     "mtk_rmsnorm_bwd_workspace": ([_I64, _I32], C.c_size_t),
     "mtk_rmsnorm_bwd": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _P], C.c_int),
+    "mtk_rmsnorm_bwd_noalloc": ([_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _P], C.c_int),
+    "mtk_noalloc_scratch_bytes": ([], C.c_size_t),
     "mtk_rope": ([_P, _I64, _I32, _I32, _I32, _I32, _P, _P, _I32, _P], C.c_int),
     "mtk_attention_fwd": ([_P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P], C.c_int),
     "mtk_attention_bwd_workspace": ([_I32, _I32, _I32, _I32, _I32], C.c_size_t),
@@ -350,6 +352,17 @@ def mtk_rmsnorm_bwd(dn, x, rstd, g, resid, dx, dx_bf16, dg, workspace, T, h, str
     _check(_lib.mtk_rmsnorm_bwd(_ptr(dn), _ptr(x), _ptr(rstd), _ptr(g), _ptr(resid), _ptr(dx),
                                 _ptr(dx_bf16), _ptr(dg), _ptr(workspace), T, h, _stream(stream)),
            "mtk_rmsnorm_bwd")
+
+
+def mtk_rmsnorm_bwd_noalloc(dn, x, rstd, g, resid, dx, dx_bf16, dg, T, h, stream=None):
+    """mtk_rmsnorm_bwd on the library's fixed per-GPU scratch (no allocation)."""
+    _check(_lib.mtk_rmsnorm_bwd_noalloc(_ptr(dn), _ptr(x), _ptr(rstd), _ptr(g), _ptr(resid),
+                                        _ptr(dx), _ptr(dx_bf16), _ptr(dg), T, h, _stream(stream)),
+           "mtk_rmsnorm_bwd_noalloc")
+
+
+def mtk_noalloc_scratch_bytes() -> int:
+    return _lib.mtk_noalloc_scratch_bytes()
 
 
 def mtk_rope(qkv, T, seq_len, n_heads, n_kv_heads, head_dim, cos_t, sin_t, inverse, stream=None):

@@ -86,6 +86,23 @@ mt_status mtk_rmsnorm_bwd(const float* dn, const float* x, const float* rstd, co
                           const float* resid, float* dx, uint16_t* dx_bf16, float* dg,
                           void* workspace, int64_t T, int32_t h, void* stream);
 
+/* mtk_rmsnorm_bwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight training loops,
+ * harnesses that forbid hipMalloc).  It allocates nothing: the column
+ * partials live in a fixed device array of mtk_noalloc_scratch_bytes() bytes
+ * (48 MiB) per GPU, held until the process ends.  Same arguments and results
+ * as mtk_rmsnorm_bwd (bit for bit: the same kernels).  MT_E_NOMEM when
+ * mtk_rmsnorm_bwd_workspace(T, h) exceeds that size (nothing is launched);
+ * MT_E_ARG as mtk_rmsnorm_bwd.  Calls that overlap in time on one GPU (other
+ * streams or threads) race on the shared array; calls ordered on one stream
+ * do not. */
+mt_status mtk_rmsnorm_bwd_noalloc(const float* dn, const float* x, const float* rstd,
+                                  const uint16_t* g, const float* resid, float* dx,
+                                  uint16_t* dx_bf16, float* dg, int64_t T, int32_t h,
+                                  void* stream);
+/* Size of that fixed per-GPU scratch array, in bytes. */
+size_t mtk_noalloc_scratch_bytes(void);
+
 /* RoPE in place on the q and k columns of qkv [T, (n_heads + 2 n_kv_heads) * d]:
  * pairs (i, i+d/2) of every head rotated by +angle (inverse = 0) or -angle,
  * angle table cos/sin fp32 [seq_len, d/2], position = t mod seq_len. */
