@@ -5,6 +5,7 @@ gradient relative L2 <= 2e-2, master weights relative L2 <= 1e-3 after the
 steps.  Pipeline invariants: the checkpoint interval, the slab-pool size and
 the CPU worker's timing must not change a single bit of the gradients.
 """
+import math
 import os
 
 import numpy as np
@@ -129,13 +130,52 @@ def test_c1_three_step_trajectory():
     assert max(weights.values()) <= 1e-2
 
 
-@pytest.mark.xfail(reason="bf16-operand gradients (error ~1e-2 at the bf16 floor) flip the "
-                          "sign of ~0.3% of AdamW's first updates; 1e-3 needs < 3e-4",
-                   strict=False)
-def test_c1_weights_within_1e3_after_three_steps():
+def test_c1_weights_after_three_steps_against_sign_flip_floor():
+    """The 1e-3 weight target after three steps, with the account of what
+    stands in its way (risk R1).  AdamW's first updates are about lr * sign(g)
+    per element, so an element whose gradient sign differs between the bf16
+    path and the exact oracle ends up 2 lr apart.  With a measured
+    sign-disagreement fraction f (step 1, identical weights on both sides) a
+    tensor of rms sigma drifts by about 2 lr sqrt(3 f) / sigma over three
+    steps.  Per tensor: gradient error delta, f, that predicted floor and the
+    measured weight error.  Asserted: the measured error stays within twice
+    the predicted floor (sign flips account for it), and tensors without a
+    flipped sign meet 1e-3; the 1e-3 target itself is reported as an expected
+    failure when missed."""
     cfg = PRESETS["C1"]
-    _, weights = independent_trajectories(cfg, 3)
-    assert max(weights.values()) <= WEIGHT_TOL
+    sess = _session(cfg)
+    st = HostState(cfg, np.float32)
+    st.load_weights(weight_stream(cfg, 0))
+    sigma = {k: float(np.sqrt(np.mean(v ** 2))) for k, v in _tensors(cfg, st.master).items()}
+    try:
+        flips, delta = {}, {}
+        for step in (1, 2, 3):
+            tok, lab = make_batch(cfg, step)
+            gl = sess.forward_backward(tok, lab)
+            ol = train_step(st, tok, lab, step)
+            assert abs(gl - ol) <= LOSS_TOL
+            if step == 1:
+                gg, og = _tensors(cfg, sess.grad), _tensors(cfg, st.grad)
+                for k in og:
+                    delta[k] = rel_l2(gg[k], og[k])
+                    flips[k] = float(np.mean(np.sign(gg[k]) != np.sign(og[k])))
+            from host_memory_centric_stateless_amd import mt_adamw_hparams, mt_adamw_step
+            mt_adamw_step(sess.ctx, mt_adamw_hparams(cfg.lr, 0.9, 0.999, 1e-8, 0.01), step)
+        gw, ow = _tensors(cfg, sess.master), _tensors(cfg, st.master)
+    finally:
+        sess.close()
+    print(f"{'tensor':24s} {'delta':>9s} {'flips f':>9s} {'floor':>9s} {'weights':>9s}")
+    worst = 0.0
+    for k in sorted(ow):
+        meas = rel_l2(gw[k], ow[k])
+        floor = 2 * cfg.lr * math.sqrt(3 * flips[k]) / sigma[k]
+        worst = max(worst, meas)
+        print(f"{str(k):24s} {delta[k]:9.2e} {flips[k]:9.2e} {floor:9.2e} {meas:9.2e}")
+        # a tensor with no flipped sign must meet the target itself
+        assert meas <= (2.0 * floor if flips[k] > 0 else WEIGHT_TOL), (k, meas, floor)
+    if worst > WEIGHT_TOL:
+        pytest.xfail(f"weights {worst:.2e} after 3 steps > {WEIGHT_TOL}: the bf16 gradients' sign "
+                     "flips set the floor printed per tensor")
 
 
 def _grads_after_one_step(cfg, **kw):
