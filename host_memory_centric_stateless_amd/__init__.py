@@ -57,7 +57,7 @@ class mt_config(C.Structure):
                 ("micro_batch", C.c_int32), ("seq_len", C.c_int32), ("ckpt_interval", C.c_int32),
                 ("n_grad_slabs", C.c_int32), ("host_threads", C.c_int32),
                 ("slab_bf16", C.c_int32), ("drain_workgroups", C.c_int32),
-                ("micro_batches_per_pass", C.c_int32)]
+                ("micro_batches_per_pass", C.c_int32), ("head_token_chunk", C.c_int32)]
 
 
 class mt_tensor_desc(C.Structure):
@@ -195,12 +195,12 @@ DEFAULT_DRAIN_WORKGROUPS = 4  # slabs leave through a 4-workgroup copy kernel
 
 def make_config(cfg, host_threads: int = 0, slab_bf16: bool = True,
                 drain_workgroups: int = DEFAULT_DRAIN_WORKGROUPS,
-                micro_batches_per_pass: int = 1) -> mt_config:
+                micro_batches_per_pass: int = 1, head_token_chunk: int = 0) -> mt_config:
     """mt_config from any object with the ModelConfig attribute names."""
     return mt_config(cfg.n_layers, cfg.hidden, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ffn,
                      cfg.vocab, cfg.rms_eps, cfg.rope_base, cfg.micro_batch, cfg.seq_len,
                      cfg.ckpt_interval, cfg.n_grad_slabs, host_threads, int(bool(slab_bf16)),
-                     int(drain_workgroups), int(micro_batches_per_pass))
+                     int(drain_workgroups), int(micro_batches_per_pass), int(head_token_chunk))
 
 
 # ------------------------------------------------------------- C-ABI calls

@@ -76,6 +76,34 @@ hipError_t launch_cross_entropy(const float* logits, int64_t ld, const int32_t* 
                                 int V, float grad_scale, int64_t n_valid, uint16_t* dlogits,
                                 int64_t ld_d, float* loss_rows, float* loss_out, hipStream_t s);
 
+// Cross-entropy in token x vocabulary chunks (the LM head never holds a whole
+// [T, V] logits matrix).  CeCoef: the dlogits coefficient of each micro-batch
+// of the pass (grad_scale / labelled tokens), rows t of micro-batch t / T_mb.
+struct CeCoef {
+  float c[32];
+  int64_t T_mb;
+};
+// Merge the softmax statistics of `rows` rows of one logits chunk (columns
+// r0 .. r0+nr of the vocabulary, row stride ld) into m_run / s_run (first:
+// overwrite) and keep the label's logit when it is in the chunk.  Pointers
+// labels, m_run, s_run, lab_logit are offset to the chunk's first row.
+hipError_t launch_ce_stats(const float* logits, int64_t ld, int64_t rows, int nr, int64_t r0,
+                           const int32_t* labels, int first, float* m_run, float* s_run,
+                           float* lab_logit, hipStream_t s);
+// lse = m + log(s) and loss_rows = lse - label logit (0 where label < 0) for T rows.
+hipError_t launch_ce_finish(const float* m_run, const float* s_run, const float* lab_logit,
+                            const int32_t* labels, int64_t T, float* lse, float* loss_rows,
+                            hipStream_t s);
+// dlogits (bf16, row stride ldd) of `rows` rows of one logits chunk; labels
+// and lse offset to the chunk's first row, which is row t0 of the pass.
+hipError_t launch_ce_grad(const float* logits, int64_t ld, int64_t rows, int nr, int64_t r0,
+                          const int32_t* labels, const float* lse, int64_t t0, const CeCoef& cf,
+                          uint16_t* dl, int64_t ldd, hipStream_t s);
+// fp32 -> bf16 round-to-nearest-even, n a multiple of 4.
+hipError_t launch_cast_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s);
+// out[0] = inv_n * sum of rows[0..n) (one workgroup, fixed order).
+hipError_t launch_loss_mean(const float* rows, int64_t n, float inv_n, float* out, hipStream_t s);
+
 // 16-byte-vector copy by `wgs` workgroups (bytes multiple of 16; either side
 // may be host-mapped pinned memory).
 hipError_t launch_copy(void* dst, const void* src, size_t bytes, int wgs, hipStream_t s);

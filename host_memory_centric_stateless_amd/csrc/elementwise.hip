@@ -306,6 +306,116 @@ __global__ __launch_bounds__(NT) void ce_kernel(const float* __restrict__ logits
   if (threadIdx.x == 0) loss_rows[row] = lse - lr[label];
 }
 
+// ---------------------------------------- cross-entropy in token x vocab chunks
+// The LM head's logits exist one token chunk x one vocabulary chunk at a time.
+// Forward: each chunk's softmax statistics (row maximum m_c and sum of
+// exp(l - m_c)) are merged into the token's running (m, s), and the label's
+// logit is kept when the label falls in the chunk.  After the last chunk
+// lse = m + log(s).  Backward: each chunk's logits are recomputed and
+// dlogits = (exp(l - lse) - onehot) * coef follows without the whole row.
+
+// Chunk statistics of one row, one workgroup per row of the token chunk.
+__global__ __launch_bounds__(NT) void ce_stats_kernel(const float* __restrict__ logits, int64_t ld,
+                                                      int nr, int64_t r0,
+                                                      const int32_t* __restrict__ labels, int first,
+                                                      float* __restrict__ m_run,
+                                                      float* __restrict__ s_run,
+                                                      float* __restrict__ lab_logit) {
+  __shared__ float shm[4], shs[4];
+  const int64_t row = blockIdx.x;
+  const float* lr = logits + row * ld;
+  float m = -INFINITY, s = 0.0f;
+  for (int c = threadIdx.x * 4; c < nr; c += NT * 4) {
+    const float4 v = *reinterpret_cast<const float4*>(lr + c);
+    const float mx = fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w));
+    const float mn = fmaxf(m, mx);
+    s = s * expf(m - mn) + expf(v.x - mn) + expf(v.y - mn) + expf(v.z - mn) + expf(v.w - mn);
+    m = mn;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float mo = __shfl_xor(m, o), so = __shfl_xor(s, o);
+    const float mn = fmaxf(m, mo);
+    s = (m == -INFINITY ? 0.0f : s * expf(m - mn)) + (mo == -INFINITY ? 0.0f : so * expf(mo - mn));
+    m = mn;
+  }
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (lane == 0) {
+    shm[w] = m;
+    shs[w] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  const float M = fmaxf(fmaxf(shm[0], shm[1]), fmaxf(shm[2], shm[3]));
+  float S = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) S += shs[k] * expf(shm[k] - M);
+  if (first) {
+    m_run[row] = M;
+    s_run[row] = S;
+  } else {
+    const float mo = m_run[row], so = s_run[row];
+    const float mn = fmaxf(mo, M);
+    s_run[row] = so * expf(mo - mn) + S * expf(M - mn);
+    m_run[row] = mn;
+  }
+  const int64_t label = labels[row];
+  if (label >= r0 && label < r0 + nr) lab_logit[row] = lr[label - r0];
+}
+
+// lse and the per-row loss (0 for ignored rows), one thread per row.
+__global__ __launch_bounds__(NT) void ce_finish_kernel(const float* __restrict__ m_run,
+                                                       const float* __restrict__ s_run,
+                                                       const float* __restrict__ lab_logit,
+                                                       const int32_t* __restrict__ labels,
+                                                       int64_t T, float* __restrict__ lse,
+                                                       float* __restrict__ loss_rows) {
+  const int64_t t = (int64_t)blockIdx.x * NT + threadIdx.x;
+  if (t >= T) return;
+  const float l = m_run[t] + logf(s_run[t]);
+  lse[t] = l;
+  loss_rows[t] = labels[t] >= 0 ? l - lab_logit[t] : 0.0f;
+}
+
+// dlogits of one token chunk x vocabulary chunk, one workgroup per row:
+// rows t0 + row of the pass; coefficient of the row's micro-batch.
+__global__ __launch_bounds__(NT) void ce_grad_kernel(const float* __restrict__ logits, int64_t ld,
+                                                     int nr, int64_t r0,
+                                                     const int32_t* __restrict__ labels,
+                                                     const float* __restrict__ lse, int64_t t0,
+                                                     CeCoef cf, uint16_t* __restrict__ dl,
+                                                     int64_t ldd) {
+  const int64_t row = blockIdx.x;
+  const float* lr = logits + row * ld;
+  uint16_t* dr = dl + row * ldd;
+  const int64_t label = labels[row];
+  if (label < 0) {
+    for (int c = threadIdx.x * 4; c < nr; c += NT * 4)
+      *reinterpret_cast<uint2*>(dr + c) = make_uint2(0u, 0u);
+    return;
+  }
+  const float l = lse[row];
+  const float coef = cf.c[(t0 + row) / cf.T_mb];
+  const int64_t lc = label - r0;  // label column inside the chunk (may be outside)
+  for (int c = threadIdx.x * 4; c < nr; c += NT * 4) {
+    const float4 v = *reinterpret_cast<const float4*>(lr + c);
+    float p[4] = {expf(v.x - l), expf(v.y - l), expf(v.z - l), expf(v.w - l)};
+    if (lc >= c && lc < c + 4) p[lc - c] -= 1.0f;
+    *reinterpret_cast<uint2*>(dr + c) =
+        make_uint2(pack_bf2(p[0] * coef, p[1] * coef), pack_bf2(p[2] * coef, p[3] * coef));
+  }
+}
+
+// fp32 -> bf16 (round to nearest even), n a multiple of 4.
+__global__ void cast_bf16_kernel(const float* __restrict__ src, uint16_t* __restrict__ dst,
+                                 int64_t n4) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+    const float4 v = reinterpret_cast<const float4*>(src)[i];
+    reinterpret_cast<uint2*>(dst)[i] = make_uint2(pack_bf2(v.x, v.y), pack_bf2(v.z, v.w));
+  }
+}
+
 // Fixed-order sum of loss_rows: thread t adds rows t, t+256, ...; then the
 // block sum.
 __global__ __launch_bounds__(NT) void loss_reduce_kernel(const float* __restrict__ rows, int64_t T,
@@ -390,6 +500,42 @@ hipError_t launch_rope(uint16_t* qkv, int64_t T, int seq, int nq, int nkv, int d
   else
     hipLaunchKernelGGL(rope_kernel, dim3((unsigned)((total + NT - 1) / NT)), dim3(NT), 0, s, qkv, T,
                        seq, nrot, ld, d, cos_t, sin_t, inverse ? -1.0f : 1.0f);
+  return hipGetLastError();
+}
+
+hipError_t launch_ce_stats(const float* logits, int64_t ld, int64_t rows, int nr, int64_t r0,
+                           const int32_t* labels, int first, float* m_run, float* s_run,
+                           float* lab_logit, hipStream_t s) {
+  hipLaunchKernelGGL(ce_stats_kernel, dim3((unsigned)rows), dim3(NT), 0, s, logits, ld, nr, r0,
+                     labels, first, m_run, s_run, lab_logit);
+  return hipGetLastError();
+}
+
+hipError_t launch_ce_finish(const float* m_run, const float* s_run, const float* lab_logit,
+                            const int32_t* labels, int64_t T, float* lse, float* loss_rows,
+                            hipStream_t s) {
+  hipLaunchKernelGGL(ce_finish_kernel, dim3((unsigned)((T + NT - 1) / NT)), dim3(NT), 0, s, m_run,
+                     s_run, lab_logit, labels, T, lse, loss_rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_ce_grad(const float* logits, int64_t ld, int64_t rows, int nr, int64_t r0,
+                          const int32_t* labels, const float* lse, int64_t t0, const CeCoef& cf,
+                          uint16_t* dl, int64_t ldd, hipStream_t s) {
+  hipLaunchKernelGGL(ce_grad_kernel, dim3((unsigned)rows), dim3(NT), 0, s, logits, ld, nr, r0,
+                     labels, lse, t0, cf, dl, ldd);
+  return hipGetLastError();
+}
+
+hipError_t launch_cast_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s) {
+  const int64_t n4 = n / 4;
+  if (n4 > 0)
+    hipLaunchKernelGGL(cast_bf16_kernel, dim3(1024), dim3(NT), 0, s, src, dst, n4);
+  return hipGetLastError();
+}
+
+hipError_t launch_loss_mean(const float* rows, int64_t n, float inv_n, float* out, hipStream_t s) {
+  hipLaunchKernelGGL(loss_reduce_kernel, dim3(1), dim3(NT), 0, s, rows, n, inv_n, out);
   return hipGetLastError();
 }
 

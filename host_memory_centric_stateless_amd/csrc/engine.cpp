@@ -141,6 +141,10 @@ struct mt_ctx {
   int parity = 0;
   int dy_idx = 0;
   bool head_grad_first = true;
+  // labelled tokens of each micro-batch of the current pass and its loss
+  // scale (the cross-entropy coefficients of the head's backward)
+  int64_t n_valid[32] = {};
+  float grad_scale = 1.0f;
   std::vector<int32_t> tok_cur;
   State state = ST_UNBOUND;
   int accumulate = 0;
@@ -813,7 +817,7 @@ mt_status run_step(mt_ctx* c, const Step& s) {
   const Plan& p = c->p;
   const mt_config& g = p.c;
   const int L = g.n_layers, K = g.ckpt_interval;
-  const int64_t T = p.T, h = g.hidden, V = g.vocab;
+  const int64_t T = p.T, h = g.hidden;
   hipStream_t cs = c->sc;
   const uint16_t* W = s.buf >= 0 ? c->wbuf[s.buf] : nullptr;
   if (s.load >= 0) MT_HIP(c, hipStreamWaitEvent(cs, c->ev_ready[s.buf], 0));
@@ -840,6 +844,8 @@ mt_status run_step(mt_ctx* c, const Step& s) {
       break;
     }
     case K_HEAD_LOGITS: {
+      // the chunk's logits, one token chunk at a time, reduced at once to
+      // softmax statistics merged into each token's running log-sum-exp
       const int ch = s.chunk;
       const uint16_t* Wr = W + (ch == 0 ? p.head[1].off : 0);
       const int64_t r0 = p.chunk_row0[ch], nr = p.chunk_row0[ch + 1] - r0;
@@ -847,8 +853,17 @@ mt_status run_step(mt_ctx* c, const Step& s) {
         MT_HIP(c, launch_rmsnorm_fwd(c->wsp<float>(p.ws.xL), W + p.head[0].off,
                                      c->wsp<uint16_t>(p.ws.xf), c->wsp<float>(p.ws.rstd_f), T,
                                      (int)h, g.rms_eps, cs));
-      MT_HIP(c, gemm(c, cs, MT_GEMM_NT, MT_EPI_F32, T, nr, h, c->wsp<uint16_t>(p.ws.xf), h, Wr, h,
-                     c->wsp<float>(p.ws.logits) + r0, V));
+      const int32_t* lab = c->wsp<int32_t>(p.ws.labels[c->parity]);
+      for (int64_t t0 = 0; t0 < T; t0 += p.head_tc) {
+        const int64_t tn = std::min<int64_t>(p.head_tc, T - t0);
+        MT_HIP(c, gemm(c, cs, MT_GEMM_NT, MT_EPI_F32, tn, nr, h, c->wsp<uint16_t>(p.ws.xf) + t0 * h,
+                       h, Wr, h, c->wsp<float>(p.ws.logits), p.head_rows));
+        KScope k(c, cs, "cross_entropy", 0, (double)tn * nr * 4);
+        MT_HIP(c, launch_ce_stats(c->wsp<float>(p.ws.logits), p.head_rows, tn, (int)nr, r0, lab + t0,
+                                  ch == 0, c->wsp<float>(p.ws.ce_m) + t0,
+                                  c->wsp<float>(p.ws.ce_s) + t0, c->wsp<float>(p.ws.ce_lab) + t0,
+                                  cs));
+      }
       break;
     }
     case K_CE: {
@@ -867,12 +882,41 @@ mt_status run_step(mt_ctx* c, const Step& s) {
       const int64_t r0 = p.chunk_row0[ch], nr = p.chunk_row0[ch + 1] - r0;
       if (ch == 0 && p.head[1].off > p.head[0].numel)
         MT_HIP(c, hipMemsetAsync(slab, 0, (size_t)p.head[1].off * es, cs));
-      const uint16_t* dl = c->wsp<uint16_t>(p.ws.dlogits) + r0;
-      MT_HIP(c, gemm(c, cs, MT_GEMM_NN, c->head_grad_first ? MT_EPI_F32 : MT_EPI_F32_ACCUM, T, h, nr,
-                     dl, V, Wr, h, c->wsp<float>(p.ws.dxf), h));
+      // per token chunk: recompute the chunk's logits, form dlogits from the
+      // forward's log-sum-exp, then dxf (+)= dl W and dW (+)= dl^T xf
+      const int32_t* lab = c->wsp<int32_t>(p.ws.labels[c->parity]);
+      CeCoef cf;
+      cf.T_mb = p.T_mb;
+      for (int mb = 0; mb < 32; ++mb)
+        cf.c[mb] = (mb < p.n_mb && c->n_valid[mb] > 0) ? c->grad_scale / (float)c->n_valid[mb] : 0.0f;
+      uint16_t* dl = c->wsp<uint16_t>(p.ws.dlogits);
+      const bool multi = p.n_tchunks > 1;
+      float* acc32 = sb ? c->wsp<float>(p.ws.dw_acc) : static_cast<float*>(dWr);
+      for (int64_t t0 = 0; t0 < T; t0 += p.head_tc) {
+        const int64_t tn = std::min<int64_t>(p.head_tc, T - t0);
+        const uint16_t* xf = c->wsp<uint16_t>(p.ws.xf) + t0 * h;
+        MT_HIP(c, gemm(c, cs, MT_GEMM_NT, MT_EPI_F32, tn, nr, h, xf, h, Wr, h,
+                       c->wsp<float>(p.ws.logits), p.head_rows));
+        {
+          KScope k(c, cs, "cross_entropy", 0, (double)tn * nr * 6);
+          MT_HIP(c, launch_ce_grad(c->wsp<float>(p.ws.logits), p.head_rows, tn, (int)nr, r0,
+                                   lab + t0, c->wsp<float>(p.ws.ce_lse) + t0, t0, cf, dl,
+                                   p.head_rows, cs));
+        }
+        MT_HIP(c, gemm(c, cs, MT_GEMM_NN, c->head_grad_first ? MT_EPI_F32 : MT_EPI_F32_ACCUM, tn, h,
+                       nr, dl, p.head_rows, Wr, h, c->wsp<float>(p.ws.dxf) + t0 * h, h));
+        if (!multi)
+          MT_HIP(c, gemm(c, cs, MT_GEMM_TN, sb ? MT_EPI_BF16 : MT_EPI_F32, nr, h, tn, dl,
+                         p.head_rows, xf, h, dWr, h));
+        else
+          MT_HIP(c, gemm(c, cs, MT_GEMM_TN, t0 == 0 ? MT_EPI_F32 : MT_EPI_F32_ACCUM, nr, h, tn, dl,
+                         p.head_rows, xf, h, acc32, h));
+      }
+      if (multi && sb) {
+        KScope k(c, cs, "cast_bf16", 0, (double)nr * h * 6);
+        MT_HIP(c, launch_cast_bf16(acc32, static_cast<uint16_t*>(dWr), nr * h, cs));
+      }
       c->head_grad_first = false;
-      MT_HIP(c, gemm(c, cs, MT_GEMM_TN, sb ? MT_EPI_BF16 : MT_EPI_F32, nr, h, T, dl, V,
-                     c->wsp<uint16_t>(p.ws.xf), h, dWr, h));
       if (ch == 0) {
         c->dy_idx = 0;
         MT_HIP(c, launch_rmsnorm_bwd(c->wsp<float>(p.ws.dxf), c->wsp<float>(p.ws.xL),
@@ -957,19 +1001,27 @@ mt_status run_until(mt_ctx* c, size_t end, const int64_t* n_valid, float grad_sc
       return MT_E_STATE;
     }
     if (s.kind == K_CE) {
-      // one launch per micro-batch of the pass, each normalised by its own
-      // valid-label count; the pass loss (slot 0) is the mean of theirs
+      // per-token loss from the merged log-sum-exp; one mean per micro-batch
+      // of the pass, each over its own labelled tokens; the pass loss (slot
+      // 0) is the mean of theirs
       const Plan& p = c->p;
-      KScope k(c, c->sc, "cross_entropy", 0, (double)p.T * p.c.vocab * 6);
-      const int64_t V = p.c.vocab, Tm = p.T_mb;
+      const int64_t Tm = p.T_mb;
       float* loss = c->wsp<float>(p.ws.loss);
+      for (int mb = 0; mb < p.n_mb; ++mb) {
+        c->n_valid[mb] = n_valid[mb];
+      }
+      c->grad_scale = grad_scale;
+      {
+        KScope k(c, c->sc, "cross_entropy", 0, (double)p.T * 20);
+        MT_HIP(c, launch_ce_finish(c->wsp<float>(p.ws.ce_m), c->wsp<float>(p.ws.ce_s),
+                                   c->wsp<float>(p.ws.ce_lab),
+                                   c->wsp<int32_t>(p.ws.labels[c->parity]), p.T,
+                                   c->wsp<float>(p.ws.ce_lse), c->wsp<float>(p.ws.loss_rows), c->sc));
+      }
       for (int mb = 0; mb < p.n_mb; ++mb)
-        MT_HIP(c, launch_cross_entropy(c->wsp<float>(p.ws.logits) + mb * Tm * V, V,
-                                       c->wsp<int32_t>(p.ws.labels[c->parity]) + mb * Tm, Tm,
-                                       (int)V, grad_scale, n_valid[mb],
-                                       c->wsp<uint16_t>(p.ws.dlogits) + mb * Tm * V, V,
-                                       c->wsp<float>(p.ws.loss_rows) + mb * Tm,
-                                       p.n_mb == 1 ? loss : loss + 1 + mb, c->sc));
+        MT_HIP(c, launch_loss_mean(c->wsp<float>(p.ws.loss_rows) + mb * Tm, Tm,
+                                   n_valid[mb] > 0 ? 1.0f / (float)n_valid[mb] : 0.0f,
+                                   p.n_mb == 1 ? loss : loss + 1 + mb, c->sc));
       if (p.n_mb > 1) MT_HIP(c, launch_mean(loss + 1, p.n_mb, loss, c->sc));
     } else {
       r = run_step(c, s);

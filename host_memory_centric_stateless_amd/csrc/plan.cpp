@@ -47,6 +47,8 @@ std::string make_plan(const mt_config& c, Plan* p) {
   if (c.drain_workgroups < 0 || c.drain_workgroups > 256) return "drain_workgroups must be in 0..256";
   if (c.micro_batches_per_pass < 1 || c.micro_batches_per_pass > 32)
     return "micro_batches_per_pass must be in 1..32";
+  if (c.head_token_chunk < 0 || c.head_token_chunk % 8)
+    return "head_token_chunk must be 0 or a positive multiple of 8";
 
   p->c = c;
   const int64_t h = c.hidden, F = c.ffn, V = c.vocab;
@@ -57,6 +59,8 @@ std::string make_plan(const mt_config& c, Plan* p) {
   p->kvd = (int64_t)c.n_kv_heads * c.head_dim;
   p->ldq = p->qd + 2 * p->kvd;
   if (p->T / 128 >= 65535) return "too many tokens per micro-batch";
+  p->head_tc = std::min<int64_t>(p->T, c.head_token_chunk > 0 ? c.head_token_chunk : 8192);
+  p->n_tchunks = (int)((p->T + p->head_tc - 1) / p->head_tc);
 
   TensorOff* L = p->layer;
   L[T_ATTN_NORM] = {"attn_norm", 0, 0, 1, (int32_t)h};
@@ -93,6 +97,9 @@ std::string make_plan(const mt_config& c, Plan* p) {
     p->chunk_e0[k] = (k == 0) ? 0 : woff + r * h;
   }
   p->chunk_e0[p->n_chunks] = p->head_elems;
+  p->head_rows = 0;
+  for (int k = 0; k < p->n_chunks; ++k)
+    p->head_rows = std::max(p->head_rows, p->chunk_row0[k + 1] - p->chunk_row0[k]);
   p->unit_elems = p->layer_elems;
   for (int k = 0; k < p->n_chunks; ++k)
     p->unit_elems = std::max(p->unit_elems, p->chunk_e0[k + 1] - p->chunk_e0[k]);
@@ -122,8 +129,17 @@ std::string make_plan(const mt_config& c, Plan* p) {
   w.xL = take(T * h * 4);
   w.xf = take(T * h * 2);
   w.rstd_f = take(T * 4);
-  w.logits = take(T * V * 4);
-  w.dlogits = take(T * V * 2);
+  // one token chunk x one vocabulary chunk of logits and dlogits, the
+  // per-token softmax statistics, and (several token chunks, bf16 slabs) an
+  // fp32 accumulator for the chunk's weight gradient
+  const size_t tc = (size_t)p->head_tc, hr = (size_t)p->head_rows;
+  w.logits = take(tc * hr * 4);
+  w.dlogits = take(tc * hr * 2);
+  w.ce_m = take(T * 4);
+  w.ce_s = take(T * 4);
+  w.ce_lab = take(T * 4);
+  w.ce_lse = take(T * 4);
+  w.dw_acc = take(p->n_tchunks > 1 && c.slab_bf16 ? hr * (size_t)h * 4 : 0);
   w.loss_rows = take(T * 4);
   w.loss = take(256);
   w.dxf = take(T * h * 4);

@@ -29,8 +29,9 @@ struct SlotLayout {
 
 // Byte offsets inside the workspace region.
 struct WorkLayout {
-  size_t xL, xf, rstd_f, logits, dlogits, loss_rows, loss, dxf, dy0, dy1, dyb, dgu, dn, dh1, dh1b,
-      dout, dsum, dqkv, partial, cos_t, sin_t, labels[2], x0[2], bytes;
+  size_t xL, xf, rstd_f, logits, dlogits, ce_m, ce_s, ce_lab, ce_lse, dw_acc, loss_rows, loss, dxf,
+      dy0, dy1, dyb, dgu, dn, dh1, dh1b, dout, dsum, dqkv, partial, cos_t, sin_t, labels[2], x0[2],
+      bytes;
 };
 
 // Indices into Plan::layer[].
@@ -52,6 +53,10 @@ struct Plan {
   // 0 starts at element 0 so it also carries final_norm.
   int n_chunks;
   std::vector<int64_t> chunk_row0, chunk_e0;
+  int64_t head_rows;    // rows of the largest vocabulary chunk
+  // The head's logits exist for one token chunk of head_tc tokens at a time.
+  int64_t head_tc;
+  int n_tchunks;
   int64_t unit_elems;
   bool slab_bf16;       // gradient slabs hold bf16 (else fp32)
   int n_segments;

@@ -29,7 +29,8 @@ class Session:
     def __init__(self, cfg, host_threads: int = 0, device: str = "cuda:0",
                  ckpt_interval: Optional[int] = None, n_grad_slabs: Optional[int] = None,
                  slab_bf16: bool = True, drain_workgroups: Optional[int] = None,
-                 micro_batches_per_pass: int = 1, host_from: Optional["Session"] = None):
+                 micro_batches_per_pass: int = 1, host_from: Optional["Session"] = None,
+                 head_token_chunk: int = 0):
         """host_from: use that session's host fp32 state (same model shape)
         instead of allocating a new one; call bind() before the first step."""
         if ckpt_interval is not None:
@@ -39,7 +40,7 @@ class Session:
         self.cfg = cfg
         self.c = make_config(cfg, host_threads, slab_bf16,
                              DEFAULT_DRAIN_WORKGROUPS if drain_workgroups is None
-                             else drain_workgroups, micro_batches_per_pass)
+                             else drain_workgroups, micro_batches_per_pass, head_token_chunk)
         self.mb_per_pass = micro_batches_per_pass
         self.req = mt_device_requirements(self.c)
         self.groups = [MT_GROUP_EMBED] + list(range(cfg.n_layers)) + [MT_GROUP_HEAD]

@@ -85,6 +85,13 @@ typedef struct mt_config {
                              layer-major order, with weights crossing the host
                              link once per pass instead of once per
                              micro-batch.  1 = one micro-batch per pass.      */
+  int32_t head_token_chunk; /* tokens per LM-head token chunk (a multiple of 8;
+                             0 = 8192).  The head's fp32 logits and bf16
+                             dlogits exist on the device for one token chunk
+                             and one vocabulary chunk at a time: the forward
+                             merges each chunk's softmax statistics into a
+                             per-token log-sum-exp, the backward recomputes
+                             the chunk's logits for its gradient.           */
 } mt_config;
 
 /* One tensor of a group's flat layout. */
@@ -103,7 +110,8 @@ typedef struct mt_device_req {
   size_t checkpoints;     /* max(1, ceil(L/K) - 1) fp32 [T, h] inputs of layers
                              K, 2K, ... (layer 0's input is the x0 staging in
                              the workspace)                                     */
-  size_t workspace;       /* head logits, gradients in flight, RoPE table, ...  */
+  size_t workspace;       /* head logits of one token chunk, gradients in
+                             flight, RoPE table, ...                            */
   size_t device_total;    /* 2*weight_buf + n_slabs*grad_slab + the rest        */
   size_t pinned_host;     /* pinned host bytes the library allocates itself     */
   size_t host_state;      /* caller-owned fp32 master+grad+m+v: 16 B/parameter  */

@@ -129,8 +129,10 @@ LAST_BLOCK_QK = ((1, "wq"), (1, "wk"))
 
 @pytest.mark.timeout(300)
 def test_c2_full_step():
+    """C2's head is streamed in 3 vocabulary chunks; here its logits also
+    exist only 2048 of the 8192 tokens at a time (4 token chunks)."""
     report = {}
-    worst, stats = gradients_at_matched_weights(PRESETS["C2"], 1, report)
+    worst, stats = gradients_at_matched_weights(PRESETS["C2"], 1, report, head_token_chunk=2048)
     for k, v in sorted(report.items()):
         print(k, " ".join(f"{e:.2e}/{sg:.1e}" for e, sg in v))
     assert worst["loss"] <= LOSS_TOL

@@ -100,11 +100,17 @@ def independent_trajectories(cfg, steps):
     return losses, weights
 
 
-@pytest.mark.parametrize("slab_bf16", [True, False])
-def test_c1_gradients_match_oracle_each_step(slab_bf16):
+@pytest.mark.parametrize("slab_bf16,head_token_chunk", [(True, 0), (False, 0), (True, 96),
+                                                         (False, 96)])
+def test_c1_gradients_match_oracle_each_step(slab_bf16, head_token_chunk):
+    """head_token_chunk 96: the LM head's logits exist for 96 of the 256
+    tokens at a time (a ragged last chunk), with the weight gradient summed
+    over the token chunks in fp32 (bf16 slabs: an fp32 accumulator cast once;
+    fp32 slabs: in the slab)."""
     cfg = PRESETS["C1"]
     report = {}
-    worst, stats = gradients_at_matched_weights(cfg, 3, report, slab_bf16=slab_bf16)
+    worst, stats = gradients_at_matched_weights(cfg, 3, report, slab_bf16=slab_bf16,
+                                                head_token_chunk=head_token_chunk)
     for k, v in sorted(report.items()):
         print(k, " ".join(f"{e:.2e}/{sg:.1e}" for e, sg in v))
     print("stats", stats)
@@ -203,7 +209,9 @@ def test_layer_major_pass_matches_oracle_and_microbatch_order():
     got = {}
     for n in (1, 2):
         print("micro_batches_per_pass", n, flush=True)
-        sess = _session(cfg, micro_batches_per_pass=n)
+        # with two micro-batches per pass, head token chunks of 96 straddle the
+        # micro-batch boundary (each row keeps its own micro-batch's scale)
+        sess = _session(cfg, micro_batches_per_pass=n, head_token_chunk=96 if n == 2 else 0)
         try:
             loss = sess.forward_backward(tok, lab)
             got[n] = (loss, _tensors(cfg, sess.grad), sess.stats())
