@@ -72,6 +72,10 @@ PRESETS: Dict[str, ModelConfig] = {
     # long context: 4 layers of the 7B shape, 1 x 131072 tokens, causal
     "C5": ModelConfig("llama-7B-shape-4L-s131072", 4, 4096, 32, 32, 128, 11008, 32000, 1, 131072,
                       grad_accum=1, ckpt_interval=4),
+    # the pages' long-context claim (a 7B model at 512K tokens on one GPU): 4 layers of the 7B
+    # shape on one sequence of 524,288 tokens, a checkpoint before every layer
+    "C6": ModelConfig("llama-7B-shape-4L-s524288", 4, 4096, 32, 32, 128, 11008, 32000, 1, 524288,
+                      grad_accum=1, ckpt_interval=1),
 }
 
 # Tiny GQA shape used for finite-difference checks of the oracle.

@@ -1,5 +1,7 @@
-"""The long-context configuration: 4 layers of the 7B shape on one sequence
-of 131,072 tokens.
+"""The long-context configurations: 4 layers of the 7B shape on one sequence
+of 131,072 tokens, and the 7B shape on one sequence of 524,288 tokens (the
+pages' long-context claim: zhichai.net "MegaTrain：单卡训百亿大模型的突破与实践",
+性能与能力; blog.travelaiplan.net "單卡也能練 100B+：MegaTrain 實戰", 適合誰用).
 
 The oracle cannot run a whole step at this length (one head's score matrix
 alone has 1.7e10 entries), so parity is checked where the oracle can compute
@@ -11,7 +13,11 @@ outputs one by one:
   sampled key rows near the end of the sequence (few queries see them);
 * a full streamed C5 step: the loss sits at its closed-form initial value
   (ln V + 0.0002 h for N(0, 0.02) weights) and every gradient is finite, and a
-  repeated step reproduces the gradients bit for bit.
+  repeated step reproduces the gradients bit for bit;
+* one 7B-shaped layer streamed over 524,288 tokens inside the device memory
+  (the LM head's logits exist one token chunk at a time): loss at its closed
+  form, finite gradients.  (A 16,384-token 7B layer is compared with the
+  oracle tensor by tensor in the configuration tests.)
 """
 import math
 
@@ -26,17 +32,15 @@ from tests.gpu_util import bf16_dev, bf16_round, dev, host
 
 pytestmark = pytest.mark.gpu
 
-S = 131072
-
-
 def _rows_ref(q, k, v, rows):
     return OM.attention_rows(q, k, v, rows)
 
 
-@pytest.mark.timeout(170)
-def test_attention_full_length_sampled_rows():
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("S", [131072, 524288])
+def test_attention_full_length_sampled_rows(S):
     nq, nkv, d = 2, 1, 128
-    print("attn s=131072 nq=2 nkv=1 d=128", flush=True)
+    print(f"attn s={S} nq=2 nkv=1 d=128", flush=True)
     qkv = random_array((S, (nq + 2 * nkv) * d), seed=21)
     xb = bf16_round(qkv)
     q = xb[:, :nq * d].reshape(1, S, nq, d)
@@ -46,7 +50,7 @@ def test_attention_full_length_sampled_rows():
     o = torch.empty((S, nq * d), dtype=torch.bfloat16, device=dev())
     lse = torch.empty((nq, S), dtype=torch.float32, device=dev())
     mt.mtk_attention_fwd(qd, o, lse, 1, S, nq, nkv, d)
-    rows = [0, 1, 127, 128, 4095, 65537, S - 129, S - 1]
+    rows = [0, 1, 127, 128, 4095, 65537, S // 2 + 3, S - 129, S - 1]
     ref = _rows_ref(q, k, v, rows)[0]
     got = host(o).reshape(S, nq, d)[rows]
     err = np.max(np.abs(got - ref)) / np.max(np.abs(ref))
@@ -116,5 +120,30 @@ def test_c5_step_loss_and_determinism():
         st = sess.stats()
         # one segment of 4 layers: nothing is recomputed
         assert st["layer_forwards"] == 2 * cfg.n_layers
+    finally:
+        sess.close()
+
+
+@pytest.mark.timeout(300)
+def test_512k_tokens_one_layer_step():
+    cfg = PRESETS["C6"].replace(n_layers=1)
+    from host_memory_centric_stateless_amd import Session
+    sess = Session(cfg)
+    try:
+        req = sess.req
+        print(f"512K: device {req.device_total / 2**30:.1f} GiB (window {req.window / 2**30:.1f}, "
+              f"workspace {req.workspace / 2**30:.1f}), pinned {req.pinned_host / 2**30:.1f} GiB",
+              flush=True)
+        assert req.device_total < 288e9
+        sess.load_weights(weight_stream(cfg, 0))
+        tok, lab = make_batch(cfg, 1)
+        print("512K step", flush=True)
+        loss = sess.forward_backward(tok, lab)
+        print("loss", loss, "stats", sess.stats(), flush=True)
+        expect = math.log(cfg.vocab) + 0.0002 * cfg.hidden
+        assert abs(loss - expect) < 0.05
+        for g, a in sess.grad.items():
+            assert np.all(np.isfinite(a)), g
+            assert np.any(a != 0), g
     finally:
         sess.close()
