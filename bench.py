@@ -137,7 +137,7 @@ def block_gemm_shapes(cfg):
     qd, kvd = cfg.n_heads * cfg.head_dim, cfg.n_kv_heads * cfg.head_dim
     ldq = qd + 2 * kvd
     NT, NN, TN = mt.MT_GEMM_NT, mt.MT_GEMM_NN, mt.MT_GEMM_TN
-    return [("gemm_nt_bf16 qkv", NT, mt.MT_EPI_BF16, T, ldq, h),
+    return [("gemm_nt_rope qkv", NT, mt.MT_EPI_ROPE, T, ldq, h),
             ("gemm_nt_resid o", NT, mt.MT_EPI_F32_RESID, T, h, qd),
             ("gemm_nt_swiglu gate/up", NT, mt.MT_EPI_SWIGLU, T, F, h),
             ("gemm_nt_resid down", NT, mt.MT_EPI_F32_RESID, T, h, F),
@@ -151,6 +151,35 @@ def block_gemm_shapes(cfg):
             ("gemm_nn_f32 dn1", NN, mt.MT_EPI_F32, T, h, ldq)]
 
 
+def head_gemm_shapes(cfg, sess_req=None):
+    """The LM head's weight-gradient product of one vocabulary chunk."""
+    import host_memory_centric_stateless_amd as mt
+    T, h = cfg.micro_batch * cfg.seq_len, cfg.hidden
+    nch = sess_req.head_chunks if sess_req else 1
+    rows = min(cfg.vocab, ((cfg.vocab + nch - 1) // nch + 255) // 256 * 256)
+    return [("gemm_tn_bf16 dWhead", mt.MT_GEMM_TN, mt.MT_EPI_BF16, rows, h, T)]
+
+
+def mfma_ceiling(iters: int = 2000, workgroups: int = 2048):
+    """The MFMA rate of a chain of register-operand MFMAs (mtk_mfma_peak),
+    with its output checked: the ceiling next to the nominal peak."""
+    import torch
+    import host_memory_centric_stateless_amd as mt
+    out = torch.zeros(workgroups * 4, dtype=torch.float32, device="cuda:0")
+    mt.mtk_mfma_peak(out, workgroups, 10)  # warm-up
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    mt.mtk_mfma_peak(out, workgroups, iters)
+    e1.record()
+    e1.synchronize()
+    ms = e0.elapsed_time(e1)
+    ok = bool(torch.all(out == 8 * 16 * iters).item())
+    flop = workgroups * 4 * 8 * iters * 32768.0
+    return {"kernel": "mfma_peak (v_mfma_f32_32x32x16_bf16 chains, register operands)",
+            "ms": ms, "TFLOPs": flop / ms / 1e9, "frac_of_nominal": flop / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS,
+            "output_checked": ok, "workgroups": workgroups, "iters": iters}
+
+
 def probe(cfg, reps: int = 2):
     """Run every block GEMM at this shape `reps` times, then a device copy of
     known size (the calibration reference for hardware byte counters), one
@@ -159,15 +188,21 @@ def probe(cfg, reps: int = 2):
     import host_memory_centric_stateless_amd as mt
     dev = torch.device("cuda:0")
     g = torch.Generator(device="cpu").manual_seed(7)
-    out = []
-    for name, lay, epi, M, N, K in block_gemm_shapes(cfg):
+    out = [mfma_ceiling()]
+    T = cfg.micro_batch * cfg.seq_len
+    cos, sin = mt.mt_host_rope_table(cfg.seq_len, cfg.head_dim, cfg.rope_base)
+    cos_d, sin_d = torch.from_numpy(cos).to(dev), torch.from_numpy(sin).to(dev)
+    from host_memory_centric_stateless_amd import make_config, mt_device_requirements
+    req = mt_device_requirements(make_config(cfg))
+    for name, lay, epi, M, N, K in block_gemm_shapes(cfg) + head_gemm_shapes(cfg, req):
         NN_ = 2 * N if epi == mt.MT_EPI_SWIGLU else N
         A = (torch.randn(M if lay != mt.MT_GEMM_TN else K, K if lay != mt.MT_GEMM_TN else M,
                          generator=g) * 0.5).to(torch.bfloat16).to(dev)
         B = (torch.randn(NN_ if lay == mt.MT_GEMM_NT else K, K if lay == mt.MT_GEMM_NT else NN_,
                          generator=g) * 0.02).to(torch.bfloat16).to(dev)
         lda, ldb = A.shape[1], B.shape[1]
-        ob = 2 if epi in (mt.MT_EPI_BF16, mt.MT_EPI_SWIGLU, mt.MT_EPI_SWIGLU_BWD) else 4
+        ob = 2 if epi in (mt.MT_EPI_BF16, mt.MT_EPI_SWIGLU, mt.MT_EPI_SWIGLU_BWD,
+                          mt.MT_EPI_ROPE) else 4
         ldc = 2 * N if epi == mt.MT_EPI_SWIGLU_BWD else N
         C = torch.empty(M * ldc * ob, dtype=torch.uint8, device=dev)
         R = torch.zeros(M, N, dtype=torch.float32, device=dev) if epi == mt.MT_EPI_F32_RESID else None
@@ -175,6 +210,9 @@ def probe(cfg, reps: int = 2):
             if epi in (mt.MT_EPI_SWIGLU, mt.MT_EPI_SWIGLU_BWD) else None
         kw = dict(R=R, ldr=N if R is not None else 0, gu=gu, ldgu=2 * N if gu is not None else 0,
                   ffn=N if gu is not None else 0)
+        if epi == mt.MT_EPI_ROPE:
+            kw.update(rope_cos=cos_d, rope_sin=sin_d, rope_seq=cfg.seq_len, rope_dim=cfg.head_dim,
+                      rope_cols=(cfg.n_heads + cfg.n_kv_heads) * cfg.head_dim)
         for _ in range(reps):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
@@ -428,6 +466,7 @@ def main():
     adamw_s = (s1["adamw_s"] - s0["adamw_s"]) / args.steps
 
     gemm = time_dominant_gemm(sess)
+    ceiling = mfma_ceiling()
     link = link_roofline(sess.req.weight_buf)
     host = host_roofline()
     # host bytes per parameter and step: the last micro-batch's fused add + AdamW +
@@ -460,6 +499,8 @@ def main():
                     "frac": ach / HBM_PEAK_GBPS}
     traffic = measured_traffic(dom["name"], cfg.name,
                                not (args.micro_batch or args.grad_accum or args.grad_slabs))
+    if roofline["bound"] == "mfma":
+        roofline["frac_of_measured_ceiling"] = roofline["achieved"] / ceiling["TFLOPs"]
     roofline.update({"traffic": traffic, "kernel": dom["name"], "launches": dom["launches"],
                      "avg_launch_ms": dom["ms"] / dom["launches"],
                      "algorithmic_per_launch": (dom["flop"] or dom["bytes"]) / dom["launches"],
@@ -584,6 +625,7 @@ def main():
         "overlap": overlap(s0, s1),
         "roofline": roofline, "kernels": kernels,
         "isolated_swiglu_gemm": {"TFLOPs": gemm["tflops"], "ms": gemm["ms"], "shape_MNK": gemm["shape"]},
+        "mfma_ceiling": ceiling,
         "layer_major": layer_major,
         "fp32_slabs": fp32_slabs,
         "cpu_baseline": base,

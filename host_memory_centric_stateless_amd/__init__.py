@@ -154,6 +154,7 @@ _SIGS = {
                                C.c_int),
     "mtk_cross_entropy": ([_P, _I64, _P, _I64, _I32, _F, _I64, _P, _I64, _P, _P, _P], C.c_int),
     "mtk_copy": ([_P, _P, C.c_size_t, _I32, _P], C.c_int),
+    "mtk_mfma_peak": ([_P, _I32, _I32, _P], C.c_int),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -399,6 +400,10 @@ def mtk_cross_entropy(logits, ld, labels, T, V, grad_scale, n_valid, dlogits, ld
     _check(_lib.mtk_cross_entropy(_ptr(logits), ld, _ptr(labels), T, V, grad_scale, n_valid,
                                   _ptr(dlogits), ld_d, _ptr(loss_rows), _ptr(loss_out),
                                   _stream(stream)), "mtk_cross_entropy")
+
+
+def mtk_mfma_peak(out, workgroups, iters, stream=None):
+    _check(_lib.mtk_mfma_peak(_ptr(out), workgroups, iters, _stream(stream)), "mtk_mfma_peak")
 
 
 def mtk_copy(dst, src, nbytes, workgroups, stream=None):
