@@ -27,6 +27,7 @@ Modules:
   layout   -- flat per-group layout, pack/unpack (lqnn 三.1)
   model    -- block / head / embedding forward and analytic backward, whole-model
               and streamed-with-recompute drivers (zhichai D2, D3; lqnn 三.4)
+  moe      -- mixture-of-experts feed-forward, the second structure group (lqnn 四)
   adamw    -- decoupled AdamW on fp32 host state (zhichai D1; lqnn 二)
   accounting -- host-state byte counts (zhichai intro; travelaiplan 核心功能 1)
 """

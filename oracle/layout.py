@@ -8,7 +8,11 @@ host memory linear in the parameter count).
 Reading of the layout (the pages give no element order): tensors of a group
 follow the block's data flow -- attn_norm, wq, wk, wv, wo, mlp_norm, w_gate,
 w_up, w_down; the head group is final_norm, w_head; the embedding group is
-emb.  Matrices are row-major [out, in].  Every tensor starts at a multiple of
+emb.  A mixture-of-experts block (its own structure group, lqnn 四: layers are
+grouped by parameter structure, MoE layers forming their own group) holds
+attn_norm .. mlp_norm, then w_router [E, h], w_gu [E * 2F_e, h] (expert e's
+gate rows, then its up rows) and w_down [E * h, F_e] (expert e's [h, F_e]).
+Matrices are row-major [out, in].  Every tensor starts at a multiple of
 256 elements and the flat length is rounded up to 256, so fp32 host arrays,
 bf16 working copies and fp32 gradient slabs share one set of element offsets.
 """
@@ -36,6 +40,12 @@ def group_shapes(cfg, group: int) -> List[Tuple[str, Tuple[int, ...]]]:
     if group == HEAD:
         return [("final_norm", (h,)), ("w_head", (V, h))]
     assert 0 <= group < cfg.n_layers
+    if getattr(cfg, "n_experts", 0) > 0 and group % cfg.moe_every == cfg.moe_every - 1:
+        # a mixture-of-experts block: its own parameter structure (lqnn 四)
+        E, Fe = cfg.n_experts, cfg.expert_ffn
+        return [("attn_norm", (h,)), ("wq", (qd, h)), ("wk", (kvd, h)), ("wv", (kvd, h)),
+                ("wo", (h, qd)), ("mlp_norm", (h,)), ("w_router", (E, h)),
+                ("w_gu", (E * 2 * Fe, h)), ("w_down", (E * h, Fe))]
     return [("attn_norm", (h,)), ("wq", (qd, h)), ("wk", (kvd, h)), ("wv", (kvd, h)),
             ("wo", (h, qd)), ("mlp_norm", (h,)), ("w_gate", (F, h)), ("w_up", (F, h)),
             ("w_down", (h, F))]

@@ -194,11 +194,16 @@ def block_forward(W: Dict[str, np.ndarray], x: np.ndarray, cfg, cos, sin, batch:
     o = attention(qr, kr, v).reshape(T, nq * d)
     h1 = x + o @ W["wo"].T
     n2, r2 = rmsnorm(h1, W["mlp_norm"], cfg.rms_eps)
+    cache = dict(x=x, n1=n1, r1=r1, qr=qr, kr=kr, v=v, o=o, h1=h1, n2=n2, r2=r2)
+    if "w_router" in W:  # a mixture-of-experts block (oracle.moe)
+        from . import moe
+        f, cache["moe"] = moe.ffn_forward(W, n2, cfg)
+        return h1 + f, cache
     a = n2 @ W["w_gate"].T
     u = n2 @ W["w_up"].T
     m = swiglu(a, u)
     y = h1 + m @ W["w_down"].T
-    cache = dict(x=x, n1=n1, r1=r1, qr=qr, kr=kr, v=v, o=o, h1=h1, n2=n2, r2=r2, a=a, u=u, m=m)
+    cache.update(a=a, u=u, m=m)
     return y, cache
 
 
@@ -209,12 +214,17 @@ def block_backward(W: Dict[str, np.ndarray], c: Dict[str, np.ndarray], dy: np.nd
     s = T // batch
     nq, nkv, d = cfg.n_heads, cfg.n_kv_heads, cfg.head_dim
     g: Dict[str, np.ndarray] = {}
-    g["w_down"] = dy.T @ c["m"]
-    dm = dy @ W["w_down"]
-    da, du = swiglu_bwd(dm, c["a"], c["u"])
-    g["w_gate"] = da.T @ c["n2"]
-    g["w_up"] = du.T @ c["n2"]
-    dn2 = da @ W["w_gate"] + du @ W["w_up"]
+    if "w_router" in W:
+        from . import moe
+        dn2, gm = moe.ffn_backward(W, c["moe"], dy, cfg)
+        g.update(gm)
+    else:
+        g["w_down"] = dy.T @ c["m"]
+        dm = dy @ W["w_down"]
+        da, du = swiglu_bwd(dm, c["a"], c["u"])
+        g["w_gate"] = da.T @ c["n2"]
+        g["w_up"] = du.T @ c["n2"]
+        dn2 = da @ W["w_gate"] + du @ W["w_up"]
     dh1n, g["mlp_norm"] = rmsnorm_bwd(dn2, c["h1"], c["r2"], W["mlp_norm"])
     dh1 = dy + dh1n
     g["wo"] = dh1.T @ c["o"]

@@ -47,6 +47,15 @@ class ModelConfig:
     rope_base: float = 10000.0
     lr: float = 1e-3
     steps: int = 3
+    # mixture-of-experts blocks (a second parameter-structure group): block l is
+    # an MoE block when n_experts > 0 and l % moe_every == moe_every - 1
+    n_experts: int = 0
+    top_k: int = 2
+    expert_ffn: int = 0
+    moe_every: int = 1
+
+    def is_moe(self, layer: int) -> bool:
+        return self.n_experts > 0 and layer % self.moe_every == self.moe_every - 1
 
     @property
     def tokens_per_microbatch(self) -> int:
@@ -80,6 +89,19 @@ PRESETS: Dict[str, ModelConfig] = {
 
 # Tiny GQA shape used for finite-difference checks of the oracle.
 FD_TINY = ModelConfig("fd-tiny-gqa", 2, 16, 4, 2, 4, 24, 32, 2, 8, grad_accum=1, ckpt_interval=1)
+# The same with its second block a mixture of 4 experts (top 2) of width 12.
+FD_TINY_MOE = FD_TINY.replace(name="fd-tiny-moe", n_experts=4, top_k=2, expert_ffn=12, moe_every=2)
+
+# Mixture-of-experts shapes (the pages' second structure group): the tiny
+# decoder with every second block an MoE of 8 experts (top 2, expert width
+# 256), and a small one at hidden 1024.
+MOE_PRESETS: Dict[str, ModelConfig] = {
+    "M1": PRESETS["C1"].replace(name="tiny-moe-2L-h256-e8", n_experts=8, top_k=2, expert_ffn=256,
+                                moe_every=2),
+    "M2": PRESETS["C2"].replace(name="small-moe-4L-h1024-e8", n_layers=4, micro_batch=2,
+                                n_experts=8, top_k=2, expert_ffn=1408, moe_every=2,
+                                ckpt_interval=2),
+}
 
 
 def tensor_specs(cfg: ModelConfig, group: int) -> List[Tuple[str, Tuple[int, ...], str]]:
@@ -97,6 +119,19 @@ def tensor_specs(cfg: ModelConfig, group: int) -> List[Tuple[str, Tuple[int, ...
         return [("final_norm", (h,), "gain"), ("w_head", (V, h), "matrix")]
     if not 0 <= group < cfg.n_layers:
         raise ValueError(f"group {group} out of range")
+    if cfg.is_moe(group):
+        E, Fe = cfg.n_experts, cfg.expert_ffn
+        return [
+            ("attn_norm", (h,), "gain"),
+            ("wq", (qd, h), "matrix"),
+            ("wk", (kvd, h), "matrix"),
+            ("wv", (kvd, h), "matrix"),
+            ("wo", (h, qd), "matrix"),
+            ("mlp_norm", (h,), "gain"),
+            ("w_router", (E, h), "matrix"),
+            ("w_gu", (E * 2 * Fe, h), "matrix"),   # expert e: gate rows, then up rows
+            ("w_down", (E * h, Fe), "matrix"),     # expert e: rows e*h .. e*h + h - 1
+        ]
     return [
         ("attn_norm", (h,), "gain"),
         ("wq", (qd, h), "matrix"),

@@ -117,3 +117,73 @@ def test_planted_accumulation_mistake_is_caught(mutation):
     finally:
         TR.train_step = orig
     assert failed, f"no pin caught {mutation}"
+
+
+# ---------------------------------------------------- mixture-of-experts block
+import oracle.moe as MOE
+import tests.test_oracle_moe as TM
+
+_moe_orig = {n: getattr(MOE, n) for n in ["route", "ffn_backward", "expert_weights"]}
+
+
+def _route_smallest(n2, w_router, k):
+    r, sel, g = _moe_orig["route"](n2, w_router, k)
+    sel2 = np.argsort(r, axis=1, kind="stable")[:, :k]
+    sl = np.take_along_axis(r, sel2, axis=1)
+    z = np.exp(sl - sl.max(axis=1, keepdims=True))
+    return r, sel2, z / z.sum(axis=1, keepdims=True)
+
+
+def _route_unnormalised(n2, w_router, k):
+    r, sel, g = _moe_orig["route"](n2, w_router, k)
+    return r, sel, np.exp(np.take_along_axis(r, sel, axis=1))
+
+
+def _bwd_no_softmax_projection(W, c, df, cfg):
+    # dr = g * dg instead of g * (dg - sum g dg): re-derive with a patched gate grad
+    dn2, grads = _moe_orig["ffn_backward"](W, c, df, cfg)
+    T = df.shape[0]
+    g, sel = c["g"], c["sel"]
+    dg = np.zeros_like(g)
+    h = df.shape[1]
+    for e in range(cfg.n_experts):
+        p = c["per"][e]
+        dg[p["tok"], p["slot"]] = np.sum(df[p["tok"]] * p["o"], axis=1)
+    right = g * (dg - np.sum(g * dg, axis=1, keepdims=True))
+    wrong = g * dg
+    dr_r, dr_w = np.zeros((T, cfg.n_experts)), np.zeros((T, cfg.n_experts))
+    np.put_along_axis(dr_r, sel, right, axis=1)
+    np.put_along_axis(dr_w, sel, wrong, axis=1)
+    grads["w_router"] = dr_w.T @ c["n2"]
+    return dn2 - dr_r @ W["w_router"] + dr_w @ W["w_router"], grads
+
+
+def _experts_shifted(W, e, h, Fe):
+    return _moe_orig["expert_weights"](W, (e + 1) % (W["w_router"].shape[0]), h, Fe)
+
+
+MOE_MUTATIONS = {
+    "moe_selects_smallest_logits": ("route", _route_smallest),
+    "moe_gates_not_normalised": ("route", _route_unnormalised),
+    "moe_softmax_backward_projection_dropped": ("ffn_backward", _bwd_no_softmax_projection),
+    "moe_wrong_expert_weights": ("expert_weights", _experts_shifted),
+}
+MOE_PINS = ["test_fd_directional_all_params_with_moe", "test_equal_experts_reduce_to_dense_swiglu",
+            "test_top_k_equal_to_e_is_the_softmax_mixture", "test_routing_and_combine_brute_force",
+            "test_moe_matches_torch_autograd_float64"]
+
+
+@pytest.mark.parametrize("mutation", sorted(MOE_MUTATIONS))
+def test_planted_moe_mistake_is_caught(mutation):
+    attr, fn = MOE_MUTATIONS[mutation]
+    failed = []
+    setattr(MOE, attr, fn)
+    try:
+        for name in MOE_PINS:
+            try:
+                getattr(TM, name)()
+            except Exception:
+                failed.append(name)
+    finally:
+        setattr(MOE, attr, _moe_orig[attr])
+    assert failed, f"no pin caught {mutation}"
