@@ -57,7 +57,9 @@ class mt_config(C.Structure):
                 ("micro_batch", C.c_int32), ("seq_len", C.c_int32), ("ckpt_interval", C.c_int32),
                 ("n_grad_slabs", C.c_int32), ("host_threads", C.c_int32),
                 ("slab_bf16", C.c_int32), ("drain_workgroups", C.c_int32),
-                ("micro_batches_per_pass", C.c_int32), ("head_token_chunk", C.c_int32)]
+                ("micro_batches_per_pass", C.c_int32), ("head_token_chunk", C.c_int32),
+                ("n_experts", C.c_int32), ("top_k", C.c_int32), ("expert_ffn", C.c_int32),
+                ("moe_every", C.c_int32)]
 
 
 class mt_tensor_desc(C.Structure):
@@ -110,7 +112,9 @@ class mt_gemm_args(C.Structure):
                 ("B", C.c_void_p), ("ldb", C.c_int64), ("C", C.c_void_p), ("ldc", C.c_int64),
                 ("R", C.c_void_p), ("ldr", C.c_int64), ("gu", C.c_void_p), ("ldgu", C.c_int64),
                 ("ffn", C.c_int64), ("rope_cos", C.c_void_p), ("rope_sin", C.c_void_p),
-                ("rope_cols", C.c_int64), ("rope_seq", C.c_int32), ("rope_dim", C.c_int32)]
+                ("rope_cols", C.c_int64), ("rope_seq", C.c_int32), ("rope_dim", C.c_int32),
+                ("group_off", C.c_void_p), ("groups", C.c_int32), ("group_reserved", C.c_int32),
+                ("group_stride_b", C.c_int64), ("group_stride_c", C.c_int64)]
 
 
 _P = C.c_void_p
@@ -127,6 +131,7 @@ _SIGS = {
     "mt_flush_grads": ([_P], C.c_int),
     "mt_sync_loss": ([_P], C.c_int),
     "mt_step_loss": ([_P, C.POINTER(C.c_float)], C.c_int),
+    "mt_moe_routing": ([_P, _I32, _P], C.c_int),
     "mt_adamw_step": ([_P, C.POINTER(mt_adamw_hparams), _I64], C.c_int),
     "mt_get_stats": ([_P, C.POINTER(mt_stats)], C.c_int),
     "mt_last_error": ([_P], C.c_char_p),
@@ -201,7 +206,9 @@ def make_config(cfg, host_threads: int = 0, slab_bf16: bool = True,
     return mt_config(cfg.n_layers, cfg.hidden, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ffn,
                      cfg.vocab, cfg.rms_eps, cfg.rope_base, cfg.micro_batch, cfg.seq_len,
                      cfg.ckpt_interval, cfg.n_grad_slabs, host_threads, int(bool(slab_bf16)),
-                     int(drain_workgroups), int(micro_batches_per_pass), int(head_token_chunk))
+                     int(drain_workgroups), int(micro_batches_per_pass), int(head_token_chunk),
+                     int(getattr(cfg, "n_experts", 0)), int(getattr(cfg, "top_k", 2)),
+                     int(getattr(cfg, "expert_ffn", 0)), int(getattr(cfg, "moe_every", 1)))
 
 
 # ------------------------------------------------------------- C-ABI calls
@@ -259,6 +266,12 @@ def mt_step_loss(ctx) -> float:
     out = C.c_float()
     _check(_lib.mt_step_loss(ctx, C.byref(out)), "mt_step_loss", ctx)
     return out.value
+
+
+def mt_moe_routing(ctx, layer: int, tokens: int, top_k: int) -> np.ndarray:
+    out = np.empty((tokens, top_k), np.int32)
+    _check(_lib.mt_moe_routing(ctx, layer, _ptr(out)), "mt_moe_routing", ctx)
+    return out
 
 
 def mt_adamw_step(ctx, hp: mt_adamw_hparams, step: int):
@@ -333,10 +346,11 @@ def mt_host_rope_table(seq_len: int, head_dim: int, base: float):
 # -------------------------------------------------------- kernel entry points
 def mtk_gemm(layout, epilogue, M, N, K, A, lda, B, ldb, Cm, ldc, R=None, ldr=0, gu=None, ldgu=0,
              ffn=0, stream=None, rope_cos=None, rope_sin=None, rope_cols=0, rope_seq=0,
-             rope_dim=0):
+             rope_dim=0, group_off=None, groups=0, group_stride_b=0, group_stride_c=0):
     a = mt_gemm_args(layout, epilogue, M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(Cm), ldc,
                      _ptr(R), ldr, _ptr(gu), ldgu, ffn, _ptr(rope_cos), _ptr(rope_sin), rope_cols,
-                     rope_seq, rope_dim)
+                     rope_seq, rope_dim, _ptr(group_off), groups, 0, group_stride_b,
+                     group_stride_c)
     _check(_lib.mtk_gemm(C.byref(a), _stream(stream)), "mtk_gemm")
 
 

@@ -45,6 +45,7 @@
 #include <atomic>
 #include <chrono>
 #include <deque>
+#include <functional>
 #include <map>
 #include <memory>
 #include <string>
@@ -52,6 +53,7 @@
 
 #include "common.h"
 #include "host_ops.h"
+#include "moe.h"
 #include "plan.h"
 
 using namespace mt;
@@ -305,7 +307,7 @@ struct mt_ctx {
     const int L = p.c.n_layers;
     if (u < L) {
       *src = layers[u].pinned;
-      *n = p.layer_elems;
+      *n = p.block_elems(u);
     } else {
       const int c = u - L;
       *src = head.pinned + p.chunk_e0[c];
@@ -335,6 +337,12 @@ struct Acts {
   uint16_t* n2;
   uint16_t* gu;
   uint16_t* m;
+  // mixture-of-experts blocks
+  float* mlog;
+  int32_t *msel, *mpos, *moff, *mrowtok;
+  float* mgate;
+  uint16_t *mx, *mgu, *mm;
+  float* myo;
 };
 
 Acts acts_of(mt_ctx* c, int w, float* x) {
@@ -350,7 +358,17 @@ Acts acts_of(mt_ctx* c, int w, float* x) {
               reinterpret_cast<float*>(b + s.rstd2),
               reinterpret_cast<uint16_t*>(b + s.n2),
               reinterpret_cast<uint16_t*>(b + s.gu),
-              reinterpret_cast<uint16_t*>(b + s.m)};
+              reinterpret_cast<uint16_t*>(b + s.m),
+              reinterpret_cast<float*>(b + s.mlog),
+              reinterpret_cast<int32_t*>(b + s.msel),
+              reinterpret_cast<int32_t*>(b + s.mpos),
+              reinterpret_cast<int32_t*>(b + s.moff),
+              reinterpret_cast<int32_t*>(b + s.mrowtok),
+              reinterpret_cast<float*>(b + s.mgate),
+              reinterpret_cast<uint16_t*>(b + s.mx),
+              reinterpret_cast<uint16_t*>(b + s.mgu),
+              reinterpret_cast<uint16_t*>(b + s.mm),
+              reinterpret_cast<float*>(b + s.myo)};
 }
 
 // Records timing events around one launch when mt_kernel_timing is on.
@@ -408,6 +426,26 @@ hipError_t gemm_qkv_rope(mt_ctx* c, hipStream_t s, int64_t T, const uint16_t* n1
   return launch_gemm(a, s);
 }
 
+// A grouped product over the experts of an MoE block (one launch): rows of
+// the expert-major row space belong to experts by off[] (device); the
+// algorithmic work counts the real token-expert pairs, not the padding.
+hipError_t gemm_grouped(mt_ctx* c, hipStream_t s, int layout, int epi, int64_t M, int64_t N,
+                        int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                        void* C, int64_t ldc, const int32_t* off, int64_t stride_b,
+                        int64_t stride_c, uint16_t* gu = nullptr, int64_t ldgu = 0,
+                        int64_t ffn = 0) {
+  const Plan& p = c->p;
+  mt_gemm_args a{layout, epi, M, N, K, A, lda, B, ldb, C, ldc, nullptr, 0, gu, ldgu, ffn,
+                 nullptr, nullptr, 0, 0, 0, off, p.c.n_experts, 0, stride_b, stride_c};
+  const double pairs = (double)p.T * p.c.top_k;
+  const double nn = (epi == MT_EPI_SWIGLU) ? 2.0 * N : (double)N;
+  const double work = layout == MT_GEMM_TN ? 2.0 * M * N * pairs : 2.0 * pairs * nn * K;
+  KScope k(c, s, layout == MT_GEMM_TN ? "gemm_tn_grouped" : layout == MT_GEMM_NN
+                                                             ? "gemm_nn_grouped" : "gemm_nt_grouped",
+           work, 0);
+  return launch_gemm(a, s);
+}
+
 // Algorithmic work of the other kernels.
 double attn_pairs(const mt_config& g) {
   return (double)g.micro_batch * g.micro_batches_per_pass * g.n_heads * 0.5 * (double)g.seq_len *
@@ -422,12 +460,14 @@ double attn_pairs(const mt_config& g) {
 
 // One decoder block forward on weights W (flat bf16 layer).  y == nullptr
 // skips the down projection (its output is not needed).
-hipError_t block_forward(mt_ctx* c, const uint16_t* W, const Acts& a, float* y) {
+hipError_t moe_forward(mt_ctx* c, const uint16_t* W, const Acts& a, float* y, int layer);
+
+hipError_t block_forward(mt_ctx* c, const uint16_t* W, const Acts& a, float* y, int layer) {
   const Plan& p = c->p;
   const mt_config& g = p.c;
   const int64_t T = p.T, h = g.hidden, F = g.ffn;
   hipStream_t s = c->sc;
-  const TensorOff* L = p.layer;
+  const TensorOff* L = p.block_layout(layer);
   const double nb_fwd = (double)T * h * 6 + h * 2 + T * 4;   // rmsnorm: x in, bf16 out
   {
     KScope k(c, s, "rmsnorm_fwd", 0, nb_fwd);
@@ -445,6 +485,7 @@ hipError_t block_forward(mt_ctx* c, const uint16_t* W, const Acts& a, float* y) 
     KScope k(c, s, "rmsnorm_fwd", 0, nb_fwd);
     CK(launch_rmsnorm_fwd(a.h1, W + L[T_MLP_NORM].off, a.n2, a.rstd2, T, (int)h, g.rms_eps, s));
   }
+  if (p.is_moe(layer)) return moe_forward(c, W, a, y, layer);
   CK(gemm(c, s, MT_GEMM_NT, MT_EPI_SWIGLU, T, F, h, a.n2, h, W + L[T_WGATE].off, h, a.m, F, nullptr,
           0, a.gu, 2 * F, F));
   if (y)
@@ -453,16 +494,87 @@ hipError_t block_forward(mt_ctx* c, const uint16_t* W, const Acts& a, float* y) 
   return hipSuccess;
 }
 
+// FFN of a mixture-of-experts block (after n2): router logits, top-k and
+// gates, the expert-major row plan, the experts' SwiGLU and down products as
+// grouped GEMMs, and (y != nullptr) y = h1 + sum_j g_j expert_j(n2).  The
+// expert outputs are kept in the window even when y is not needed: the
+// gates' backward reads them.
+hipError_t moe_forward(mt_ctx* c, const uint16_t* W, const Acts& a, float* y, int layer) {
+  const Plan& p = c->p;
+  const mt_config& g = p.c;
+  const int64_t T = p.T, h = g.hidden, Fe = g.expert_ffn, R = p.moe_rows;
+  const int E = g.n_experts, k = g.top_k;
+  hipStream_t s = c->sc;
+  const TensorOff* Mo = p.moe;
+  CK(gemm(c, s, MT_GEMM_NT, MT_EPI_F32, T, E, h, a.n2, h, W + Mo[M_ROUTER].off, h, a.mlog, E));
+  {
+    KScope ks(c, s, "moe_route", 0, (double)T * (E * 4 + k * 8) + (double)R * h * 4);
+    CK(launch_moe_route(a.mlog, E, T, E, k, a.msel, a.mgate, s));
+    // keep this block's selection for mt_moe_routing (a recompute writes the same)
+    CK(launch_copy(c->wsp<int32_t>(p.ws.mroute) + (int64_t)(layer / g.moe_every) * T * k, a.msel,
+                   (size_t)T * k * 4, 8, s));
+    CK(launch_moe_plan(a.msel, T, E, k, a.moff, a.mpos, a.mrowtok, s));
+    CK(launch_moe_gather(a.n2, (int)h, a.mrowtok, a.moff, E, R, a.mx, s));
+  }
+  CK(gemm_grouped(c, s, MT_GEMM_NT, MT_EPI_SWIGLU, R, Fe, h, a.mx, h, W + Mo[M_GU].off, h, a.mm, Fe,
+                  a.moff, 2 * Fe * h, 0, a.mgu, 2 * Fe, Fe));
+  CK(gemm_grouped(c, s, MT_GEMM_NT, MT_EPI_F32, R, h, Fe, a.mm, Fe, W + Mo[M_DOWN].off, Fe, a.myo,
+                  h, a.moff, h * Fe, 0));
+  if (y) {
+    KScope ks(c, s, "moe_combine", 0, (double)T * h * 8 + (double)T * k * h * 4);
+    CK(launch_moe_combine(a.h1, a.myo, a.mpos, a.mgate, k, (int)h, T, y, s));
+  }
+  return hipSuccess;
+}
+
+// Backward of the mixture-of-experts FFN down to dn (the gradient of n2):
+// gates and combine, the experts' products (grouped), their weight gradients
+// into the slab, the router's.
+hipError_t moe_backward(mt_ctx* c, const uint16_t* W, const Acts& a, const float* dy, float* dn,
+                        const std::function<void*(int)>& slab, int wepi) {
+  const Plan& p = c->p;
+  const mt_config& g = p.c;
+  const int64_t T = p.T, h = g.hidden, Fe = g.expert_ffn, R = p.moe_rows, ldl = p.moe_ldl;
+  const int E = g.n_experts, k = g.top_k;
+  hipStream_t s = c->sc;
+  const TensorOff* Mo = p.moe;
+  uint16_t* dout = c->wsp<uint16_t>(p.ws.mdout);
+  float* dX = c->wsp<float>(p.ws.mdx);
+  uint16_t* dlog = c->wsp<uint16_t>(p.ws.mdlog);
+  uint16_t* dgu = c->wsp<uint16_t>(p.ws.dgu);
+  {
+    KScope ks(c, s, "moe_route_bwd", 0, (double)T * h * 4 + (double)T * k * h * 6);
+    CK(launch_moe_bwd_gates(dy, a.myo, a.mpos, a.msel, a.mgate, k, E, (int)h, T, dout, dlog, ldl,
+                            s));
+    CK(launch_moe_zero_pad(a.mrowtok, a.moff, E, (int)h, R, dout, s));
+  }
+  CK(gemm_grouped(c, s, MT_GEMM_NN, MT_EPI_SWIGLU_BWD, R, Fe, h, dout, h, W + Mo[M_DOWN].off, Fe,
+                  dgu, 2 * Fe, a.moff, h * Fe, 0, a.mgu, 2 * Fe, Fe));
+  CK(gemm_grouped(c, s, MT_GEMM_TN, wepi, h, Fe, R, dout, h, a.mm, Fe, slab(M_DOWN), Fe, a.moff, 0,
+                  h * Fe));
+  CK(gemm_grouped(c, s, MT_GEMM_TN, wepi, 2 * Fe, h, R, dgu, 2 * Fe, a.mx, h, slab(M_GU), h, a.moff,
+                  0, 2 * Fe * h));
+  CK(gemm_grouped(c, s, MT_GEMM_NN, MT_EPI_F32, R, h, 2 * Fe, dgu, 2 * Fe, W + Mo[M_GU].off, h, dX,
+                  h, a.moff, 2 * Fe * h, 0));
+  CK(gemm(c, s, MT_GEMM_TN, wepi, E, h, T, dlog, ldl, a.n2, h, slab(M_ROUTER), h));
+  {
+    KScope ks(c, s, "moe_combine", 0, (double)T * k * h * 4 + (double)T * h * 4);
+    CK(launch_moe_bwd_combine(dX, a.mpos, k, (int)h, T, dn, s));
+  }
+  CK(gemm(c, s, MT_GEMM_NN, MT_EPI_F32_ACCUM, T, h, E, dlog, ldl, W + Mo[M_ROUTER].off, h, dn, h));
+  return hipSuccess;
+}
+
 // One decoder block backward.  dy/dyb: gradient of the block output (fp32 and
 // bf16); writes dx/dxb (gradient of the block input) and every weight
 // gradient into `slab` at the layer's flat offsets.
 hipError_t block_backward(mt_ctx* c, const uint16_t* W, const Acts& a, const float* dy,
-                          uint16_t* dyb, float* dx, void* slab_base) {
+                          uint16_t* dyb, float* dx, void* slab_base, int layer) {
   const Plan& p = c->p;
   const mt_config& g = p.c;
   const int64_t T = p.T, h = g.hidden, F = g.ffn;
   hipStream_t s = c->sc;
-  const TensorOff* L = p.layer;
+  const TensorOff* L = p.block_layout(layer);
   uint16_t* dgu = c->wsp<uint16_t>(p.ws.dgu);
   float* dn = c->wsp<float>(p.ws.dn);
   float* dh1 = c->wsp<float>(p.ws.dh1);
@@ -473,17 +585,21 @@ hipError_t block_backward(mt_ctx* c, const uint16_t* W, const Acts& a, const flo
   // weight gradients land in the slab at the layer's flat offsets, fp32 or bf16
   const bool sb = p.slab_bf16;
   const int wepi = sb ? MT_EPI_BF16 : MT_EPI_F32;
-  auto slab = [&](int t) -> void* {
+  const std::function<void*(int)> slab = [&](int t) -> void* {
     return static_cast<uint8_t*>(slab_base) + (size_t)L[t].off * (sb ? 2 : 4);
   };
   auto dg32 = [&](int t) { return sb ? nullptr : static_cast<float*>(slab(t)); };
   auto dg16 = [&](int t) { return sb ? static_cast<uint16_t*>(slab(t)) : nullptr; };
-  // MLP: dm = dy Wd, fused SwiGLU backward -> dgu = [da | du]
-  CK(gemm(c, s, MT_GEMM_NN, MT_EPI_SWIGLU_BWD, T, F, h, dyb, h, W + L[T_WDOWN].off, F, dgu, 2 * F,
-          nullptr, 0, a.gu, 2 * F, F));
-  CK(gemm(c, s, MT_GEMM_TN, wepi, h, F, T, dyb, h, a.m, F, slab(T_WDOWN), F));
-  CK(gemm(c, s, MT_GEMM_TN, wepi, 2 * F, h, T, dgu, 2 * F, a.n2, h, slab(T_WGATE), h));
-  CK(gemm(c, s, MT_GEMM_NN, MT_EPI_F32, T, h, 2 * F, dgu, 2 * F, W + L[T_WGATE].off, h, dn, h));
+  if (p.is_moe(layer)) {
+    CK(moe_backward(c, W, a, dy, dn, slab, wepi));
+  } else {
+    // MLP: dm = dy Wd, fused SwiGLU backward -> dgu = [da | du]
+    CK(gemm(c, s, MT_GEMM_NN, MT_EPI_SWIGLU_BWD, T, F, h, dyb, h, W + L[T_WDOWN].off, F, dgu, 2 * F,
+            nullptr, 0, a.gu, 2 * F, F));
+    CK(gemm(c, s, MT_GEMM_TN, wepi, h, F, T, dyb, h, a.m, F, slab(T_WDOWN), F));
+    CK(gemm(c, s, MT_GEMM_TN, wepi, 2 * F, h, T, dgu, 2 * F, a.n2, h, slab(T_WGATE), h));
+    CK(gemm(c, s, MT_GEMM_NN, MT_EPI_F32, T, h, 2 * F, dgu, 2 * F, W + L[T_WGATE].off, h, dn, h));
+  }
   const double nb_bwd = (double)T * h * 18;  // dn, x, resid in; dx (fp32 + bf16) out
   {
     KScope k(c, s, "rmsnorm_bwd", 0, nb_bwd);
@@ -839,7 +955,7 @@ mt_status run_step(mt_ctx* c, const Step& s) {
       } else if (s.write_y) {
         y = c->slot_x(w + 1);
       }
-      MT_HIP(c, block_forward(c, W, acts_of(c, w, x), y));
+      MT_HIP(c, block_forward(c, W, acts_of(c, w, x), y, l));
       c->st.layer_forwards += 1;
       break;
     }
@@ -935,17 +1051,20 @@ mt_status run_step(mt_ctx* c, const Step& s) {
       const int sl = acquire_slab(c);
       if (sl < 0) return MT_E_ABORTED;
       void* slab = c->dslab[sl];
-      if (p.layer_elems != p.layer[T_WDOWN].off + p.layer[T_WDOWN].numel ||
-          p.layer[T_WQ].off != p.layer[T_ATTN_NORM].numel ||
-          p.layer[T_MLP_NORM].numel + p.layer[T_MLP_NORM].off != p.layer[T_WGATE].off)
-        MT_HIP(c, hipMemsetAsync(slab, 0, (size_t)p.layer_elems * (p.slab_bf16 ? 2 : 4), cs));
+      {  // padding between tensors (absent at the supported widths) must read as zero
+        const TensorOff* BL = p.block_layout(l);
+        bool gaps = BL[T_COUNT - 1].off + BL[T_COUNT - 1].numel != p.block_elems(l);
+        for (int t = 1; t < T_COUNT; ++t) gaps = gaps || BL[t].off != BL[t - 1].off + BL[t - 1].numel;
+        if (gaps)
+          MT_HIP(c, hipMemsetAsync(slab, 0, (size_t)p.block_elems(l) * (p.slab_bf16 ? 2 : 4), cs));
+      }
       float* x = (l % K == 0) ? c->ckpt_ptr(l / K) : c->slot_x(w);
       float* dy = c->wsp<float>(c->dy_idx ? p.ws.dy1 : p.ws.dy0);
       float* dx = c->wsp<float>(c->dy_idx ? p.ws.dy0 : p.ws.dy1);
-      MT_HIP(c, block_backward(c, W, acts_of(c, w, x), dy, c->wsp<uint16_t>(p.ws.dyb), dx, slab));
+      MT_HIP(c, block_backward(c, W, acts_of(c, w, x), dy, c->wsp<uint16_t>(p.ws.dyb), dx, slab, l));
       c->dy_idx ^= 1;
       c->st.layer_backwards += 1;
-      mt_status r = offload_slab(c, sl, l, 0, p.layer_elems, l);
+      mt_status r = offload_slab(c, sl, l, 0, p.block_elems(l), l);
       if (r != MT_OK) return r;
       break;
     }
@@ -1188,7 +1307,7 @@ extern "C" mt_status mt_bind_layer(mt_ctx* c, int32_t group, float* master, floa
     want = p.head_elems;
     b = &c->head;
   } else if (group >= 0 && group < p.c.n_layers) {
-    want = p.layer_elems;
+    want = p.block_elems(group);
     b = &c->layers[group];
   } else {
     return MT_E_ARG;
@@ -1370,6 +1489,18 @@ extern "C" mt_status mt_step_loss(mt_ctx* c, float* loss_out) {
   double sum = 0.0;
   for (int s : sl) sum += (double)c->loss_pin[s];
   *loss_out = (float)(sum / (double)sl.size());
+  return MT_OK;
+}
+
+extern "C" mt_status mt_moe_routing(mt_ctx* c, int32_t layer, int32_t* sel_out) {
+  mt_status r = check_live(c);
+  if (r != MT_OK) return r;
+  const Plan& p = c->p;
+  if (!sel_out || layer < 0 || layer >= p.c.n_layers || !p.is_moe(layer)) return MT_E_ARG;
+  const size_t n = (size_t)p.T * p.c.top_k;
+  MT_HIP(c, hipStreamSynchronize(c->sc));
+  MT_HIP(c, hipMemcpy(sel_out, c->wsp<int32_t>(p.ws.mroute) + (layer / p.c.moe_every) * n, n * 4,
+                      hipMemcpyDeviceToHost));
   return MT_OK;
 }
 

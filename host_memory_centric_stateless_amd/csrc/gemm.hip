@@ -667,8 +667,9 @@ __device__ inline bf16x8_t frag_tsw(const uint16_t* lds, int row_base, int ks, i
 }
 
 template <int LAYOUT, int EPI>
-__global__ __launch_bounds__(512) void gemm_direct_kernel(mt_gemm_args p, int nm, int nn) {
+__global__ __launch_bounds__(512) void gemm_direct_kernel(mt_gemm_args pa, int nm, int nn) {
   constexpr int BM = 256, BN = 256, WVM = 2, WVN = 4, NTH = 512;
+  mt_gemm_args p = pa;
   constexpr bool A_T = (LAYOUT == MT_GEMM_TN);
   constexpr bool B_T = (LAYOUT != MT_GEMM_NT);
   constexpr bool SWI = (EPI == MT_EPI_SWIGLU);
@@ -683,6 +684,24 @@ __global__ __launch_bounds__(512) void gemm_direct_kernel(mt_gemm_args p, int nm
 
   int tm, tn;
   if (!tile_of(blockIdx.x, nm, nn, tm, tn)) return;
+  if (p.groups > 0) {
+    // grouped product: this workgroup's group and its operands (uniform values)
+    if constexpr (LAYOUT == MT_GEMM_TN) {
+      const int g = blockIdx.y;
+      const int64_t r0 = p.group_off[g], r1 = p.group_off[g + 1];
+      p.A += r0 * p.lda;
+      p.B += r0 * p.ldb;
+      p.K = r1 - r0;
+      p.C = static_cast<char*>(p.C) +
+            g * p.group_stride_c * (EPI == MT_EPI_BF16 ? 2 : 4);
+    } else {
+      const int64_t mt0 = (int64_t)tm * BM;
+      if (mt0 >= p.group_off[p.groups]) return;  // past the last group's rows
+      int g = 0;
+      while (g + 1 < p.groups && p.group_off[g + 1] <= mt0) ++g;
+      p.B += g * p.group_stride_b;
+    }
+  }
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -824,13 +843,16 @@ hipError_t launch_direct(const mt_gemm_args& a, hipStream_t s) {
   const int nn = (int)((EPI == MT_EPI_SWIGLU) ? (a.N + 127) / 128 : (a.N + 255) / 256);
   const int nm = (int)((a.M + 255) / 256);
   const int per = (nm * nn + NXCD - 1) / NXCD;
-  hipLaunchKernelGGL((gemm_direct_kernel<LAYOUT, EPI>), dim3((unsigned)(per * NXCD)), dim3(512), 0,
-                     s, a, nm, nn);
+  // grouped weight-gradient products: one grid row of tiles per group
+  const unsigned gy = (a.groups > 0 && LAYOUT == MT_GEMM_TN) ? (unsigned)a.groups : 1u;
+  hipLaunchKernelGGL((gemm_direct_kernel<LAYOUT, EPI>), dim3((unsigned)(per * NXCD), gy), dim3(512),
+                     0, s, a, nm, nn);
   return hipGetLastError();
 }
 
 template <int LAYOUT, int EPI>
 hipError_t launch_one(const mt_gemm_args& a, hipStream_t s) {
+  if (a.groups > 0) return launch_direct<LAYOUT, EPI>(a, s);  // shapes checked by gemm_shape_ok
   const int64_t nbig = ((a.M + 255) / 256) * ((a.N + 255) / 256);
   if (a.M >= 1024 && a.N >= 1024 && nbig >= 128) {
     // the direct loads move 16-byte chunks: operand bases must be 16-byte aligned
@@ -857,6 +879,24 @@ bool gemm_shape_ok(const mt_gemm_args& a, const char** why) {
     return bad("C, R and gu must be 16-byte aligned");
   const bool at = a.layout == MT_GEMM_TN, bt = a.layout != MT_GEMM_NT;
   if ((at ? a.lda < a.M : a.lda < a.K) || (bt ? a.ldb < a.N : a.ldb < a.K)) return bad("lda/ldb");
+  if (a.groups != 0) {
+    // grouped products run on the direct-to-LDS kernel: 16-byte aligned
+    // operands, per-group row blocks of 256, k steps of 128
+    if (a.groups < 0 || a.groups > 64 || !a.group_off) return bad("groups / group_off");
+    if (((uintptr_t)a.A | (uintptr_t)a.B) & 15) return bad("grouped operands must be 16-byte aligned");
+    if (a.layout == MT_GEMM_TN) {
+      if (a.K % 256) return bad("grouped TN: K (row space) must be a multiple of 256");
+      if (a.epilogue != MT_EPI_BF16 && a.epilogue != MT_EPI_F32)
+        return bad("grouped TN: BF16 or F32 epilogue");
+      if (a.group_stride_c < a.M * a.ldc) return bad("group_stride_c");
+    } else {
+      if (a.M % 256 || a.K % 128) return bad("grouped NT/NN: M multiple of 256, K of 128");
+      if (a.epilogue == MT_EPI_F32_RESID || a.epilogue == MT_EPI_F32_ACCUM ||
+          a.epilogue == MT_EPI_ROPE)
+        return bad("grouped NT/NN: BF16, F32 or SwiGLU epilogues");
+      if (a.group_stride_b <= 0) return bad("group_stride_b");
+    }
+  }
   if (a.epilogue == MT_EPI_SWIGLU) {
     if (a.layout != MT_GEMM_NT) return bad("SWIGLU needs the NT layout");
     if (a.ffn != a.N || !a.gu || a.ldgu < 2 * a.ffn || a.ldc < a.N) return bad("SWIGLU args");

@@ -17,6 +17,9 @@
 
 namespace mt {
 
+// every block is a mixture-of-experts block (no dense FFN tail needed)
+static bool all_moe(const mt_config& c) { return c.n_experts > 0 && c.moe_every == 1; }
+
 static void lay(TensorOff* t, int n, int64_t* total) {
   int64_t off = 0;
   for (int i = 0; i < n; ++i) {
@@ -49,6 +52,13 @@ std::string make_plan(const mt_config& c, Plan* p) {
     return "micro_batches_per_pass must be in 1..32";
   if (c.head_token_chunk < 0 || c.head_token_chunk % 8)
     return "head_token_chunk must be 0 or a positive multiple of 8";
+  if (c.n_experts != 0) {
+    if (c.n_experts < 8 || c.n_experts > 64 || c.n_experts % 8)
+      return "n_experts must be 0 or a multiple of 8 up to 64";
+    if (c.top_k < 1 || c.top_k > 8 || c.top_k > c.n_experts) return "top_k must be in 1..min(8, E)";
+    if (c.expert_ffn < 128 || c.expert_ffn % 128) return "expert_ffn must be a multiple of 128";
+    if (c.moe_every < 1) return "moe_every must be >= 1";
+  }
 
   p->c = c;
   const int64_t h = c.hidden, F = c.ffn, V = c.vocab;
@@ -77,6 +87,19 @@ std::string make_plan(const mt_config& c, Plan* p) {
   if (L[T_WK].off != L[T_WQ].off + L[T_WQ].numel || L[T_WV].off != L[T_WK].off + L[T_WK].numel ||
       L[T_WUP].off != L[T_WGATE].off + L[T_WGATE].numel)
     return "fused projections not contiguous";
+  // mixture-of-experts block layout (used only when n_experts > 0)
+  p->any_moe = false;
+  for (int l = 0; l < c.n_layers; ++l) p->any_moe = p->any_moe || p->is_moe(l);
+  const int64_t E = c.n_experts, Fe = c.expert_ffn;
+  TensorOff* Mo = p->moe;
+  for (int i = 0; i <= T_MLP_NORM; ++i) Mo[i] = L[i];
+  Mo[M_ROUTER] = {"w_router", 0, 0, (int32_t)E, (int32_t)h};
+  Mo[M_GU] = {"w_gu", 0, 0, (int32_t)(E * 2 * Fe), (int32_t)h};
+  Mo[M_DOWN] = {"w_down", 0, 0, (int32_t)(E * h), (int32_t)Fe};
+  lay(Mo, T_COUNT, &p->moe_elems);
+  if (!p->any_moe) p->moe_elems = 0;
+  p->moe_rows = round_up(p->T * c.top_k, 256) + 256 * E;
+  p->moe_ldl = round_up(E, 8);
 
   p->head[0] = {"final_norm", 0, 0, 1, (int32_t)h};
   p->head[1] = {"w_head", 0, 0, (int32_t)V, (int32_t)h};
@@ -100,7 +123,7 @@ std::string make_plan(const mt_config& c, Plan* p) {
   p->head_rows = 0;
   for (int k = 0; k < p->n_chunks; ++k)
     p->head_rows = std::max(p->head_rows, p->chunk_row0[k + 1] - p->chunk_row0[k]);
-  p->unit_elems = p->layer_elems;
+  p->unit_elems = std::max(p->layer_elems, p->moe_elems);
   for (int k = 0; k < p->n_chunks; ++k)
     p->unit_elems = std::max(p->unit_elems, p->chunk_e0[k + 1] - p->chunk_e0[k]);
   p->n_segments = (c.n_layers + c.ckpt_interval - 1) / c.ckpt_interval;
@@ -119,9 +142,33 @@ std::string make_plan(const mt_config& c, Plan* p) {
   s.h1 = take(T * h * 4);
   s.rstd2 = take(T * 4);
   s.n2 = take(T * h * 2);
+  const size_t tail0 = o;
   s.gu = take(T * 2 * F * 2);
   s.m = take(T * F * 2);
-  s.bytes = o;
+  const size_t dense_end = o;
+  size_t moe_end = tail0;
+  if (p->any_moe) {
+    const size_t R = (size_t)p->moe_rows, k = (size_t)c.top_k;
+    o = tail0;
+    s.mlog = take(T * (size_t)E * 4);
+    s.msel = take(T * k * 4);
+    s.mgate = take(T * k * 4);
+    s.mpos = take(T * k * 4);
+    s.moff = take(65 * 4);
+    s.mrowtok = take(R * 4);
+    s.mx = take(R * h * 2);
+    s.mgu = take(R * 2 * Fe * 2);
+    s.mm = take(R * Fe * 2);
+    s.myo = take(R * h * 4);
+    moe_end = o;
+  }
+  // a slot holds one block at a time: the larger of the two tails
+  if (!p->any_moe)
+    s.bytes = dense_end;
+  else if (all_moe(c))
+    s.bytes = moe_end;
+  else
+    s.bytes = std::max(dense_end, moe_end);
 
   // workspace
   o = 0;
@@ -146,7 +193,7 @@ std::string make_plan(const mt_config& c, Plan* p) {
   w.dy0 = take(T * h * 4);
   w.dy1 = take(T * h * 4);
   w.dyb = take(T * h * 2);
-  w.dgu = take(T * 2 * F * 2);
+  w.dgu = take(std::max(T * 2 * F * 2, p->any_moe ? (size_t)p->moe_rows * 2 * Fe * 2 : 0));
   w.dn = take(T * h * 4);
   w.dh1 = take(T * h * 4);
   w.dh1b = take(T * h * 2);
@@ -161,6 +208,12 @@ std::string make_plan(const mt_config& c, Plan* p) {
   w.labels[1] = take(T * 4);
   w.x0[0] = take(T * h * 4);
   w.x0[1] = take(T * h * 4);
+  const size_t R = p->any_moe ? (size_t)p->moe_rows : 0;
+  w.mdout = take(R * h * 2);
+  w.mdx = take(R * h * 4);
+  w.mdlog = take(p->any_moe ? T * (size_t)p->moe_ldl * 2 : 0);
+  // the expert selection of every MoE block in the last forward (mt_moe_routing)
+  w.mroute = take(p->any_moe ? (size_t)(c.n_layers / c.moe_every) * T * c.top_k * 4 : 0);
   w.bytes = o;
 
   p->weight_buf_bytes = round_bytes((size_t)p->unit_elems * 2);
@@ -192,9 +245,9 @@ extern "C" mt_status mt_layout(const mt_config* cfg, int32_t group, mt_tensor_de
     n = 2;
     total = p.head_elems;
   } else if (group >= 0 && group < cfg->n_layers) {
-    t = p.layer;
+    t = p.block_layout(group);
     n = mt::T_COUNT;
-    total = p.layer_elems;
+    total = p.block_elems(group);
   } else {
     return MT_E_ARG;
   }
@@ -225,12 +278,14 @@ extern "C" mt_status mt_device_requirements(const mt_config* cfg, mt_device_req*
                       p.window_bytes + p.ckpt_bytes + p.ws.bytes;
   int64_t nparams = (int64_t)cfg->vocab * cfg->hidden;  // embedding
   nparams += p.head[0].numel + p.head[1].numel;
-  int64_t per_layer = 0;
-  for (int i = 0; i < mt::T_COUNT; ++i) per_layer += p.layer[i].numel;
-  nparams += per_layer * cfg->n_layers;
+  int64_t block_elems = 0;
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    for (int i = 0; i < mt::T_COUNT; ++i) nparams += p.block_layout(l)[i].numel;
+    block_elems += p.block_elems(l);
+  }
   out->host_state = (size_t)nparams * 16;
   const size_t T = (size_t)p.T;
-  out->pinned_host = (size_t)(p.layer_elems * cfg->n_layers + p.head_elems) * 2 +
+  out->pinned_host = (size_t)(block_elems + p.head_elems) * 2 +
                      (size_t)cfg->n_grad_slabs * p.slab_bytes + 4 * T * cfg->hidden * 4 +
                      2 * T * 4 + 4096 * 4;
   out->unit_elems = p.unit_elems;

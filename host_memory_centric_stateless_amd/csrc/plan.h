@@ -24,18 +24,24 @@ struct TensorOff {
 // Byte offsets of one window slot (activations of one block kept for its
 // backward).
 struct SlotLayout {
-  size_t x, rstd1, n1, qkv, o, lse, h1, rstd2, n2, gu, m, bytes;
+  size_t x, rstd1, n1, qkv, o, lse, h1, rstd2, n2, gu, m;
+  // mixture-of-experts blocks, after n2 (the same slot holds one block at a
+  // time): router logits, selection, gates, row plan, expert-major rows
+  size_t mlog, msel, mgate, mpos, moff, mrowtok, mx, mgu, mm, myo;
+  size_t bytes;
 };
 
 // Byte offsets inside the workspace region.
 struct WorkLayout {
   size_t xL, xf, rstd_f, logits, dlogits, ce_m, ce_s, ce_lab, ce_lse, dw_acc, loss_rows, loss, dxf,
       dy0, dy1, dyb, dgu, dn, dh1, dh1b, dout, dsum, dqkv, partial, cos_t, sin_t, labels[2], x0[2],
-      bytes;
+      mdout, mdx, mdlog, mroute, bytes;
 };
 
-// Indices into Plan::layer[].
+// Indices into Plan::layer[] (dense blocks) and Plan::moe[] (mixture-of-
+// experts blocks: the attention part shares the first six indices).
 enum { T_ATTN_NORM = 0, T_WQ, T_WK, T_WV, T_WO, T_MLP_NORM, T_WGATE, T_WUP, T_WDOWN, T_COUNT };
+enum { M_ROUTER = T_MLP_NORM + 1, M_GU, M_DOWN };
 
 struct Plan {
   mt_config c;
@@ -45,6 +51,17 @@ struct Plan {
   int64_t qd, kvd, ldq; // q width, kv width, qkv row width
   TensorOff layer[T_COUNT];
   int64_t layer_elems;
+  // mixture-of-experts blocks (a second structure group)
+  TensorOff moe[T_COUNT];
+  int64_t moe_elems;
+  int64_t moe_rows;      // expert-major row space: T k rounded to 256, + 256 E
+  int64_t moe_ldl;       // row stride of the router-logit gradient (E rounded to 8)
+  bool any_moe;
+  bool is_moe(int l) const {
+    return c.n_experts > 0 && l % c.moe_every == c.moe_every - 1;
+  }
+  const TensorOff* block_layout(int l) const { return is_moe(l) ? moe : layer; }
+  int64_t block_elems(int l) const { return is_moe(l) ? moe_elems : layer_elems; }
   TensorOff head[2];    // final_norm, w_head
   int64_t head_elems;
   int64_t embed_elems;

@@ -92,6 +92,20 @@ typedef struct mt_config {
                              merges each chunk's softmax statistics into a
                              per-token log-sum-exp, the backward recomputes
                              the chunk's logits for its gradient.           */
+  /* Mixture-of-experts blocks, a second parameter-structure group (m.lqnn.cn
+   * MegaTrain article, 四: layers are grouped by structure, MoE layers form
+   * their own group with their own flat layout).  Block l is an MoE block when
+   * n_experts > 0 and l % moe_every == moe_every - 1.  Its FFN: router logits
+   * r = n2 W_router^T; the top_k experts by logit (ties to the lower index);
+   * gates = softmax over the selected logits; each expert a SwiGLU of width
+   * expert_ffn; the block adds sum_j gate_j * expert_j(n2).  Flat layout of an
+   * MoE block: attn_norm, wq, wk, wv, wo, mlp_norm, w_router [E, h], w_gu
+   * [E * 2 expert_ffn, h] (expert e's gate rows, then its up rows), w_down
+   * [E * h, expert_ffn]. */
+  int32_t n_experts;      /* E: 0 (no MoE block) or a multiple of 8, <= 64      */
+  int32_t top_k;          /* experts per token, 1..min(8, E)                    */
+  int32_t expert_ffn;     /* F_e, a multiple of 128                             */
+  int32_t moe_every;      /* >= 1                                               */
 } mt_config;
 
 /* One tensor of a group's flat layout. */
@@ -308,6 +322,14 @@ mt_status mt_get_kernel_times(mt_ctx* ctx, mt_kernel_time* out, int32_t cap, int
  * last one completed.  Waits for those losses on the GPU.  MT_E_STATE if no
  * pass has run yet; MT_E_ARG for null pointers. */
 mt_status mt_step_loss(mt_ctx* ctx, float* loss_out);
+
+/* The expert selection of MoE block `layer` in the last forward pass: top_k
+ * expert indices per token, [T, top_k] int32 (T = tokens of the pass), the
+ * largest router logit first.  Waits for the compute stream.  MT_E_ARG if
+ * `layer` is not an MoE block.  (lqnn 四: the MoE group's routing is the
+ * state a caller inspects for expert load; parity checks hand it to the
+ * oracle, since a selection is a discontinuous function of the logits.) */
+mt_status mt_moe_routing(mt_ctx* ctx, int32_t layer, int32_t* sel_out);
 
 /* Message of the last error of the context (a string owned by it). */
 const char* mt_last_error(const mt_ctx* ctx);

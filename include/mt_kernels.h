@@ -67,6 +67,20 @@ typedef struct mt_gemm_args {
   const float* rope_sin;
   int64_t rope_cols;        /* ROPE only: columns [0, rope_cols) are rotated      */
   int32_t rope_seq, rope_dim;
+  /* Grouped products (the experts of an MoE block, one launch for all of
+   * them).  groups = 0: an ordinary product.  groups = G > 0: group_off is a
+   * device int32 array [G + 1] of row offsets, multiples of 256, increasing;
+   * the rows of group g are [group_off[g], group_off[g+1]) of a row space of
+   * at most M (NT, NN) or K (TN) rows, known only on the device.
+   *   NT, NN: rows of A and C belong to groups; group g multiplies by
+   *           B + g * group_stride_b (elements).  M is the row space's size.
+   *   TN:     group g reduces over its own rows (the k index):
+   *           C + g * group_stride_c (elements) = sum over those rows of
+   *           A(row, m) B(row, n); K is the row space's size; an empty group
+   *           writes zeros. */
+  const int32_t* group_off;
+  int32_t groups, group_reserved;
+  int64_t group_stride_b, group_stride_c;
 } mt_gemm_args;
 
 mt_status mtk_gemm(const mt_gemm_args* args, void* stream);

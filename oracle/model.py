@@ -180,8 +180,11 @@ def swiglu_bwd(dm, a, u):
 
 
 # ------------------------------------------------------------------- block
-def block_forward(W: Dict[str, np.ndarray], x: np.ndarray, cfg, cos, sin, batch: int):
-    """One decoder block.  x [T, h] with T = batch * seq.  Returns (y, cache)."""
+def block_forward(W: Dict[str, np.ndarray], x: np.ndarray, cfg, cos, sin, batch: int,
+                  sel=None):
+    """One decoder block.  x [T, h] with T = batch * seq.  sel: an expert
+    selection handed to a mixture-of-experts block (oracle.moe.route).
+    Returns (y, cache)."""
     T, h = x.shape
     s = T // batch
     nq, nkv, d = cfg.n_heads, cfg.n_kv_heads, cfg.head_dim
@@ -197,7 +200,7 @@ def block_forward(W: Dict[str, np.ndarray], x: np.ndarray, cfg, cos, sin, batch:
     cache = dict(x=x, n1=n1, r1=r1, qr=qr, kr=kr, v=v, o=o, h1=h1, n2=n2, r2=r2)
     if "w_router" in W:  # a mixture-of-experts block (oracle.moe)
         from . import moe
-        f, cache["moe"] = moe.ffn_forward(W, n2, cfg)
+        f, cache["moe"] = moe.ffn_forward(W, n2, cfg, sel)
         return h1 + f, cache
     a = n2 @ W["w_gate"].T
     u = n2 @ W["w_up"].T
@@ -293,17 +296,19 @@ def _tables(cfg, dtype):
 
 
 def forward_backward_whole(params: Dict[int, Dict[str, np.ndarray]], tokens: np.ndarray,
-                           labels: np.ndarray, cfg, grad_scale: float):
+                           labels: np.ndarray, cfg, grad_scale: float, routing=None):
     """Plain model: keep every layer's activations, then backward.
-    params {group: {name: array}}; tokens/labels [b, s].  Returns (loss, grads
-    {group: {name: array}})."""
+    params {group: {name: array}}; tokens/labels [b, s]; routing: optional
+    {layer: expert selection} for mixture-of-experts blocks.  Returns (loss,
+    grads {group: {name: array}})."""
+    routing = routing or {}
     dtype = params[L.EMBED]["emb"].dtype
     cos, sin = _tables(cfg, dtype)
     b = tokens.shape[0]
     x = embed(params[L.EMBED]["emb"], tokens)
     caches = []
     for l in range(cfg.n_layers):
-        x, c = block_forward(params[l], x, cfg, cos, sin, b)
+        x, c = block_forward(params[l], x, cfg, cos, sin, b, routing.get(l))
         caches.append(c)
     loss, dy, gh = head_forward_backward(params[L.HEAD], x, labels.reshape(-1), grad_scale,
                                          cfg.rms_eps)
@@ -317,7 +322,7 @@ def forward_backward_whole(params: Dict[int, Dict[str, np.ndarray]], tokens: np.
 def forward_backward_streamed(flats: Dict[int, np.ndarray], tokens: np.ndarray,
                               labels: np.ndarray, cfg, grad_scale: float, K: int,
                               grad_flats: Dict[int, np.ndarray], accumulate: bool,
-                              stats: Optional[dict] = None):
+                              stats: Optional[dict] = None, routing=None):
     """Streamed execution with segment recompute.
 
     flats: {group: flat array} holding the weights (lqnn 三.1).  Forward keeps
@@ -326,8 +331,10 @@ def forward_backward_streamed(flats: Dict[int, np.ndarray], tokens: np.ndarray,
     runs the segment's layers backwards; each layer's gradient is packed into a
     flat array and written (accumulate=False) or added (accumulate=True) into
     ``grad_flats[group]`` -- the host gradient of lqnn 二 / 三.3.
+    routing: optional {layer: expert selection} for mixture-of-experts blocks.
     Returns the micro-batch loss.
     """
+    routing = routing or {}
     dtype = flats[L.EMBED].dtype
     cos, sin = _tables(cfg, dtype)
     b = tokens.shape[0]
@@ -337,7 +344,7 @@ def forward_backward_streamed(flats: Dict[int, np.ndarray], tokens: np.ndarray,
     for l in range(nL):
         if l % K == 0:
             ckpt.append(x)
-        x, _ = block_forward(L.unpack(cfg, l, flats[l]), x, cfg, cos, sin, b)
+        x, _ = block_forward(L.unpack(cfg, l, flats[l]), x, cfg, cos, sin, b, routing.get(l))
     loss, dy, gh = head_forward_backward(L.unpack(cfg, L.HEAD, flats[L.HEAD]), x,
                                          labels.reshape(-1), grad_scale, cfg.rms_eps)
 
@@ -355,7 +362,7 @@ def forward_backward_streamed(flats: Dict[int, np.ndarray], tokens: np.ndarray,
         x = ckpt[seg]
         window = []
         for l in range(lo, hi):
-            x, c = block_forward(L.unpack(cfg, l, flats[l]), x, cfg, cos, sin, b)
+            x, c = block_forward(L.unpack(cfg, l, flats[l]), x, cfg, cos, sin, b, routing.get(l))
             window.append(c)
             recomputed += 1
         for l in reversed(range(lo, hi)):

@@ -52,22 +52,34 @@ def expert_weights(W: Dict[str, np.ndarray], e: int, h: int, Fe: int):
     return gu[:Fe], gu[Fe:], W["w_down"][e * h:(e + 1) * h]
 
 
-def route(n2: np.ndarray, w_router: np.ndarray, k: int):
-    """Router logits r [T, E], selected experts sel [T, k] (M2) and gates g [T, k] (M3)."""
+def route(n2: np.ndarray, w_router: np.ndarray, k: int, sel=None):
+    """Router logits r [T, E], selected experts sel [T, k] (M2) and gates g [T, k] (M3).
+    sel: a selection taken elsewhere (a parity run hands in the one the
+    kernels took, which may differ from this one only at near-ties: the
+    selection is a discontinuous function of the logits)."""
     r = n2 @ w_router.T
-    dec = _bf16(n2).astype(np.float64) @ _bf16(w_router).astype(np.float64).T
-    sel = np.argsort(-dec, axis=1, kind="stable")[:, :k]
+    if sel is None:
+        sel = decide(n2, w_router, k)
+    sel = np.asarray(sel)
     sl = np.take_along_axis(r, sel, axis=1)
     z = np.exp(sl - sl.max(axis=1, keepdims=True))
     g = z / z.sum(axis=1, keepdims=True)
     return r, sel, g
 
 
-def ffn_forward(W: Dict[str, np.ndarray], n2: np.ndarray, cfg) -> Tuple[np.ndarray, dict]:
-    """sum_j g_j E_{e_j}(n2) for every token.  Returns (f [T, h], cache)."""
+def decide(n2: np.ndarray, w_router: np.ndarray, k: int) -> np.ndarray:
+    """The k largest router logits per token, ties to the lower index, decided
+    on bf16-rounded operands (M2)."""
+    dec = _bf16(n2).astype(np.float64) @ _bf16(w_router).astype(np.float64).T
+    return np.argsort(-dec, axis=1, kind="stable")[:, :k]
+
+
+def ffn_forward(W: Dict[str, np.ndarray], n2: np.ndarray, cfg, sel=None) -> Tuple[np.ndarray, dict]:
+    """sum_j g_j E_{e_j}(n2) for every token (sel: see :func:`route`).
+    Returns (f [T, h], cache)."""
     T, h = n2.shape
     E, k, Fe = cfg.n_experts, cfg.top_k, cfg.expert_ffn
-    r, sel, g = route(n2, W["w_router"], k)
+    r, sel, g = route(n2, W["w_router"], k, sel)
     f = np.zeros_like(n2)
     per = []
     for e in range(E):

@@ -48,8 +48,10 @@ class HostState:
 
 def train_step(st: HostState, tokens: np.ndarray, labels: np.ndarray, step: int,
                hp: Optional[AdamWHparams] = None, K: Optional[int] = None,
-               mode: str = "streamed") -> float:
-    """tokens/labels [acc, b, s].  Updates st in place; returns the step loss."""
+               mode: str = "streamed", routing=None) -> float:
+    """tokens/labels [acc, b, s].  Updates st in place; returns the step loss.
+    routing: optional [acc] list of {layer: expert selection} for
+    mixture-of-experts blocks (see oracle.moe.route)."""
     cfg = st.cfg
     hp = hp or AdamWHparams(lr=cfg.lr)
     K = K or cfg.ckpt_interval
@@ -59,9 +61,11 @@ def train_step(st: HostState, tokens: np.ndarray, labels: np.ndarray, step: int,
     for mb in range(acc):
         if mode == "streamed":
             loss = forward_backward_streamed(st.master, tokens[mb], labels[mb], cfg, scale, K,
-                                             st.grad, accumulate=mb > 0)
+                                             st.grad, accumulate=mb > 0,
+                                             routing=routing[mb] if routing else None)
         elif mode == "whole":
-            loss, grads = forward_backward_whole(st.params(), tokens[mb], labels[mb], cfg, scale)
+            loss, grads = forward_backward_whole(st.params(), tokens[mb], labels[mb], cfg, scale,
+                                                 routing=routing[mb] if routing else None)
             for g in st.groups:
                 gf = L.pack(cfg, g, grads[g], dtype=st.dtype)
                 if mb == 0:

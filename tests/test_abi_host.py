@@ -48,6 +48,26 @@ def test_layout_matches_oracle(name):
         assert [(d[0], d[1], d[2]) for d in descs] == [(e[0], e[2], e[3]) for e in ent]
 
 
+@pytest.mark.parametrize("name", ["M1", "M2"])
+def test_moe_layout_matches_oracle(name):
+    """Both structure groups of a mixture-of-experts model: every block's
+    layout (dense and MoE) equals the oracle's, and the host-state bytes
+    count both."""
+    from synth_inputs import MOE_PRESETS
+    cfg = MOE_PRESETS[name]
+    c = mt.make_config(cfg)
+    for g in [OL.EMBED] + list(range(cfg.n_layers)) + [OL.HEAD]:
+        descs, total = mt.mt_layout(c, g)
+        ent, ototal = OL.group_layout(cfg, g)
+        assert total == ototal
+        assert [(d[0], d[1], d[2]) for d in descs] == [(e[0], e[2], e[3]) for e in ent]
+    r = mt.mt_device_requirements(c)
+    assert r.host_state == 16 * OL.param_count(cfg)
+    bad = cfg.replace(n_experts=6)
+    with pytest.raises(mt.MtError):
+        mt.mt_device_requirements(mt.make_config(bad))
+
+
 def test_layout_rejects_bad_group_and_config():
     c = mt.make_config(PRESETS["C1"])
     with pytest.raises(mt.MtError):

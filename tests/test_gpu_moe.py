@@ -1,0 +1,210 @@
+"""The mixture-of-experts structure group on the GPU (m.lqnn.cn MegaTrain
+article, 四: layers grouped by parameter structure, MoE layers in their own
+group on the same flat layout, streams and slabs).
+
+* the grouped bf16 MFMA GEMM (one launch over every expert, row offsets on
+  the device) against per-expert products in float64, for each layout and
+  epilogue the MoE block uses, with an empty expert and ragged row counts;
+* streamed training steps of a model whose odd blocks are MoE blocks against
+  the CPU oracle (loss and every gradient tensor; the oracle is handed the
+  GPU's expert choices after checking they differ from its own only at
+  near-ties of the router logits);
+* pipeline invariants: the checkpoint interval and the slab pool size do not
+  change a bit of the gradients.
+"""
+import numpy as np
+import pytest
+import torch
+
+import host_memory_centric_stateless_amd as mt
+from oracle.train import HostState, train_step
+from synth_inputs import MOE_PRESETS, make_batch, random_array, weight_stream
+from tests.gpu_util import bf16_dev, bf16_round, dev, host, rel_l2, rel_max
+from tests.test_gpu_step import GRAD_TOL, LOSS_TOL, _session, _tensors
+
+pytestmark = pytest.mark.gpu
+
+COUNTS = [300, 0, 17, 256, 1, 513, 40, 99]   # rows of each expert (one empty)
+
+
+def _row_space(counts):
+    off = [0]
+    for c in counts:
+        off.append(off[-1] + (c + 255) // 256 * 256)
+    return np.array(off, np.int32)
+
+
+def _rows(counts, off, width, seed, std=1.0):
+    """Expert-major rows: real rows random, padding rows zero."""
+    X = np.zeros((int(off[-1]) + 512, width), np.float32)   # extra rows past the last block
+    rng = np.random.default_rng(seed)
+    for e, c in enumerate(counts):
+        X[off[e]:off[e] + c] = rng.standard_normal((c, width)).astype(np.float32) * std
+    return X
+
+
+def test_grouped_gemm_matches_per_expert_products():
+    E, h, Fe = len(COUNTS), 256, 384
+    off = _row_space(COUNTS)
+    R = X_rows = int(off[-1]) + 512
+    offd = torch.from_numpy(off).to(dev())
+    X = _rows(COUNTS, off, h, 1)
+    Wgu = random_array((E * 2 * Fe, h), seed=2, std=0.05)
+    Wd = random_array((E * h, Fe), seed=3, std=0.05)
+    Xb, Wgub, Wdb = bf16_round(X), bf16_round(Wgu), bf16_round(Wd)
+    # NT SwiGLU: m = silu(X Wg_e^T) * (X Wu_e^T), gu kept
+    m = torch.zeros((R, Fe), dtype=torch.bfloat16, device=dev())
+    gu = torch.zeros((R, 2 * Fe), dtype=torch.bfloat16, device=dev())
+    mt.mtk_gemm(mt.MT_GEMM_NT, mt.MT_EPI_SWIGLU, R, Fe, h, bf16_dev(X), h, bf16_dev(Wgu), h, m, Fe,
+                gu=gu, ldgu=2 * Fe, ffn=Fe, group_off=offd, groups=E, group_stride_b=2 * Fe * h)
+    # NT F32: Yo = m Wd_e^T
+    Yo = torch.zeros((R, h), dtype=torch.float32, device=dev())
+    mt.mtk_gemm(mt.MT_GEMM_NT, mt.MT_EPI_F32, R, h, Fe, m, Fe, bf16_dev(Wd), Fe, Yo, h,
+                group_off=offd, groups=E, group_stride_b=h * Fe)
+    G, Mg, Y = host(gu), host(m), host(Yo)
+    dO = _rows(COUNTS, off, h, 4)
+    dOb = bf16_round(dO)
+    dgu = torch.zeros((R, 2 * Fe), dtype=torch.bfloat16, device=dev())
+    mt.mtk_gemm(mt.MT_GEMM_NN, mt.MT_EPI_SWIGLU_BWD, R, Fe, h, bf16_dev(dO), h, bf16_dev(Wd), Fe,
+                dgu, 2 * Fe, gu=gu, ldgu=2 * Fe, ffn=Fe, group_off=offd, groups=E,
+                group_stride_b=h * Fe)
+    dX = torch.zeros((R, h), dtype=torch.float32, device=dev())
+    mt.mtk_gemm(mt.MT_GEMM_NN, mt.MT_EPI_F32, R, h, 2 * Fe, dgu, 2 * Fe, bf16_dev(Wgu), h, dX, h,
+                group_off=offd, groups=E, group_stride_b=2 * Fe * h)
+    dWd = torch.full((E * h, Fe), float("nan"), dtype=torch.float32, device=dev())
+    mt.mtk_gemm(mt.MT_GEMM_TN, mt.MT_EPI_F32, h, Fe, R, bf16_dev(dO), h, m, Fe, dWd, Fe,
+                group_off=offd, groups=E, group_stride_c=h * Fe)
+    dWgu = torch.full((E * 2 * Fe, h), float("nan"), dtype=torch.bfloat16, device=dev())
+    mt.mtk_gemm(mt.MT_GEMM_TN, mt.MT_EPI_BF16, 2 * Fe, h, R, dgu, 2 * Fe, bf16_dev(X), h, dWgu, h,
+                group_off=offd, groups=E, group_stride_c=2 * Fe * h)
+    DG, DX, DWD, DWGU = host(dgu), host(dX), host(dWd), host(dWgu)
+    from oracle.model import swiglu_bwd
+    for e, c in enumerate(COUNTS):
+        r0, r1 = int(off[e]), int(off[e + 1])
+        if c == 0:   # an empty expert: zero weight gradients
+            assert np.all(DWD[e * h:(e + 1) * h] == 0) and np.all(DWGU[e * 2 * Fe:(e + 1) * 2 * Fe] == 0)
+            continue
+        wg, wu = Wgub[e * 2 * Fe:e * 2 * Fe + Fe], Wgub[e * 2 * Fe + Fe:(e + 1) * 2 * Fe]
+        wd = Wdb[e * h:(e + 1) * h]
+        a, u = Xb[r0:r1] @ wg.T, Xb[r0:r1] @ wu.T
+        sc = max(np.max(np.abs(a)), np.max(np.abs(u)), 1e-30)
+        assert np.all(np.abs(G[r0:r1, :Fe] - a) <= 2 ** -8 * np.abs(a) + 2e-5 * sc), e
+        assert np.all(np.abs(G[r0:r1, Fe:] - u) <= 2 ** -8 * np.abs(u) + 2e-5 * sc), e
+        ref_y = Mg[r0:r1] @ wd.T
+        assert rel_max(Y[r0:r1], ref_y) < 2e-5, e
+        assert np.all(Y[r0 + c:r1] == 0)   # padding rows stay zero
+        dm = dOb[r0:r1] @ wd
+        da, du = swiglu_bwd(dm, G[r0:r1, :Fe], G[r0:r1, Fe:])
+        assert rel_max(DG[r0:r1, :Fe], da) < 1e-2 and rel_max(DG[r0:r1, Fe:], du) < 1e-2, e
+        assert rel_max(DX[r0:r1], DG[r0:r1] @ Wgub[e * 2 * Fe:(e + 1) * 2 * Fe]) < 2e-5, e
+        assert rel_max(DWD[e * h:(e + 1) * h], dOb[r0:r1].T @ Mg[r0:r1]) < 2e-5, e
+        ref = DG[r0:r1].T @ Xb[r0:r1]
+        assert np.all(np.abs(DWGU[e * 2 * Fe:(e + 1) * 2 * Fe] - ref)
+                      <= 2 ** -8 * np.abs(ref) + 2e-5 * np.max(np.abs(ref))), e
+
+
+def _gpu_routing(sess, cfg):
+    T = cfg.micro_batch * cfg.seq_len
+    return {l: mt.mt_moe_routing(sess.ctx, l, T, cfg.top_k) for l in range(cfg.n_layers)
+            if cfg.is_moe(l)}
+
+
+def _check_routing(cfg, st, tok, routing):
+    """The expert choice is a discontinuous function of the router logits, and
+    the two sides' logits differ by bf16 rounding upstream, so their choices
+    may differ where two logits nearly tie.  Compare what is unique: the
+    oracle, fed the GPU's choices in the blocks before, decides block by block
+    on its own; every token where it chooses other experts than the GPU must
+    be a near-tie of its exact router logits.  Returns the count."""
+    from oracle import layout as L
+    from oracle import model as OM
+    from oracle import moe as OMOE
+    P = st.params()
+    cos, sin = OM.rope_tables(cfg.seq_len, cfg.head_dim, cfg.rope_base, np.float32)
+    x = OM.embed(P[L.EMBED]["emb"], tok)
+    flips = 0
+    for l in range(cfg.n_layers):
+        if cfg.is_moe(l):
+            _, c = OM.block_forward(P[l], x, cfg, cos, sin, tok.shape[0])
+            own, r = c["moe"]["sel"], c["moe"]["r"]
+            scale = float(np.std(r))
+            for t in np.nonzero(np.any(np.sort(own, 1) != np.sort(routing[l], 1), axis=1))[0]:
+                mine = set(routing[l][t]) - set(own[t])
+                theirs = set(own[t]) - set(routing[l][t])
+                gap = max(abs(r[t, a] - r[t, b]) for a in mine for b in theirs)
+                # the two sides' n2 differ by the bf16 rounding of every block
+                # before; a gap under 5 % of the logits' spread is a tie at that precision
+                assert gap < 5e-2 * scale, (l, t, gap, scale)
+                flips += 1
+        x, _ = OM.block_forward(P[l], x, cfg, cos, sin, tok.shape[0], routing.get(l))
+    return flips
+
+
+def moe_parity(cfg, steps, **kw):
+    """Steps at matched weights: each GPU step against the oracle given the
+    GPU's expert choices (checked to differ from the oracle's own only at
+    near-ties).  Returns (worst loss, worst gradient, per-tensor report)."""
+    from tests.test_gpu_step import _sync_state
+    sess = _session(cfg, **kw)
+    st = HostState(cfg, np.float32)
+    st.load_weights(weight_stream(cfg, 0))
+    worst = {"loss": 0.0, "grad": 0.0}
+    report = {}
+    try:
+        for step in range(1, steps + 1):
+            _sync_state(sess, st)
+            tok, lab = make_batch(cfg, step)
+            gl = sess.forward_backward(tok, lab)
+            routing = _gpu_routing(sess, cfg)
+            flips = _check_routing(cfg, st, tok[0], routing)
+            # a wrong choice rule would differ almost everywhere; bf16 ties are a few percent
+            assert flips <= 0.05 * tok[0].size * len(routing), flips
+            ol = train_step(st, tok, lab, step, routing=[routing])
+            worst["loss"] = max(worst["loss"], abs(gl - ol))
+            gg, og = _tensors(cfg, sess.grad), _tensors(cfg, st.grad)
+            for k in og:
+                e = rel_l2(gg[k], og[k])
+                report.setdefault(k, []).append(e)
+                worst["grad"] = max(worst["grad"], e)
+            print(f"{cfg.name}: step {step} loss gpu {gl:.6f} oracle {ol:.6f}, near-tie choices "
+                  f"{flips}, worst grad rel L2 {worst['grad']:.3e}", flush=True)
+    finally:
+        sess.close()
+    for k, v in sorted(report.items()):
+        print("grad", k, " ".join(f"{e:.2e}" for e in v))
+    return worst
+
+
+@pytest.mark.parametrize("slab_bf16", [True, False])
+def test_moe_steps_match_oracle(slab_bf16):
+    worst = moe_parity(MOE_PRESETS["M1"], 3, slab_bf16=slab_bf16)
+    assert worst["loss"] <= LOSS_TOL
+    assert worst["grad"] <= GRAD_TOL
+
+
+def test_moe_pipeline_invariants_bit_exact():
+    cfg = MOE_PRESETS["M1"].replace(n_layers=4, grad_accum=2)
+    base = None
+    for kw in ({"ckpt_interval": 1}, {"ckpt_interval": 2}, {"ckpt_interval": 4},
+               {"n_grad_slabs": 1}, {"drain_workgroups": 0}):
+        sess = _session(cfg, **kw)
+        try:
+            tok, lab = make_batch(cfg, 1)
+            loss = sess.forward_backward(tok, lab)
+            g = {k: a.copy() for k, a in sess.grad.items()}
+        finally:
+            sess.close()
+        print(kw, loss, flush=True)
+        if base is None:
+            base = (loss, g)
+            continue
+        assert loss == base[0], kw
+        for k in g:
+            np.testing.assert_array_equal(g[k], base[1][k], err_msg=str((kw, k)))
+
+
+@pytest.mark.timeout(300)
+def test_moe_small_step_matches_oracle():
+    worst = moe_parity(MOE_PRESETS["M2"], 1)
+    assert worst["loss"] <= LOSS_TOL
+    assert worst["grad"] <= GRAD_TOL
