@@ -33,26 +33,36 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 KERNEL_COPY_WGS = (4, 8, 32)
 
 
+def layer_matrix_params(cfg, layer: int) -> int:
+    """Weights one token multiplies in block `layer`: the attention projections
+    plus the dense SwiGLU FFN, or for a mixture-of-experts block the router and
+    the top_k experts it is routed to."""
+    h = cfg.hidden
+    qd, kvd = cfg.n_heads * cfg.head_dim, cfg.n_kv_heads * cfg.head_dim
+    attn = h * qd + 2 * h * kvd + qd * h
+    if getattr(cfg, "n_experts", 0) and cfg.is_moe(layer):
+        return attn + h * cfg.n_experts + cfg.top_k * 3 * h * cfg.expert_ffn
+    return attn + 3 * h * cfg.ffn
+
+
 def model_flops_per_token(cfg) -> float:
     """6 * (block matrices + LM head) + causal attention (fwd + bwd = 3x fwd);
     recompute is not counted."""
-    h, F, V = cfg.hidden, cfg.ffn, cfg.vocab
-    qd, kvd = cfg.n_heads * cfg.head_dim, cfg.n_kv_heads * cfg.head_dim
-    p_mm = h * qd + 2 * h * kvd + qd * h + 3 * h * F
-    return 6.0 * (cfg.n_layers * p_mm + h * V) + 6.0 * cfg.n_layers * cfg.seq_len * qd
+    qd = cfg.n_heads * cfg.head_dim
+    p_mm = sum(layer_matrix_params(cfg, l) for l in range(cfg.n_layers))
+    return 6.0 * (p_mm + cfg.hidden * cfg.vocab) + 6.0 * cfg.n_layers * cfg.seq_len * qd
 
 
 def hardware_flops_per_token(cfg) -> float:
     """Adds the recompute forwards (every layer outside the last segment) and
     the flash-backward recompute of the scores (2.5x the forward attention)."""
-    h, F = cfg.hidden, cfg.ffn
-    qd, kvd = cfg.n_heads * cfg.head_dim, cfg.n_kv_heads * cfg.head_dim
-    p_mm = h * qd + 2 * h * kvd + qd * h + 3 * h * F
+    qd = cfg.n_heads * cfg.head_dim
     K = cfg.ckpt_interval
     nseg = -(-cfg.n_layers // K)
-    recomputed = cfg.n_layers - (cfg.n_layers - (nseg - 1) * K)
+    recomputed = (nseg - 1) * K
     attn_fwd = 2.0 * cfg.seq_len * qd
-    return model_flops_per_token(cfg) + recomputed * (2.0 * p_mm + attn_fwd) + \
+    return model_flops_per_token(cfg) + \
+        sum(2.0 * layer_matrix_params(cfg, l) + attn_fwd for l in range(recomputed)) + \
         cfg.n_layers * 0.5 * attn_fwd
 
 
@@ -402,9 +412,9 @@ def main():
 
     import torch
     from host_memory_centric_stateless_amd import Session
-    from synth_inputs import PRESETS, make_batch, weight_stream
+    from synth_inputs import MOE_PRESETS, PRESETS, make_batch, weight_stream
 
-    cfg = PRESETS[args.config]
+    cfg = PRESETS[args.config] if args.config in PRESETS else MOE_PRESETS[args.config]
     if args.micro_batch or args.grad_accum or args.grad_slabs:
         cfg = cfg.replace(micro_batch=args.micro_batch or cfg.micro_batch,
                           grad_accum=args.grad_accum or cfg.grad_accum,
