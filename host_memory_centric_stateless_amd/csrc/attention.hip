@@ -196,30 +196,194 @@ __device__ inline void store_head_row(const f32x16_t (&acc)[D / 32], uint16_t* d
   }
 }
 
+// ------------------------------------------------------- grid order
+// Workgroup id -> (block, batch x head).  Blocks go in decreasing order of
+// work, heaviest first over all heads (under the causal mask a query block's
+// work grows with its index and a key block's falls), so the grid drains
+// evenly.  Workgroups are handed to the 8 XCDs in turn (id % 8); when
+// nbh = batch x heads is a multiple of 8, the (batch, head) pairs are laid out
+// so that all workgroups of one head run on one XCD and its K/V (or Q/dO)
+// rows are read from that XCD's L2.
+constexpr int NXCD = 8;
+__device__ inline void attn_order(int id, int nblk, int nbh, bool high_first, int& blk, int& bh) {
+  const int i = id / nbh, r = id - i * nbh;
+  blk = high_first ? nblk - 1 - i : i;
+  bh = (nbh % NXCD == 0) ? (r % NXCD) * (nbh / NXCD) + r / NXCD : r;
+}
+
+// ------------------------------------------------- padded LDS tiles
+// Tiles go from global memory straight into LDS with buffer_load ... lds: one
+// such load moves 64 lanes x 16 bytes into 1 KB of LDS in lane order, with no
+// VGPR staging and no ds_write.  A tile of R rows of one head (D bf16 each)
+// is laid out with a row pitch of 2D + PAD bytes; the lanes whose 16 bytes
+// land in a pad (or past the last row) load a chunk of the tile that another
+// lane loads too, and what they write is never read.  The pads make the
+// fragment reads free of bank conflicts with addresses that are one
+// per-lane base plus immediate offsets:
+//   * PAD = 16 (a row starts one 16-byte slot further round the 256-byte
+//     bank sweep): the 16 lanes of a ds_read_b128 read one chunk of 16
+//     consecutive rows in 16 distinct slots;
+//   * PAD = 64 (four slots): the 32 lanes of a ds_read_b64_tr_b16 read four
+//     chunks of four consecutive rows in 16 distinct slots.
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ inline void dma16(__amdgpu_buffer_rsrc_t rs, uint16_t* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds, 16, voff, 0, 0, 0);
+}
+
+template <int D, int R, int PAD>
+struct PTile {
+  static constexpr int PITCH = 2 * D + PAD;             // bytes
+  static constexpr int N = (R * PITCH + 1023) / 1024;   // 1 KB loads per tile
+  static constexpr int ELEMS = N * 512;                 // LDS elements a stage takes
+  static constexpr int V = (N + 3) / 4;                 // loads per wave (at most)
+};
+
+// The loads of one tile by the 4 waves of a workgroup, rows of stride ld
+// elements in global memory.  Every wave issues V loads per tile (wave w
+// loads w, w + 4, ...); a wave's loads past the tile's N go to a 1 KB junk
+// area, and a tile past the end of the sequence gets an empty buffer
+// resource (its loads touch no memory and return zeros).  So every wave
+// issues the same loads on every tile, and a wait can name how many of them
+// may still be in flight.
+template <int D, int R, int PAD>
+struct TileDma {
+  using P = PTile<D, R, PAD>;
+  uint32_t off[P::V];
+  int span;
+  __device__ inline TileDma(int64_t ld, int wave, int lane) {
+#pragma unroll
+    for (int k = 0; k < P::V; ++k) {
+      const int byte = (wave + 4 * k) * 1024 + lane * 16;
+      int r = byte / P::PITCH, c = (byte % P::PITCH) >> 4;
+      if (r >= R || c >= D / 8) {  // pad or past the tile: any chunk the tile loads anyway
+        r = r < R ? r : R - 1;
+        c = 0;
+      }
+      off[k] = (uint32_t)(((int64_t)r * ld + c * 8) * 2);
+    }
+    span = (int)(((R - 1) * ld + D) * 2);
+  }
+  __device__ inline void load(const uint16_t* src, bool valid, uint16_t* lds, uint16_t* junk,
+                              int wave) const {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(src), (short)0, valid ? span : 0, BUF_FLAGS);
+#pragma unroll
+    for (int k = 0; k < P::V; ++k)
+      dma16(rs, wave + 4 * k < P::N ? lds + (wave + 4 * k) * 512 : junk, off[k]);
+  }
+};
+// this wave's loads into LDS have landed (a barrier then covers every wave's)
+__device__ inline void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// all but this wave's N most recent loads have landed
+template <int N>
+__device__ inline void wait_dma_but() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Workgroup barrier for LDS tiles with direct loads in flight: this wave's
+// LDS reads have returned, then s_barrier, with no memory fence (a fence
+// would wait for every load of the wave, including the prefetches; the
+// caller has already waited for the loads the next tile reads).  The empty
+// asm statements keep the compiler from moving memory accesses across it.
+__device__ inline void tile_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Per-lane element offset of the row read: rows base + lane % 32,
+// d = 16 ks + 8 (lane / 32) + 0..7 at + 16 ks (ds_read_b128; PAD 16).
+template <int D>
+__device__ inline int row_base(int lane) {
+  return (lane & 31) * (D + 8) + (lane >> 5) * 8;
+}
+// Per-lane element offset of the transpose read (PAD 64): for the fragment
+// of d = 32 dd + lane % 32 over tile rows base + 8 (e / 4) + 4 (lane / 32) +
+// e % 4 (e = 0..7, the order the probabilities use as the B operand), add
+// 32 dd for the low four rows and 8 rows more for the high four.  One
+// ds_read_b64_tr_b16 over a 16-lane group hands lane i element i % 4 of the
+// 8-byte chunks addressed by lanes i / 4 + 4 j (j = 0..3); lane s of group
+// grp addresses row 4 (grp / 2) + s / 4 at d = 16 (grp & 1) + 4 (s % 4).
+template <int D>
+__device__ inline int tr_base(int lane) {
+  const int grp = lane >> 4, sl = lane & 15;
+  return (4 * (grp >> 1) + (sl >> 2)) * (D + 32) + 16 * (grp & 1) + 4 * (sl & 3);
+}
+__device__ inline bf16x8_t tr_read(const uint16_t* lo, const uint16_t* hi) {
+  typedef short s4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s4 lds_s4;
+  const s4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)lo);
+  const s4 c = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)hi);
+  const u32x2 x = __builtin_bit_cast(u32x2, a), y = __builtin_bit_cast(u32x2, c);
+  return as_frag(u32x4{x[0], x[1], y[0], y[1]});
+}
+
+// Maximum and sum of a value over a lane and its partner lane ^ 32 (one VALU
+// swap instead of an LDS permute).
+__device__ inline float pair_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float pair_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // --------------------------------------------------------------- forward
-// 256 threads = 4 waves x 32 queries; key/value tiles of 64 rows, double
-// buffered: the next tile's global loads are in flight while this tile's
-// scores, softmax and P V run.  At most 256 VGPRs, so two workgroups share a
-// CU.
+// 256 threads = 4 waves x 32 queries; key/value tiles of 32 rows in padded
+// LDS, four stages each, one barrier per tile.  Software pipelined per wave:
+// while the probabilities of tile t are formed (VALU), the scores of tile
+// t + 1 run on the matrix cores, and while P_t V_t runs, the row maxima of
+// tile t + 1 are taken.  Tile t's step issues the loads of K and V tile t + 3
+// and, before its barrier, waits only for those that step t + 1 reads (K tile
+// t + 2 and V tile t + 1), so a load has about two tiles of work to land.
+// The running maximum is updated lazily (only when a tile's maximum exceeds
+// it by more than RESCALE_SLACK); the row sum adds the fp32 probabilities.
+// Two workgroups per CU.
+template <int D>
+__device__ inline void fwd_scores(f32x16_t& s, const uint16_t* kt, const bf16x8_t (&qf)[D / 16]) {
+  zero(s);
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) s = mfma(ld_frag(kt + ks * 16), qf[ks], s);
+}
+__device__ inline float max16(const f32x16_t& s) {
+  float m = fmaxf(s[0], s[1]);
+#pragma unroll
+  for (int r = 2; r < 16; r += 2) m = fmaxf(m, fmaxf(s[r], s[r + 1]));
+  return m;
+}
+
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __restrict__ qkv,
                                                           uint16_t* __restrict__ out,
                                                           float* __restrict__ lse, int seq,
-                                                          int nq, int nkv, int64_t T) {
-  constexpr int BKV = 64, KS = D / 16, DT = D / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BKV * PITCH];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BKV * PITCH];
+                                                          int nq, int nkv, int64_t T, int nbh) {
+  constexpr int BKV = 32, KS = D / 16, DT = D / 32;
+  using KT = PTile<D, BKV, 16>;
+  using VT = PTile<D, BKV, 64>;
+  constexpr int PV = D + 32;  // V row pitch, elements
+  __shared__ __attribute__((aligned(16))) uint16_t K0[KT::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t K1[KT::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t K2[KT::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t K3[KT::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t V0[VT::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t V1[VT::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t V2[VT::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t V3[VT::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t junk[512];
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, known uniform
-  const int qb = gridDim.x - 1 - blockIdx.x;
-  const int j = blockIdx.y, b = blockIdx.z;
+  int qb, bh;
+  attn_order(blockIdx.x, seq / 128, nbh, true, qb, bh);
+  const int b = bh / nq, j = bh % nq;
   const int kvh = j / (nq / nkv);
   const int64_t ld = (int64_t)(nq + 2 * nkv) * D;
   const int64_t row0 = (int64_t)b * seq;
   const uint16_t* Qp = qkv + j * D;
-  const uint16_t* Kp = qkv + (int64_t)nq * D + kvh * D;
-  const uint16_t* Vp = qkv + (int64_t)(nq + nkv) * D + kvh * D;
+  const uint16_t* Kp = qkv + (int64_t)nq * D + kvh * D + row0 * ld;
+  const uint16_t* Vp = qkv + (int64_t)(nq + nkv) * D + kvh * D + row0 * ld;
   const float sl2 = LOG2E / sqrtf((float)D);
 
   const int q0 = qb * 128 + w * 32;
@@ -227,95 +391,137 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
   bf16x8_t qf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) qf[ks] = ld_frag(Qp + (row0 + q) * ld + ks * 16 + g * 8);
-
   f32x16_t acc[DT];
 #pragma unroll
   for (int dd = 0; dd < DT; ++dd) zero(acc[dd]);
   float m_run = -INFINITY, l_run = 0.0f;
+  const int rb = row_base<D>(lane), tb = tr_base<D>(lane);
+  const TileDma<D, BKV, 16> kdma(ld, w, lane);
+  const TileDma<D, BKV, 64> vdma(ld, w, lane);
 
-  TileCopy<BKV, D> ck(ld, tid), cv(ld, tid);
-  const int nkb = (qb * 128 + 127) / BKV + 1;  // key tiles up to the block's last query
-  ck.load(Kp + row0 * ld);
-  cv.load(Vp + row0 * ld);
-  ck.store(Ks[0], tid);
-  cv.store(Vs[0], tid);
+  const int nkt = 4 * qb + 4;  // key tiles up to the workgroup's last query (a multiple of 4)
+  const int ntw = q0 / 32 + 1;  // tiles this wave needs; its last one is diagonal
+
+  kdma.load(Kp, true, K0, junk, w);  // nkt >= 4
+  kdma.load(Kp + BKV * ld, true, K1, junk, w);
+  kdma.load(Kp + 2 * BKV * ld, true, K2, junk, w);
+  vdma.load(Vp, true, V0, junk, w);
+  vdma.load(Vp + BKV * ld, true, V1, junk, w);
+  vdma.load(Vp + 2 * BKV * ld, true, V2, junk, w);
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) settle(qf[ks]);
+  wait_dma();
   __syncthreads();
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int cur = kb & 1, kv0 = kb * BKV;
-    const bool more = kb + 1 < nkb;
-    if (more) {
-      ck.load(Kp + (row0 + kv0 + BKV) * ld);
-      cv.load(Vp + (row0 + kv0 + BKV) * ld);
-    }
-    if (kv0 <= q0 + 31) {
-      const uint16_t* ks_t = Ks[cur];
-      const uint16_t* vs_t = Vs[cur];
-      f32x16_t sc[2];
+  // The tiles carry x = S sl2 - m_run (log2 units relative to the running
+  // maximum), formed while the previous tile's P V runs; mx is the lane's
+  // maximum of x.  The first tile sets m_run to its row maximum.
+  auto mask = [&](f32x16_t& x, int t) {  // keys after the lane's query
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        zero(sc[i]);
-        score_group<KS, 0>(sc[i], ks_t, i * 32, qf, lane);
+    for (int r = 0; r < 16; ++r)
+      if (t * BKV + (r >> 2) * 8 + g * 4 + (r & 3) > q) x[r] = -INFINITY;
+  };
+  f32x16_t sA, sB;
+  fwd_scores<D>(sA, K0 + rb, qf);
+  if (ntw == 1) mask(sA, 0);
+  m_run = pair_max(max16(sA)) * sl2;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) sA[r] = fmaf(sA[r], sl2, -m_run);
+  float mx = 0.0f;
+
+  // Tile t: x holds its exponents and mx their lane maximum; kn is the K
+  // stage of tile t + 1, vt the V stage of tile t; xn / mx receive tile t + 1.
+  auto tile = [&](int t, f32x16_t& x, f32x16_t& xn, const uint16_t* kn, const uint16_t* vt) {
+    if (t >= ntw) return;
+    // The K fragments of tile t + 1 are read first (their LDS latency runs
+    // under the mask and rescale below).  They are read and multiplied even
+    // after the wave's last tile (whatever stage (t + 1) % 4 then holds; the
+    // scores are never used): one straight-line path, so the accumulators
+    // keep their registers.
+    bf16x8_t kf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kf[ks] = ld_frag(kn + rb + ks * 16);
+    bf16x8_t vf[2][DT];  // the V fragments of P_t V_t
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int dd = 0; dd < DT; ++dd) {
+        const uint16_t* p = vt + tb + hh * 16 * PV + dd * 32;
+        vf[hh][dd] = tr_read(p, p + 8 * PV);
       }
-      // causal mask only where some key of the tile lies after some query of
-      // the wave (wave-uniform branch)
-      if (kv0 + BKV - 1 > q0) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (kv0 + i * 32 + (r >> 2) * 8 + g * 4 + (r & 3) > q) sc[i][r] = -INFINITY;
-      }
-      float mloc = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sc[i][r]);
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32)) * sl2;
-      // The running maximum only has to bound the exponents, not equal the
-      // row maximum: it moves (and the accumulator is rescaled) only when a
-      // row's maximum exceeds it by more than RESCALE_SLACK, so probabilities
-      // stay below 2^RESCALE_SLACK and most tiles skip the rescale.
-      const bool grow = mloc > m_run + RESCALE_SLACK;
-      if (__ballot(grow)) {
-        const float alpha = grow ? exp2_hw(m_run - mloc) : 1.0f;
-        m_run = grow ? mloc : m_run;
-        l_run *= alpha;
-#pragma unroll
-        for (int dd = 0; dd < DT; ++dd)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[dd][r] *= alpha;
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pr = exp2_hw(fmaf(sc[i][r], sl2, -m_run));
-          sc[i][r] = pr;
-          l_run += pr;
-        }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const f32x16_t& pv = sc[i];
-          const bf16x8_t pf = as_frag(u32x4{pack_bf2(pv[hh * 8 + 0], pv[hh * 8 + 1]),
-                                            pack_bf2(pv[hh * 8 + 2], pv[hh * 8 + 3]),
-                                            pack_bf2(pv[hh * 8 + 4], pv[hh * 8 + 5]),
-                                            pack_bf2(pv[hh * 8 + 6], pv[hh * 8 + 7])});
-#pragma unroll
-          for (int dd = 0; dd < DT; ++dd)
-            acc[dd] = mfma(tr_frag(vs_t, i * 32 + hh * 16, dd * 32, lane), pf, acc[dd]);
-        }
+    if (t == ntw - 1 && t > 0) {
+      mask(x, t);
+      mx = max16(x);
     }
-    if (more) {
-      ck.store(Ks[cur ^ 1], tid);
-      cv.store(Vs[cur ^ 1], tid);
+    // The running maximum only has to bound the exponents: it moves (and the
+    // accumulator is rescaled) only when a row's maximum exceeds it by more
+    // than RESCALE_SLACK, so probabilities stay below 2^RESCALE_SLACK and
+    // most tiles skip the rescale.
+    const float rise = pair_max(mx);
+    const bool grow = rise > RESCALE_SLACK;
+    if (__ballot(grow)) {
+      const float dm = grow ? rise : 0.0f;
+      const float alpha = exp2_hw(-dm);
+      m_run += dm;
+      l_run *= alpha;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[r] -= dm;
+#pragma unroll
+      for (int dd = 0; dd < DT; ++dd)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[dd][r] *= alpha;
     }
-    __syncthreads();
+    // S_{t+1} on the matrix cores while P_t (rounded to bf16: the B
+    // fragments of P V) is formed on the VALU
+    zero(xn);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) xn = mfma(kf[ks], qf[ks], xn);
+    uint32_t u[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float a = exp2_hw(x[2 * k]), c = exp2_hw(x[2 * k + 1]);
+      u[k] = pack_bf2(a, c);
+      l_run += a;
+      l_run += c;
+    }
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 32 / KS, 0);  // its share of the VALU
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const bf16x8_t pf[2] = {as_frag(u32x4{u[0], u[1], u[2], u[3]}),
+                            as_frag(u32x4{u[4], u[5], u[6], u[7]})};
+    // P_t V_t while the exponents of tile t + 1 and their maxima are formed
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int dd = 0; dd < DT; ++dd) acc[dd] = mfma(vf[hh][dd], pf[hh], acc[dd]);
+    const float m = m_run;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) xn[r] = fmaf(xn[r], sl2, -m);
+    mx = max16(xn);
+  };
+  // Step t: K tile t + 1 is in stage kn, V tile t in stage vt; the step fills
+  // stages kfill / vfill (those of tiles t - 1) with tiles t + 3.  Before its
+  // barrier it waits for K tile t + 2 and V tile t + 1: V tile t + 2 and the
+  // step's own loads may still be in flight.
+  auto step = [&](int t, f32x16_t& s, f32x16_t& sn, const uint16_t* kn, const uint16_t* vt,
+                  uint16_t* kfill, uint16_t* vfill) {
+    const bool more = t + 3 < nkt;
+    kdma.load(Kp + (int64_t)(t + 3) * BKV * ld, more, kfill, junk, w);
+    vdma.load(Vp + (int64_t)(t + 3) * BKV * ld, more, vfill, junk, w);
+    tile(t, s, sn, kn, vt);
+    wait_dma_but<2 * VT::V + KT::V>();
+    tile_barrier();
+  };
+  for (int t = 0; t < nkt; t += 4) {
+    step(t, sA, sB, K1, V0, K3, V3);
+    step(t + 1, sB, sA, K2, V1, K0, V0);
+    step(t + 2, sA, sB, K3, V2, K1, V1);
+    step(t + 3, sB, sA, K0, V3, K2, V2);
   }
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+
+  const float l_tot = pair_sum(l_run);
   const float inv = 1.0f / l_tot;
   uint16_t* op = out + (row0 + q) * (int64_t)nq * D + j * D;
 #pragma unroll
@@ -363,15 +569,16 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
     const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ dsum, uint16_t* __restrict__ dqkv,
     const float* __restrict__ cos_t, const float* __restrict__ sin_t, int seq, int nq, int nkv,
-    int64_t T) {
+    int64_t T, int nbh) {
   constexpr int BKV = 64, KS = D / 16, DT = D / 32;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BKV * PITCH];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BKV * PITCH];
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, known uniform
-  const int qb = gridDim.x - 1 - blockIdx.x;
-  const int j = blockIdx.y, b = blockIdx.z;
+  int qb, bh;
+  attn_order(blockIdx.x, seq / 128, nbh, true, qb, bh);
+  const int b = bh / nq, j = bh % nq;
   const int kvh = j / (nq / nkv);
   const int64_t ld = (int64_t)(nq + 2 * nkv) * D;
   const int64_t row0 = (int64_t)b * seq;
@@ -477,7 +684,7 @@ __device__ __forceinline__ void dkdv_body(const uint16_t* __restrict__ qkv,
                                           uint16_t* __restrict__ dqkv, float* __restrict__ part,
                                           const float* __restrict__ cos_t,
                                           const float* __restrict__ sin_t, int seq, int nq,
-                                          int nkv, int64_t T) {
+                                          int nkv, int64_t T, int nbh) {
   constexpr int BQ = 64, KS = D / 16, DT = D / 32;
   __shared__ __attribute__((aligned(16))) uint16_t Qs[2][BQ * PITCH];
   __shared__ __attribute__((aligned(16))) uint16_t Os[2][BQ * PITCH];  // dO
@@ -486,12 +693,14 @@ __device__ __forceinline__ void dkdv_body(const uint16_t* __restrict__ qkv,
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, known uniform
-  const int kvb = gridDim.x - 1 - blockIdx.x;
-  const int b = blockIdx.z;
+  int kvb, bh;
+  attn_order(blockIdx.x, seq / 128, nbh, false, kvb, bh);
+  // SPLIT: one workgroup per query head hd, writing that head's fp32 share
+  // of dK or dV; otherwise one per kv head hd, walking its group.
+  const int nh = SPLIT ? nq : nkv;
+  const int b = bh / nh, hd = bh % nh;
   const int grp = nq / nkv;
-  // SPLIT: one workgroup per query head (blockIdx.y), writing that head's
-  // fp32 share of dK or dV; otherwise one per kv head, walking its group.
-  const int kvh = SPLIT ? (int)blockIdx.y / grp : (int)blockIdx.y;
+  const int kvh = SPLIT ? hd / grp : hd;
   const int64_t ld = (int64_t)(nq + 2 * nkv) * D;
   const int64_t ldo = (int64_t)nq * D;
   const int64_t row0 = (int64_t)b * seq;
@@ -521,7 +730,7 @@ __device__ __forceinline__ void dkdv_body(const uint16_t* __restrict__ qkv,
   const float* stat_src = (DK && w == 1) ? dsum : lse;
   float stat = 0.0f;
   auto gload = [&](int it) {
-    const int j = SPLIT ? (int)blockIdx.y : kvh * grp + it / per_head;
+    const int j = SPLIT ? hd : kvh * grp + it / per_head;
     const int q0 = (qt0 + (SPLIT ? it : it % per_head)) * BQ;
     cq.load(qkv + j * D + (row0 + q0) * ld);
     co.load(dout + j * D + (row0 + q0) * ldo);
@@ -610,8 +819,8 @@ __device__ __forceinline__ void dkdv_body(const uint16_t* __restrict__ qkv,
     __syncthreads();
   }
   if constexpr (SPLIT) {
-    // unscaled fp32 share of query head blockIdx.y: part [nq][T][D]
-    float* dst = part + ((int64_t)blockIdx.y * T + row0 + kv) * D;
+    // unscaled fp32 share of query head hd: part [nq][T][D]
+    float* dst = part + ((int64_t)hd * T + row0 + kv) * D;
 #pragma unroll
     for (int dd = 0; dd < DT; ++dd)
 #pragma unroll
@@ -694,8 +903,9 @@ template <int D, bool SPLIT>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dv_kernel(
     const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ dsum, uint16_t* __restrict__ dqkv,
-    float* __restrict__ part, int seq, int nq, int nkv, int64_t T) {
-  dkdv_body<D, false, SPLIT>(qkv, dout, lse, dsum, dqkv, part, nullptr, nullptr, seq, nq, nkv, T);
+    float* __restrict__ part, int seq, int nq, int nkv, int64_t T, int nbh) {
+  dkdv_body<D, false, SPLIT>(qkv, dout, lse, dsum, dqkv, part, nullptr, nullptr, seq, nq, nkv, T,
+                             nbh);
 }
 
 template <int D, bool SPLIT>
@@ -703,16 +913,17 @@ __global__ __launch_bounds__(256, MT_DK_WAVES_PER_SIMD) void attn_bwd_dk_kernel(
     const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ dsum, uint16_t* __restrict__ dqkv,
     float* __restrict__ part, const float* __restrict__ cos_t, const float* __restrict__ sin_t,
-    int seq, int nq, int nkv, int64_t T) {
-  dkdv_body<D, true, SPLIT>(qkv, dout, lse, dsum, dqkv, part, cos_t, sin_t, seq, nq, nkv, T);
+    int seq, int nq, int nkv, int64_t T, int nbh) {
+  dkdv_body<D, true, SPLIT>(qkv, dout, lse, dsum, dqkv, part, cos_t, sin_t, seq, nq, nkv, T, nbh);
 }
 
 template <int D>
 hipError_t fwd_d(const uint16_t* qkv, uint16_t* o, float* lse, int batch, int seq, int nq, int nkv,
                  hipStream_t s) {
   const int64_t T = (int64_t)batch * seq;
-  hipLaunchKernelGGL(attn_fwd_kernel<D>, dim3(seq / 128, nq, batch), dim3(256), 0, s, qkv, o, lse,
-                     seq, nq, nkv, T);
+  const int nbh = nq * batch;
+  hipLaunchKernelGGL(attn_fwd_kernel<D>, dim3((unsigned)(seq / 128 * nbh)), dim3(256), 0, s, qkv, o,
+                     lse, seq, nq, nkv, T, nbh);
   return hipGetLastError();
 }
 
@@ -727,24 +938,27 @@ hipError_t bwd_d(const uint16_t* qkv, const uint16_t* o, const uint16_t* dout, c
   const int64_t n = T * nq;
   hipLaunchKernelGGL(attn_dsum_kernel<D>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, o,
                      dout, dsum, nq, T);
+  const int nblk = seq / 128;
   if (nq == nkv) {
-    hipLaunchKernelGGL((attn_bwd_dv_kernel<D, false>), dim3(seq / 128, nkv, batch), dim3(256), 0,
-                       s, qkv, dout, lse, dsum, dqkv, nullptr, seq, nq, nkv, T);
-    hipLaunchKernelGGL((attn_bwd_dk_kernel<D, false>), dim3(seq / 128, nkv, batch), dim3(256), 0,
-                       s, qkv, dout, lse, dsum, dqkv, nullptr, cos_t, sin_t, seq, nq, nkv, T);
+    const int nbh = nkv * batch;
+    hipLaunchKernelGGL((attn_bwd_dv_kernel<D, false>), dim3((unsigned)(nblk * nbh)), dim3(256), 0,
+                       s, qkv, dout, lse, dsum, dqkv, nullptr, seq, nq, nkv, T, nbh);
+    hipLaunchKernelGGL((attn_bwd_dk_kernel<D, false>), dim3((unsigned)(nblk * nbh)), dim3(256), 0,
+                       s, qkv, dout, lse, dsum, dqkv, nullptr, cos_t, sin_t, seq, nq, nkv, T, nbh);
   } else {
+    const int nbh = nq * batch;
     const int64_t nv = T * nkv * (D / 4), nk = T * nkv * (cos_t ? D / 8 : D / 4);
-    hipLaunchKernelGGL((attn_bwd_dv_kernel<D, true>), dim3(seq / 128, nq, batch), dim3(256), 0, s,
-                       qkv, dout, lse, dsum, dqkv, part, seq, nq, nkv, T);
+    hipLaunchKernelGGL((attn_bwd_dv_kernel<D, true>), dim3((unsigned)(nblk * nbh)), dim3(256), 0,
+                       s, qkv, dout, lse, dsum, dqkv, part, seq, nq, nkv, T, nbh);
     hipLaunchKernelGGL(attn_gqa_reduce_kernel<D>, dim3((unsigned)((nv + 255) / 256)), dim3(256), 0,
                        s, part, dqkv, T, nq, nkv, nq + nkv, 1.0f, nullptr, nullptr, seq);
-    hipLaunchKernelGGL((attn_bwd_dk_kernel<D, true>), dim3(seq / 128, nq, batch), dim3(256), 0, s,
-                       qkv, dout, lse, dsum, dqkv, part, nullptr, nullptr, seq, nq, nkv, T);
+    hipLaunchKernelGGL((attn_bwd_dk_kernel<D, true>), dim3((unsigned)(nblk * nbh)), dim3(256), 0,
+                       s, qkv, dout, lse, dsum, dqkv, part, nullptr, nullptr, seq, nq, nkv, T, nbh);
     hipLaunchKernelGGL(attn_gqa_reduce_kernel<D>, dim3((unsigned)((nk + 255) / 256)), dim3(256), 0,
                        s, part, dqkv, T, nq, nkv, nq, 1.0f / sqrtf((float)D), cos_t, sin_t, seq);
   }
-  hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, dim3(seq / 128, nq, batch), dim3(256), 0, s, qkv,
-                     dout, lse, dsum, dqkv, cos_t, sin_t, seq, nq, nkv, T);
+  hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, dim3((unsigned)(nblk * nq * batch)), dim3(256), 0, s,
+                     qkv, dout, lse, dsum, dqkv, cos_t, sin_t, seq, nq, nkv, T, nq * batch);
   return hipGetLastError();
 }
 

@@ -45,15 +45,21 @@ extern "C" mt_status mtk_rope(uint16_t* qkv, int64_t T, int32_t seq_len, int32_t
                                 inverse, (hipStream_t)stream));
 }
 
+// The kernels launch (seq / 128) x heads x batch workgroups in one grid
+// dimension (at most 2^24 of them).
 static bool attn_ok(int32_t batch, int32_t seq, int32_t nq, int32_t nkv, int32_t d) {
   return batch >= 1 && seq >= 128 && seq % 128 == 0 && nq >= 1 && nkv >= 1 && nq % nkv == 0 &&
-         (d == 64 || d == 128) && nq <= 65535 && batch <= 65535;
+         (d == 64 || d == 128) && nq <= 65535 && batch <= 65535 &&
+         (int64_t)(seq / 128) * nq * batch <= (int64_t)1 << 24;
 }
+// Rows are moved in 16-byte vectors (and K/V tiles by 16-byte direct loads).
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 extern "C" mt_status mtk_attention_fwd(const uint16_t* qkv, uint16_t* o, float* lse,
                                        int32_t batch, int32_t seq_len, int32_t n_heads,
                                        int32_t n_kv_heads, int32_t head_dim, void* stream) {
-  if (!qkv || !o || !lse || !attn_ok(batch, seq_len, n_heads, n_kv_heads, head_dim))
+  if (!qkv || !o || !lse || !attn_ok(batch, seq_len, n_heads, n_kv_heads, head_dim) ||
+      !aligned16(qkv) || !aligned16(o))
     return MT_E_ARG;
   return hip_status(launch_attn_fwd(qkv, o, lse, batch, seq_len, n_heads, n_kv_heads, head_dim,
                                     (hipStream_t)stream));
@@ -71,7 +77,8 @@ extern "C" mt_status mtk_attention_bwd(const uint16_t* qkv, const uint16_t* o,
                                        int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
                                        void* stream) {
   if (!qkv || !o || !dout || !lse || !workspace || !dqkv ||
-      !attn_ok(batch, seq_len, n_heads, n_kv_heads, head_dim))
+      !attn_ok(batch, seq_len, n_heads, n_kv_heads, head_dim) || !aligned16(qkv) ||
+      !aligned16(o) || !aligned16(dout) || !aligned16(dqkv))
     return MT_E_ARG;
   return hip_status(launch_attn_bwd(qkv, o, dout, lse, workspace, dqkv, batch, seq_len, n_heads,
                                     n_kv_heads, head_dim, nullptr, nullptr, (hipStream_t)stream));
@@ -85,7 +92,8 @@ extern "C" mt_status mtk_attention_bwd_rope(const uint16_t* qkv, const uint16_t*
                                             const float* sin_t, void* stream) {
   if (!qkv || !o || !dout || !lse || !workspace || !dqkv || !cos_t || !sin_t ||
       (((uintptr_t)cos_t | (uintptr_t)sin_t) & 15) ||
-      !attn_ok(batch, seq_len, n_heads, n_kv_heads, head_dim))
+      !attn_ok(batch, seq_len, n_heads, n_kv_heads, head_dim) || !aligned16(qkv) ||
+      !aligned16(o) || !aligned16(dout) || !aligned16(dqkv))
     return MT_E_ARG;
   return hip_status(launch_attn_bwd(qkv, o, dout, lse, workspace, dqkv, batch, seq_len, n_heads,
                                     n_kv_heads, head_dim, cos_t, sin_t, (hipStream_t)stream));

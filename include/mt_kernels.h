@@ -126,7 +126,9 @@ mt_status mtk_rope(uint16_t* qkv, int64_t T, int32_t seq_len, int32_t n_heads,
 
 /* Causal grouped-query flash attention forward.  q, k, v are column blocks of
  * qkv [T, (nq + 2 nkv) d]; o bf16 [T, nq d]; lse fp32 [nq, T] (natural-log
- * log-sum-exp of the scaled scores).  seq_len multiple of 128, d 64 or 128. */
+ * log-sum-exp of the scaled scores).  seq_len multiple of 128, d 64 or 128,
+ * (seq_len / 128) * nq * batch <= 2^24; qkv and o 16-byte aligned (MT_E_ARG
+ * otherwise). */
 mt_status mtk_attention_fwd(const uint16_t* qkv, uint16_t* o, float* lse, int32_t batch,
                             int32_t seq_len, int32_t n_heads, int32_t n_kv_heads,
                             int32_t head_dim, void* stream);
@@ -142,7 +144,8 @@ size_t mtk_attention_bwd_workspace(int32_t batch, int32_t seq_len, int32_t n_hea
  * scratch of mtk_attention_bwd_workspace(...) bytes, owned by the caller, no
  * contents kept between calls.  Deterministic (no float atomics; dk/dv summed
  * over the query heads of a group in fixed order).  MT_E_ARG for null
- * pointers or sizes attention_fwd rejects. */
+ * pointers, sizes attention_fwd rejects, or qkv, o, dout, dqkv not 16-byte
+ * aligned. */
 mt_status mtk_attention_bwd(const uint16_t* qkv, const uint16_t* o, const uint16_t* dout,
                             const float* lse, void* workspace, uint16_t* dqkv, int32_t batch,
                             int32_t seq_len, int32_t n_heads, int32_t n_kv_heads,
