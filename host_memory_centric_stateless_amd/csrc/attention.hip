@@ -290,23 +290,24 @@ __device__ inline void tile_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Per-lane element offset of the row read: rows base + lane % 32,
-// d = 16 ks + 8 (lane / 32) + 0..7 at + 16 ks (ds_read_b128; PAD 16).
-template <int D>
+// Per-lane element offset of the row read of a tile with a pad of PE
+// elements per row: rows base + lane % 32, d = 16 ks + 8 (lane / 32) + 0..7
+// at + 16 ks (ds_read_b128).
+template <int D, int PE>
 __device__ inline int row_base(int lane) {
-  return (lane & 31) * (D + 8) + (lane >> 5) * 8;
+  return (lane & 31) * (D + PE) + (lane >> 5) * 8;
 }
-// Per-lane element offset of the transpose read (PAD 64): for the fragment
+// Per-lane element offset of the transpose read (pad PE elements): for the fragment
 // of d = 32 dd + lane % 32 over tile rows base + 8 (e / 4) + 4 (lane / 32) +
 // e % 4 (e = 0..7, the order the probabilities use as the B operand), add
 // 32 dd for the low four rows and 8 rows more for the high four.  One
 // ds_read_b64_tr_b16 over a 16-lane group hands lane i element i % 4 of the
 // 8-byte chunks addressed by lanes i / 4 + 4 j (j = 0..3); lane s of group
 // grp addresses row 4 (grp / 2) + s / 4 at d = 16 (grp & 1) + 4 (s % 4).
-template <int D>
+template <int D, int PE>
 __device__ inline int tr_base(int lane) {
   const int grp = lane >> 4, sl = lane & 15;
-  return (4 * (grp >> 1) + (sl >> 2)) * (D + 32) + 16 * (grp & 1) + 4 * (sl & 3);
+  return (4 * (grp >> 1) + (sl >> 2)) * (D + PE) + 16 * (grp & 1) + 4 * (sl & 3);
 }
 __device__ inline bf16x8_t tr_read(const uint16_t* lo, const uint16_t* hi) {
   typedef short s4 __attribute__((ext_vector_type(4)));
@@ -315,6 +316,14 @@ __device__ inline bf16x8_t tr_read(const uint16_t* lo, const uint16_t* hi) {
   const s4 c = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)hi);
   const u32x2 x = __builtin_bit_cast(u32x2, a), y = __builtin_bit_cast(u32x2, c);
   return as_frag(u32x4{x[0], x[1], y[0], y[1]});
+}
+
+// The value, opaque to the compiler.  A per-lane LDS offset passed through
+// this inside a loop is added to its stage's base there, instead of one
+// address register per stage being hoisted out of the loop.
+__device__ inline int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
 }
 
 // Maximum and sum of a value over a lane and its partner lane ^ 32 (one VALU
@@ -395,7 +404,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
 #pragma unroll
   for (int dd = 0; dd < DT; ++dd) zero(acc[dd]);
   float m_run = -INFINITY, l_run = 0.0f;
-  const int rb = row_base<D>(lane), tb = tr_base<D>(lane);
+  const int rb = row_base<D, 8>(lane), tb = tr_base<D, 32>(lane);
   const TileDma<D, BKV, 16> kdma(ld, w, lane);
   const TileDma<D, BKV, 64> vdma(ld, w, lane);
 
@@ -537,9 +546,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
 }
 
 // ------------------------------------------------- backward: D = rowsum(dO*O)
+// Also writes lse2 = lse log2(e), the row statistic in the base-2 units the
+// gradient kernels use.
 template <int D>
 __global__ void attn_dsum_kernel(const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout,
-                                 float* __restrict__ dsum, int nq, int64_t T) {
+                                 const float* __restrict__ lse, float* __restrict__ dsum,
+                                 float* __restrict__ lse2, int nq, int64_t T) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // t * nq + j
   if (idx >= T * nq) return;
   const int64_t t = idx / nq;
@@ -558,21 +570,38 @@ __global__ void attn_dsum_kernel(const uint16_t* __restrict__ o, const uint16_t*
     }
   }
   dsum[(int64_t)j * T + t] = s;
+  lse2[(int64_t)j * T + t] = lse[(int64_t)j * T + t] * LOG2E;
 }
 
 // ------------------------------------------------------- backward: dQ
-// Query block outer (4 waves x 32 queries), key/value tiles of 64 rows,
-// double buffered.  dQ^T += K^T dS^T takes K^T from the same LDS tile through
-// transpose reads.
+// Query block outer (4 waves x 32 queries, one query per lane), key and value
+// tiles of 32 rows in padded LDS, four stages each, one barrier per tile.
+// Per key tile t a wave forms S_t = K_t q and dP_t = V_t dO on the matrix
+// cores, then dS_t = P_t (dP_t - D) on the VALU while dQ += K_{t-1}^T dS_{t-1}
+// (the previous tile's, K^T through transpose reads) runs on the matrix
+// cores.  K tiles carry a 48-byte pad (row reads conflict-free, transpose
+// reads at most two-way), V tiles a 16-byte one.  Tile t's step fills K stage
+// (t + 2) % 4 (a K tile is read by two steps) and V stage (t + 3) % 4.
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
     const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dout,
-    const float* __restrict__ lse, const float* __restrict__ dsum, uint16_t* __restrict__ dqkv,
+    const float* __restrict__ lse2, const float* __restrict__ dsum, uint16_t* __restrict__ dqkv,
     const float* __restrict__ cos_t, const float* __restrict__ sin_t, int seq, int nq, int nkv,
     int64_t T, int nbh) {
-  constexpr int BKV = 64, KS = D / 16, DT = D / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BKV * PITCH];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BKV * PITCH];
+  constexpr int BKV = 32, KS = D / 16, DT = D / 32;
+  constexpr int KPE = 24, VPE = 8;  // row pads, elements
+  using KT = PTile<D, BKV, 2 * KPE>;
+  using VT = PTile<D, BKV, 2 * VPE>;
+  constexpr int PK = D + KPE;
+  __shared__ __attribute__((aligned(16))) uint16_t K0[KT::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t K1[KT::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t K2[KT::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t K3[KT::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t V0[VT::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t V1[VT::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t V2[VT::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t V3[VT::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t junk[512];
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, known uniform
@@ -583,8 +612,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
   const int64_t ld = (int64_t)(nq + 2 * nkv) * D;
   const int64_t row0 = (int64_t)b * seq;
   const uint16_t* Qp = qkv + j * D;
-  const uint16_t* Kp = qkv + (int64_t)nq * D + kvh * D;
-  const uint16_t* Vp = qkv + (int64_t)(nq + nkv) * D + kvh * D;
+  const uint16_t* Kp = qkv + (int64_t)nq * D + kvh * D + row0 * ld;
+  const uint16_t* Vp = qkv + (int64_t)(nq + nkv) * D + kvh * D + row0 * ld;
   const float sl2 = LOG2E / sqrtf((float)D);
 
   const int q0 = qb * 128 + w * 32;
@@ -596,73 +625,119 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
     qf[ks] = ld_frag(Qp + (row0 + q) * ld + ks * 16 + g * 8);
     df[ks] = ld_frag(dop + ks * 16 + g * 8);
   }
-  const float lse2 = lse[(int64_t)j * T + row0 + q] * LOG2E;
+  const float lq = lse2[(int64_t)j * T + row0 + q];
   const float dq_sum = dsum[(int64_t)j * T + row0 + q];
-
   f32x16_t acc[DT];
 #pragma unroll
   for (int dd = 0; dd < DT; ++dd) zero(acc[dd]);
+  const int rbk = row_base<D, KPE>(lane), tbk = tr_base<D, KPE>(lane);
+  const int rbv = row_base<D, VPE>(lane);
+  const TileDma<D, BKV, 2 * KPE> kdma(ld, w, lane);
+  const TileDma<D, BKV, 2 * VPE> vdma(ld, w, lane);
 
-  TileCopy<BKV, D> ck(ld, tid), cv(ld, tid);
-  const int nkb = (qb * 128 + 127) / BKV + 1;
-  ck.load(Kp + row0 * ld);
-  cv.load(Vp + row0 * ld);
-  ck.store(Ks[0], tid);
-  cv.store(Vs[0], tid);
+  const int nkt = 4 * qb + 4;   // key tiles up to the workgroup's last query (a multiple of 4)
+  const int ntw = q0 / 32 + 1;  // tiles this wave needs; its last one is diagonal
+
+  kdma.load(Kp, true, K0, junk, w);
+  kdma.load(Kp + BKV * ld, true, K1, junk, w);
+  kdma.load(Kp + 2 * BKV * ld, true, K2, junk, w);
+  vdma.load(Vp, true, V0, junk, w);
+  vdma.load(Vp + BKV * ld, true, V1, junk, w);
+  vdma.load(Vp + 2 * BKV * ld, true, V2, junk, w);
+  vdma.load(Vp + 3 * BKV * ld, true, V3, junk, w);
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     settle(qf[ks]);
     settle(df[ks]);
   }
-  settle(lse2);
+  settle(lq);
   settle(dq_sum);
+  wait_dma();
   __syncthreads();
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int cur = kb & 1, kv0 = kb * BKV;
-    const bool more = kb + 1 < nkb;
-    if (more) {
-      ck.load(Kp + (row0 + kv0 + BKV) * ld);
-      cv.load(Vp + (row0 + kv0 + BKV) * ld);
+
+  f32x16_t sc, dp;
+  bf16x8_t ds[2];
+  // S_t and dP_t from K and V stages kt, vt (the causal mask on the wave's
+  // diagonal tile)
+  auto scores = [&](int t, const uint16_t* kt, const uint16_t* vt) {
+    const uint16_t* ka = kt + opaque(rbk);
+    const uint16_t* va = vt + opaque(rbv);
+    bf16x8_t kf[KS], vf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      kf[ks] = ld_frag(ka + ks * 16);
+      vf[ks] = ld_frag(va + ks * 16);
     }
-    if (kv0 <= q0 + 31) {
-      const uint16_t* ks_t = Ks[cur];
-      const uint16_t* vs_t = Vs[cur];
-      const bool diag = kv0 + BKV - 1 > q0;
-      // the two 32-key halves of the tile one after the other (fewer live
-      // registers); the accumulation order stays fixed
+    zero(sc);
+    zero(dp);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        f32x16_t sc, dp;
-        zero(sc);
-        zero(dp);
-        score_group<KS / 2, 0>(sc, ks_t, i * 32, qf, lane);
-        score_group<KS / 2, 0>(dp, vs_t, i * 32, df, lane);
-        score_group<KS / 2, KS / 2>(sc, ks_t, i * 32, qf, lane);
-        score_group<KS / 2, KS / 2>(dp, vs_t, i * 32, df, lane);
-        if (diag) {
+    for (int ks = 0; ks < KS; ++ks) {
+      sc = mfma(kf[ks], qf[ks], sc);
+      dp = mfma(vf[ks], df[ks], dp);
+    }
+    if (t == ntw - 1) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (kv0 + i * 32 + (r >> 2) * 8 + g * 4 + (r & 3) > q) sc[r] = -INFINITY;
+      for (int r = 0; r < 16; ++r)
+        if (t * BKV + (r >> 2) * 8 + g * 4 + (r & 3) > q) sc[r] = -INFINITY;
+    }
+  };
+  // dS_t = P_t (dP_t - D), rounded to bf16: the B fragments of K^T dS^T
+  auto grads = [&]() {
+    uint32_t u[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float a = exp2_hw(fmaf(sc[2 * k], sl2, -lq)) * (dp[2 * k] - dq_sum);
+      const float c = exp2_hw(fmaf(sc[2 * k + 1], sl2, -lq)) * (dp[2 * k + 1] - dq_sum);
+      u[k] = pack_bf2(a, c);
+    }
+    ds[0] = as_frag(u32x4{u[0], u[1], u[2], u[3]});
+    ds[1] = as_frag(u32x4{u[4], u[5], u[6], u[7]});
+  };
+  scores(0, K0, V0);
+  grads();
+  __syncthreads();  // every wave has read V0 before step 1 refills it
+
+  // Step t (1 .. nkt): K tile t in stage kc, t - 1 in kp, V tile t in vc;
+  // fills kfill with K tile t + 2 and vfill with V tile t + 3.  dQ of tile
+  // t - 1 runs under dS of tile t (formed from stale scores, and never used,
+  // on the step after the wave's last tile).  Before the barrier it waits for
+  // K tile t + 1 and V tile t + 1.
+  auto step = [&](int t, const uint16_t* kc, const uint16_t* kp, const uint16_t* vc,
+                  uint16_t* kfill, uint16_t* vfill) {
+    kdma.load(Kp + (int64_t)(t + 2) * BKV * ld, t + 2 < nkt, kfill, junk, w);
+    vdma.load(Vp + (int64_t)(t + 3) * BKV * ld, t + 3 < nkt, vfill, junk, w);
+    if (t <= ntw) {
+      const bf16x8_t dsp[2] = {ds[0], ds[1]};
+      if (t < ntw) scores(t, kc, vc);
+      bf16x8_t kt[2][DT];
+      const uint16_t* kpt = kp + opaque(tbk);
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int dd = 0; dd < DT; ++dd) {
+          const uint16_t* p = kpt + hh * 16 * PK + dd * 32;
+          kt[hh][dd] = tr_read(p, p + 8 * PK);
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sc[r] = exp2_hw(fmaf(sc[r], sl2, -lse2)) * (dp[r] - dq_sum);
+      for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const bf16x8_t sf = as_frag(u32x4{pack_bf2(sc[hh * 8 + 0], sc[hh * 8 + 1]),
-                                            pack_bf2(sc[hh * 8 + 2], sc[hh * 8 + 3]),
-                                            pack_bf2(sc[hh * 8 + 4], sc[hh * 8 + 5]),
-                                            pack_bf2(sc[hh * 8 + 6], sc[hh * 8 + 7])});
+        for (int dd = 0; dd < DT; ++dd) acc[dd] = mfma(kt[hh][dd], dsp[hh], acc[dd]);
+      grads();
 #pragma unroll
-          for (int dd = 0; dd < DT; ++dd)
-            acc[dd] = mfma(tr_frag(ks_t, i * 32 + hh * 16, dd * 32, lane), sf, acc[dd]);
-        }
+      for (int k = 0; k < 2 * DT; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 72 / (2 * DT), 0);  // its share of the VALU
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (more) {
-      ck.store(Ks[cur ^ 1], tid);
-      cv.store(Vs[cur ^ 1], tid);
-    }
-    __syncthreads();
+    wait_dma_but<2 * VT::V + KT::V>();
+    tile_barrier();
+  };
+  for (int t = 1; t <= nkt; t += 4) {
+    step(t, K1, K0, V1, K3, V0);
+    step(t + 1, K2, K1, V2, K0, V1);
+    step(t + 2, K3, K2, V3, K1, V2);
+    step(t + 3, K0, K3, V0, K2, V3);
   }
   store_head_row<D>(acc, dqkv + (row0 + q) * ld + j * D, 1.0f / sqrtf((float)D), cos_t, sin_t, q,
                     g);
@@ -670,37 +745,56 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
 
 // ---------------------------------------------------- backward: dK, dV
 // Key block outer (4 waves x 32 keys, one key per lane), so grouped query
-// heads are summed in a fixed order without atomics.  The (query head, query
-// tile) pairs after the block form one sequence of 64-row Q / dO tiles, double
-// buffered with their LSE and D rows.  dV^T += dO^T P and dK^T += Q^T dS take
-// dO^T and Q^T from the same tiles through transpose reads.  dK and dV are two
-// launches of this kernel (DK selects which): each then holds one accumulator
-// and fits two waves per SIMD, at the price of recomputing P in both.
+// heads are summed in a fixed order without atomics (each query head's share
+// in fp32, added by attn_gqa_reduce_kernel).  The 32-row Q and dO tiles after
+// the block (and their D and lse log2(e) rows) stream through padded LDS,
+// four stages, one barrier per tile.  Per tile a wave forms S = Q k (and dP = dO v for dK) on the matrix
+// cores, then P (dV) or dS = P (dP - D) (dK) on the VALU while the previous
+// tile's dV^T += dO^T P or dK^T += Q^T dS (dO^T, Q^T through transpose reads)
+// runs on the matrix cores.  dK and dV are two launches of this kernel (DK
+// selects which): each then holds one accumulator and fits two waves per
+// SIMD, at the price of forming P in both.  The tile read both ways (Q for
+// dK) carries a 48-byte pad, a tile read by rows a 16-byte one, a tile read
+// by transposes a 64-byte one.  Tile it's step fills stage (it + 2) % 4.
 template <int D, bool DK, bool SPLIT>
 __device__ __forceinline__ void dkdv_body(const uint16_t* __restrict__ qkv,
                                           const uint16_t* __restrict__ dout,
-                                          const float* __restrict__ lse,
-                                          const float* __restrict__ dsum,
+                                          const float* __restrict__ stats, int stat_off,
                                           uint16_t* __restrict__ dqkv, float* __restrict__ part,
                                           const float* __restrict__ cos_t,
                                           const float* __restrict__ sin_t, int seq, int nq,
                                           int nkv, int64_t T, int nbh) {
-  constexpr int BQ = 64, KS = D / 16, DT = D / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][BQ * PITCH];
-  __shared__ __attribute__((aligned(16))) uint16_t Os[2][BQ * PITCH];  // dO
-  __shared__ __attribute__((aligned(16))) float Ls[2][BQ];
-  __shared__ __attribute__((aligned(16))) float Ds[2][BQ];
+  constexpr int BQ = 32, KS = D / 16, DT = D / 32;
+  constexpr int QPE = DK ? 24 : 8, OPE = DK ? 8 : 32;  // row pads, elements
+  using QT = PTile<D, BQ, 2 * QPE>;
+  using OT = PTile<D, BQ, 2 * OPE>;
+  constexpr int PT = D + (DK ? QPE : OPE);  // pitch of the transposed tile
+  __shared__ __attribute__((aligned(16))) uint16_t Q0[QT::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t Q1[QT::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t Q2[QT::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t Q3[QT::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t O0[OT::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t O1[OT::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t O2[OT::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t O3[OT::ELEMS];
+  // per stage: D of the tile's 32 queries, then their lse log2(e)
+  __shared__ __attribute__((aligned(16))) float S0[64];
+  __shared__ __attribute__((aligned(16))) float S1[64];
+  __shared__ __attribute__((aligned(16))) float S2[64];
+  __shared__ __attribute__((aligned(16))) float S3[64];
+  __shared__ __attribute__((aligned(16))) uint16_t junk[512];
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, known uniform
   int kvb, bh;
   attn_order(blockIdx.x, seq / 128, nbh, false, kvb, bh);
-  // SPLIT: one workgroup per query head hd, writing that head's fp32 share
-  // of dK or dV; otherwise one per kv head hd, walking its group.
+  // SPLIT (grouped heads): one workgroup per query head hd, writing that
+  // head's fp32 share of dK or dV.  Otherwise nq == nkv: one workgroup per
+  // head, writing dK or dV itself.
   const int nh = SPLIT ? nq : nkv;
   const int b = bh / nh, hd = bh % nh;
-  const int grp = nq / nkv;
-  const int kvh = SPLIT ? hd / grp : hd;
+  const int kvh = SPLIT ? hd / (nq / nkv) : hd;
+  const int j = hd;  // the query head whose tiles the workgroup walks
   const int64_t ld = (int64_t)(nq + 2 * nkv) * D;
   const int64_t ldo = (int64_t)nq * D;
   const int64_t row0 = (int64_t)b * seq;
@@ -719,104 +813,163 @@ __device__ __forceinline__ void dkdv_body(const uint16_t* __restrict__ qkv,
   f32x16_t acc[DT];
 #pragma unroll
   for (int dd = 0; dd < DT; ++dd) zero(acc[dd]);
-  const int qt0 = (kvb * 128) / BQ, nqt = seq / BQ;
-  const int per_head = nqt - qt0, n_it = SPLIT ? per_head : grp * per_head;
+  const int qt0 = kvb * 4, nqt = seq / BQ;
+  const int n_it = nqt - qt0;  // query tiles from the block's first (a multiple of 4)
+  const int first = qt0 + w;  // the wave's first query tile that sees one of its keys (diagonal)
+  const int rbq = row_base<D, QPE>(lane), rbo = row_base<D, OPE>(lane);
+  const int tbt = tr_base<D, DK ? QPE : OPE>(lane);
+  const TileDma<D, BQ, 2 * QPE> qdma(ld, w, lane);
+  const TileDma<D, BQ, 2 * OPE> odma(ldo, w, lane);
+  // statistics: lane l < 32 loads D of query l of the tile, lane l >= 32 its lse log2(e)
+  const uint32_t soff = (uint32_t)(((lane < 32) ? lane : stat_off + lane - 32) * 4);
+  const int sspan = (stat_off + 32) * 4;
 
-  TileCopy<BQ, D> cq(ld, tid), co(ldo, tid);
-  // Each wave also reads one 64-row statistics vector of the tile (BQ is the
-  // wave size): wave 1 the D rows (dK only), every other wave the LSE rows;
-  // waves 0 and 1 keep theirs.
-  static_assert(BQ == 64, "one statistics row per lane");
-  const float* stat_src = (DK && w == 1) ? dsum : lse;
-  float stat = 0.0f;
-  auto gload = [&](int it) {
-    const int j = SPLIT ? hd : kvh * grp + it / per_head;
-    const int q0 = (qt0 + (SPLIT ? it : it % per_head)) * BQ;
-    cq.load(qkv + j * D + (row0 + q0) * ld);
-    co.load(dout + j * D + (row0 + q0) * ldo);
+  // Loads of query tile it (of query head j) into (qs, os, st); past the
+  // end: empty.
+  auto load = [&](int it, uint16_t* qs, uint16_t* os, float* st) {
+    const bool valid = it < n_it;
+    const int q0 = (qt0 + (valid ? it : 0)) * BQ;
+    qdma.load(qkv + j * D + (row0 + q0) * ld, valid, qs, junk, w);
+    odma.load(dout + j * D + (row0 + q0) * ldo, valid, os, junk, w);
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(stat_src + (int64_t)j * T + row0 + q0), (short)0, BQ * 4, BUF_FLAGS);
-    stat = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, lane * 4, 0, 0));
+        const_cast<float*>(stats + (int64_t)j * T + row0 + q0), (short)0, valid ? sspan : 0,
+        BUF_FLAGS);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(w == 0 ? (void*)st : (void*)junk), 4,
+                                             soff, 0, 0, 0);
   };
-  auto sstore = [&](int buf) {
-    cq.store(Qs[buf], tid);
-    co.store(Os[buf], tid);
-    if (w == 0)
-      Ls[buf][lane] = stat * LOG2E;
-    else if (DK && w == 1)
-      Ds[buf][lane] = stat;
-  };
-  gload(0);
-  sstore(0);
+  load(0, Q0, O0, S0);  // n_it >= 4
+  load(1, Q1, O1, S1);
+  load(2, Q2, O2, S2);
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     settle(kf[ks]);
     if constexpr (DK) settle(vf[ks]);
   }
+  wait_dma();
   __syncthreads();
-  for (int it = 0; it < n_it; ++it) {
-    const int cur = it & 1;
-    const int q0 = (qt0 + (SPLIT ? it : it % per_head)) * BQ;
-    const bool more = it + 1 < n_it;
-    if (more) gload(it + 1);
-    if (q0 + BQ - 1 >= kw0) {
-      const uint16_t* qs_t = Qs[cur];
-      const uint16_t* os_t = Os[cur];
-      const bool diag = q0 < kw0 + 31;  // some query of the tile precedes some key
-      // the two 32-query halves of the tile one after the other (fewer live
-      // registers); the accumulation order stays fixed
+
+  f32x16_t sc, dp;
+  zero(sc);
+  zero(dp);
+  bf16x8_t pf[2];  // P (dV) or dS (dK) of the latest tile, rounded to bf16
+  // S (and dP) of sequence element it from stages qs, os, with the causal
+  // mask on the wave's diagonal tile; then P or dS from the statistics st.
+  // Tiles before the wave's first give zeros.
+  auto scores = [&](int it, const uint16_t* qs, const uint16_t* os) {
+    const int i = qt0 + it;
+    if (i < first) return;
+    const uint16_t* qa = qs + opaque(rbq);
+    const uint16_t* oa = os + opaque(rbo);
+    bf16x8_t af[KS], bf[DK ? KS : 1];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        f32x16_t sc, dp;
-        zero(sc);
-        if constexpr (DK) zero(dp);
-        if constexpr (DK) {
-          // two chains; batching their reads would take dK past the register
-          // budget that lets a drain wave share its CU
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            sc = mfma(row_frag(qs_t, i * 32, ks * 16, lane), kf[ks], sc);
-            dp = mfma(row_frag(os_t, i * 32, ks * 16, lane), vf[ks], dp);
-          }
-        } else {
-          score_group<KS, 0>(sc, qs_t, i * 32, kf, lane);
-        }
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int ql = i * 32 + rr * 8 + g * 4;
-          const float4 l4 = *reinterpret_cast<const float4*>(&Ls[cur][ql]);
-          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-          float dv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-          if constexpr (DK) {
-            const float4 d4 = *reinterpret_cast<const float4*>(&Ds[cur][ql]);
-            dv[0] = d4.x; dv[1] = d4.y; dv[2] = d4.z; dv[3] = d4.w;
-          }
-          if (diag) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (kv > q0 + ql + e) sc[rr * 4 + e] = -INFINITY;
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = rr * 4 + e;
-            const float pr = exp2_hw(fmaf(sc[r], sl2, -lv[e]));
-            sc[r] = DK ? pr * (dp[r] - dv[e]) : pr;  // dS for dK, P for dV
-          }
-        }
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const bf16x8_t f = as_frag(u32x4{pack_bf2(sc[hh * 8 + 0], sc[hh * 8 + 1]),
-                                           pack_bf2(sc[hh * 8 + 2], sc[hh * 8 + 3]),
-                                           pack_bf2(sc[hh * 8 + 4], sc[hh * 8 + 5]),
-                                           pack_bf2(sc[hh * 8 + 6], sc[hh * 8 + 7])});
-#pragma unroll
-          for (int dd = 0; dd < DT; ++dd)
-            acc[dd] = mfma(tr_frag(DK ? qs_t : os_t, i * 32 + hh * 16, dd * 32, lane), f, acc[dd]);
-        }
-      }
+    for (int ks = 0; ks < KS; ++ks) {
+      af[ks] = ld_frag(qa + ks * 16);
+      if constexpr (DK) bf[ks] = ld_frag(oa + ks * 16);
     }
-    if (more) sstore(cur ^ 1);
-    __syncthreads();
+    zero(sc);
+    if constexpr (DK) zero(dp);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      sc = mfma(af[ks], kf[ks], sc);
+      if constexpr (DK) dp = mfma(bf[ks], vf[ks], dp);
+    }
+    // the transpose reads that follow are issued after these products (the
+    // row fragments are then dead: fewer live registers)
+    __builtin_amdgcn_sched_barrier(0);
+    if (i == first) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (kv > i * BQ + (r >> 2) * 8 + g * 4 + (r & 3)) sc[r] = -INFINITY;
+    }
+  };
+  // Rows rr = 2 h, 2 h + 1 of the lane's probabilities (P, or dS for dK) of
+  // sequence element it, packed into u[4 h .. 4 h + 3]; then the B fragments
+  // (zeros before the wave's first tile).
+  uint32_t u[8];
+  auto probs_half = [&](int h, const float* st) {
+#pragma unroll
+    for (int rr = 2 * h; rr < 2 * h + 2; ++rr) {
+      const float4 l4 = *reinterpret_cast<const float4*>(st + 32 + rr * 8 + g * 4);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+      float dv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if constexpr (DK) {
+        const float4 d4 = *reinterpret_cast<const float4*>(st + rr * 8 + g * 4);
+        dv[0] = d4.x; dv[1] = d4.y; dv[2] = d4.z; dv[3] = d4.w;
+      }
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = rr * 4 + e;
+        const float pr = exp2_hw(fmaf(sc[r], sl2, -lv[e]));
+        v[e] = DK ? pr * (dp[r] - dv[e]) : pr;
+      }
+      u[2 * rr] = pack_bf2(v[0], v[1]);
+      u[2 * rr + 1] = pack_bf2(v[2], v[3]);
+    }
+  };
+  auto probs_frags = [&](int it) {
+    const bool live = qt0 + it >= first;
+    pf[0] = as_frag(live ? u32x4{u[0], u[1], u[2], u[3]} : u32x4{0, 0, 0, 0});
+    pf[1] = as_frag(live ? u32x4{u[4], u[5], u[6], u[7]} : u32x4{0, 0, 0, 0});
+  };
+  scores(0, Q0, O0);
+  probs_half(0, S0);
+  probs_half(1, S0);
+  probs_frags(0);
+
+  // Step it (1 .. n_it): element it in stages (qc, oc, sc_), it - 1 in
+  // (qp, op); fills (qf_, of_, sf_) with element it + 2.  The accumulation of
+  // element it - 1 runs under the probabilities of element it (formed from
+  // stale scores, and never used, on the last step).  Before the barrier it
+  // waits for element it + 1.
+  auto step = [&](int it, const uint16_t* qc, const uint16_t* oc, const float* stc,
+                  const uint16_t* qp, const uint16_t* op, uint16_t* qfill, uint16_t* ofill,
+                  float* sfill) {
+    load(it + 2, qfill, ofill, sfill);
+    const bf16x8_t pp[2] = {pf[0], pf[1]};
+    if (it < n_it) scores(it, qc, oc);
+    const uint16_t* tt = (DK ? qp : op) + opaque(tbt);
+    auto tr_half = [&](int hh, bf16x8_t (&x)[DT]) {
+#pragma unroll
+      for (int dd = 0; dd < DT; ++dd) {
+        const uint16_t* p = tt + hh * 16 * PT + dd * 32;
+        x[dd] = tr_read(p, p + 8 * PT);
+      }
+    };
+    // half hh of the accumulation under half hh of the probabilities (half
+    // the statistics live at a time); the second half's transpose reads are
+    // issued under the first half's products
+    bf16x8_t xa[DT], xb[DT];
+    tr_half(0, xa);
+#pragma unroll
+    for (int dd = 0; dd < DT; ++dd) acc[dd] = mfma(xa[dd], pp[0], acc[dd]);
+    tr_half(1, xb);
+    probs_half(0, stc);
+#pragma unroll
+    for (int k = 0; k < DT; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                     // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                     // two LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x002, (DK ? 36 : 24) / DT, 0);  // its VALU share
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int dd = 0; dd < DT; ++dd) acc[dd] = mfma(xb[dd], pp[1], acc[dd]);
+    probs_half(1, stc);
+#pragma unroll
+    for (int k = 0; k < DT; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                     // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, (DK ? 36 : 24) / DT, 0);  // its VALU share
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    probs_frags(it);
+    wait_dma_but<QT::V + OT::V + 1>();
+    tile_barrier();
+  };
+  for (int it = 1; it <= n_it; it += 4) {
+    step(it, Q1, O1, S1, Q0, O0, Q3, O3, S3);
+    step(it + 1, Q2, O2, S2, Q1, O1, Q0, O0, S0);
+    step(it + 2, Q3, O3, S3, Q2, O2, Q1, O1, S1);
+    step(it + 3, Q0, O0, S0, Q3, O3, Q2, O2, S2);
   }
   if constexpr (SPLIT) {
     // unscaled fp32 share of query head hd: part [nq][T][D]
@@ -892,29 +1045,23 @@ __global__ __launch_bounds__(256) void attn_gqa_reduce_kernel(const float* __res
   }
 }
 
-// dK holds both K and V fragments and two score chains: 248 VGPRs, two waves
-// per SIMD (one wave per SIMD was slower: 7B shape, backward 2.12 ms against
-// 1.76 ms when this was chosen).
-#ifndef MT_DK_WAVES_PER_SIMD
-#define MT_DK_WAVES_PER_SIMD 2
-#endif
-
 template <int D, bool SPLIT>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dv_kernel(
     const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dout,
-    const float* __restrict__ lse, const float* __restrict__ dsum, uint16_t* __restrict__ dqkv,
+    const float* __restrict__ stats, int stat_off, uint16_t* __restrict__ dqkv,
     float* __restrict__ part, int seq, int nq, int nkv, int64_t T, int nbh) {
-  dkdv_body<D, false, SPLIT>(qkv, dout, lse, dsum, dqkv, part, nullptr, nullptr, seq, nq, nkv, T,
-                             nbh);
+  dkdv_body<D, false, SPLIT>(qkv, dout, stats, stat_off, dqkv, part, nullptr, nullptr, seq, nq,
+                             nkv, T, nbh);
 }
 
 template <int D, bool SPLIT>
-__global__ __launch_bounds__(256, MT_DK_WAVES_PER_SIMD) void attn_bwd_dk_kernel(
+__global__ __launch_bounds__(256, 2) void attn_bwd_dk_kernel(
     const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dout,
-    const float* __restrict__ lse, const float* __restrict__ dsum, uint16_t* __restrict__ dqkv,
+    const float* __restrict__ stats, int stat_off, uint16_t* __restrict__ dqkv,
     float* __restrict__ part, const float* __restrict__ cos_t, const float* __restrict__ sin_t,
     int seq, int nq, int nkv, int64_t T, int nbh) {
-  dkdv_body<D, true, SPLIT>(qkv, dout, lse, dsum, dqkv, part, cos_t, sin_t, seq, nq, nkv, T, nbh);
+  dkdv_body<D, true, SPLIT>(qkv, dout, stats, stat_off, dqkv, part, cos_t, sin_t, seq, nq, nkv, T,
+                            nbh);
 }
 
 template <int D>
@@ -932,33 +1079,37 @@ hipError_t fwd_d(const uint16_t* qkv, uint16_t* o, float* lse, int batch, int se
 // the group's shares are added by attn_gqa_reduce_kernel.
 template <int D>
 hipError_t bwd_d(const uint16_t* qkv, const uint16_t* o, const uint16_t* dout, const float* lse,
-                 float* dsum, float* part, uint16_t* dqkv, const float* cos_t, const float* sin_t,
-                 int batch, int seq, int nq, int nkv, hipStream_t s) {
+                 float* dsum, float* lse2, float* part, uint16_t* dqkv, const float* cos_t,
+                 const float* sin_t, int batch, int seq, int nq, int nkv, hipStream_t s) {
   const int64_t T = (int64_t)batch * seq;
   const int64_t n = T * nq;
   hipLaunchKernelGGL(attn_dsum_kernel<D>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, o,
-                     dout, dsum, nq, T);
+                     dout, lse, dsum, lse2, nq, T);
   const int nblk = seq / 128;
+  // dsum and lse2 are one allocation: lse2 starts stat_off floats after dsum
+  const int stat_off = (int)(lse2 - dsum);
   if (nq == nkv) {
     const int nbh = nkv * batch;
     hipLaunchKernelGGL((attn_bwd_dv_kernel<D, false>), dim3((unsigned)(nblk * nbh)), dim3(256), 0,
-                       s, qkv, dout, lse, dsum, dqkv, nullptr, seq, nq, nkv, T, nbh);
+                       s, qkv, dout, dsum, stat_off, dqkv, nullptr, seq, nq, nkv, T, nbh);
     hipLaunchKernelGGL((attn_bwd_dk_kernel<D, false>), dim3((unsigned)(nblk * nbh)), dim3(256), 0,
-                       s, qkv, dout, lse, dsum, dqkv, nullptr, cos_t, sin_t, seq, nq, nkv, T, nbh);
+                       s, qkv, dout, dsum, stat_off, dqkv, nullptr, cos_t, sin_t, seq, nq, nkv, T,
+                       nbh);
   } else {
     const int nbh = nq * batch;
     const int64_t nv = T * nkv * (D / 4), nk = T * nkv * (cos_t ? D / 8 : D / 4);
     hipLaunchKernelGGL((attn_bwd_dv_kernel<D, true>), dim3((unsigned)(nblk * nbh)), dim3(256), 0,
-                       s, qkv, dout, lse, dsum, dqkv, part, seq, nq, nkv, T, nbh);
+                       s, qkv, dout, dsum, stat_off, dqkv, part, seq, nq, nkv, T, nbh);
     hipLaunchKernelGGL(attn_gqa_reduce_kernel<D>, dim3((unsigned)((nv + 255) / 256)), dim3(256), 0,
                        s, part, dqkv, T, nq, nkv, nq + nkv, 1.0f, nullptr, nullptr, seq);
     hipLaunchKernelGGL((attn_bwd_dk_kernel<D, true>), dim3((unsigned)(nblk * nbh)), dim3(256), 0,
-                       s, qkv, dout, lse, dsum, dqkv, part, nullptr, nullptr, seq, nq, nkv, T, nbh);
+                       s, qkv, dout, dsum, stat_off, dqkv, part, nullptr, nullptr, seq, nq, nkv, T,
+                       nbh);
     hipLaunchKernelGGL(attn_gqa_reduce_kernel<D>, dim3((unsigned)((nk + 255) / 256)), dim3(256), 0,
                        s, part, dqkv, T, nq, nkv, nq, 1.0f / sqrtf((float)D), cos_t, sin_t, seq);
   }
   hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, dim3((unsigned)(nblk * nq * batch)), dim3(256), 0, s,
-                     qkv, dout, lse, dsum, dqkv, cos_t, sin_t, seq, nq, nkv, T, nq * batch);
+                     qkv, dout, lse2, dsum, dqkv, cos_t, sin_t, seq, nq, nkv, T, nq * batch);
   return hipGetLastError();
 }
 
@@ -971,27 +1122,30 @@ hipError_t launch_attn_fwd(const uint16_t* qkv, uint16_t* o, float* lse, int bat
   return hipErrorInvalidValue;
 }
 
-// Workspace: the D rows (fp32 [nq, T]), then with grouped heads the
-// per-query-head dK/dV shares (fp32 [nq, T, d]).
+// Workspace: the D rows and lse log2(e) (fp32 [nq, T] each), then with
+// grouped heads the per-query-head dK/dV shares (fp32 [nq, T, d]).
 static size_t dsum_bytes(int64_t T, int nq) { return ((size_t)T * nq * 4 + 255) / 256 * 256; }
 
 size_t attn_bwd_workspace_bytes(int batch, int seq, int nq, int nkv, int d) {
   const int64_t T = (int64_t)batch * seq;
-  return dsum_bytes(T, nq) + (nq != nkv ? (size_t)T * nq * d * 4 : 0);
+  return 2 * dsum_bytes(T, nq) + (nq != nkv ? (size_t)T * nq * d * 4 : 0);
 }
 
 hipError_t launch_attn_bwd(const uint16_t* qkv, const uint16_t* o, const uint16_t* dout,
                            const float* lse, void* workspace, uint16_t* dqkv, int batch, int seq,
                            int nq, int nkv, int d, const float* cos_t, const float* sin_t,
                            hipStream_t s) {
+  const size_t sb = dsum_bytes((int64_t)batch * seq, nq);
   float* dsum = static_cast<float*>(workspace);
-  float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                         dsum_bytes((int64_t)batch * seq, nq));
+  float* lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + sb);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + 2 * sb);
   if (!cos_t != !sin_t) return hipErrorInvalidValue;
   if (d == 128)
-    return bwd_d<128>(qkv, o, dout, lse, dsum, part, dqkv, cos_t, sin_t, batch, seq, nq, nkv, s);
+    return bwd_d<128>(qkv, o, dout, lse, dsum, lse2, part, dqkv, cos_t, sin_t, batch, seq, nq,
+                      nkv, s);
   if (d == 64)
-    return bwd_d<64>(qkv, o, dout, lse, dsum, part, dqkv, cos_t, sin_t, batch, seq, nq, nkv, s);
+    return bwd_d<64>(qkv, o, dout, lse, dsum, lse2, part, dqkv, cos_t, sin_t, batch, seq, nq, nkv,
+                     s);
   return hipErrorInvalidValue;
 }
 
