@@ -183,9 +183,10 @@ def mfma_ceiling(iters: int = 2000, workgroups: int = 2048):
     e1.record()
     e1.synchronize()
     ms = e0.elapsed_time(e1)
-    ok = bool(torch.all(out == 8 * 16 * iters).item())
-    flop = workgroups * 4 * 8 * iters * 32768.0
-    return {"kernel": "mfma_peak (v_mfma_f32_32x32x16_bf16 chains, register operands)",
+    ch = mt.mtk_mfma_peak_chains()
+    ok = bool(torch.all(out == ch * 16 * iters).item())
+    flop = workgroups * 4 * ch * iters * 32768.0
+    return {"kernel": f"mfma_peak ({ch} v_mfma_f32_32x32x16_bf16 chains per wave, register operands)",
             "ms": ms, "TFLOPs": flop / ms / 1e9, "frac_of_nominal": flop / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS,
             "output_checked": ok, "workgroups": workgroups, "iters": iters}
 

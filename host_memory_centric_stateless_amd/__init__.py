@@ -160,6 +160,7 @@ _SIGS = {
     "mtk_cross_entropy": ([_P, _I64, _P, _I64, _I32, _F, _I64, _P, _I64, _P, _P, _P], C.c_int),
     "mtk_copy": ([_P, _P, C.c_size_t, _I32, _P], C.c_int),
     "mtk_mfma_peak": ([_P, _I32, _I32, _P], C.c_int),
+    "mtk_mfma_peak_chains": ([], C.c_int32),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -418,6 +419,10 @@ def mtk_cross_entropy(logits, ld, labels, T, V, grad_scale, n_valid, dlogits, ld
 
 def mtk_mfma_peak(out, workgroups, iters, stream=None):
     _check(_lib.mtk_mfma_peak(_ptr(out), workgroups, iters, _stream(stream)), "mtk_mfma_peak")
+
+
+def mtk_mfma_peak_chains() -> int:
+    return _lib.mtk_mfma_peak_chains()
 
 
 def mtk_copy(dst, src, nbytes, workgroups, stream=None):

@@ -743,40 +743,33 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
                     g);
 }
 
-// ---------------------------------------------------- backward: dK, dV
-// Key block outer (4 waves x 32 keys, one key per lane), so grouped query
-// heads are summed in a fixed order without atomics (each query head's share
-// in fp32, added by attn_gqa_reduce_kernel).  The 32-row Q and dO tiles after
-// the block (and their D and lse log2(e) rows) stream through padded LDS,
-// four stages, one barrier per tile.  Per tile a wave forms S = Q k (and dP = dO v for dK) on the matrix
-// cores, then P (dV) or dS = P (dP - D) (dK) on the VALU while the previous
-// tile's dV^T += dO^T P or dK^T += Q^T dS (dO^T, Q^T through transpose reads)
-// runs on the matrix cores.  dK and dV are two launches of this kernel (DK
-// selects which): each then holds one accumulator and fits two waves per
-// SIMD, at the price of forming P in both.  The tile read both ways (Q for
-// dK) carries a 48-byte pad, a tile read by rows a 16-byte one, a tile read
-// by transposes a 64-byte one.  Tile it's step fills stage (it + 2) % 4.
-template <int D, bool DK, bool SPLIT>
-__device__ __forceinline__ void dkdv_body(const uint16_t* __restrict__ qkv,
-                                          const uint16_t* __restrict__ dout,
-                                          const float* __restrict__ stats, int stat_off,
-                                          uint16_t* __restrict__ dqkv, float* __restrict__ part,
-                                          const float* __restrict__ cos_t,
-                                          const float* __restrict__ sin_t, int seq, int nq,
-                                          int nkv, int64_t T, int nbh) {
-  constexpr int BQ = 32, KS = D / 16, DT = D / 32;
-  constexpr int QPE = DK ? 24 : 8, OPE = DK ? 8 : 32;  // row pads, elements
-  using QT = PTile<D, BQ, 2 * QPE>;
-  using OT = PTile<D, BQ, 2 * OPE>;
-  constexpr int PT = D + (DK ? QPE : OPE);  // pitch of the transposed tile
-  __shared__ __attribute__((aligned(16))) uint16_t Q0[QT::ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t Q1[QT::ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t Q2[QT::ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t Q3[QT::ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t O0[OT::ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t O1[OT::ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t O2[OT::ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t O3[OT::ELEMS];
+// ------------------------------------------------ backward: dK and dV fused
+// One launch for both: key block outer (4 waves x 32 keys, one key per lane,
+// one wave per SIMD so that a wave holds K, V and both accumulators), the
+// 32-row Q and dO tiles after the block (and their D and lse log2(e) rows)
+// streaming through padded LDS, four stages, one barrier per tile.  Per tile a
+// wave forms S = Q k and dP = dO v on the matrix cores (two chains), then P
+// and dS = P (dP - D) on the VALU while the previous tile's dV^T += dO^T P and
+// dK^T += Q^T dS (eight accumulator chains) run on the matrix cores.  Both
+// tiles are read by rows and by transposes: 48-byte pads.  Grouped heads
+// (SPLIT): one workgroup per query head, writing fp32 shares of dK and dV.
+template <int D, bool SPLIT>
+__global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
+    const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dout,
+    const float* __restrict__ stats, int stat_off, uint16_t* __restrict__ dqkv,
+    float* __restrict__ part_k, float* __restrict__ part_v, const float* __restrict__ cos_t,
+    const float* __restrict__ sin_t, int seq, int nq, int nkv, int64_t T, int nbh) {
+  constexpr int BQ = 32, KS = D / 16, DT = D / 32, PE = 24;
+  using TT = PTile<D, BQ, 2 * PE>;
+  constexpr int PT = D + PE;
+  __shared__ __attribute__((aligned(16))) uint16_t Q0[TT::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t Q1[TT::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t Q2[TT::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t Q3[TT::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t O0[TT::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t O1[TT::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t O2[TT::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t O3[TT::ELEMS];
   // per stage: D of the tile's 32 queries, then their lse log2(e)
   __shared__ __attribute__((aligned(16))) float S0[64];
   __shared__ __attribute__((aligned(16))) float S1[64];
@@ -788,9 +781,6 @@ __device__ __forceinline__ void dkdv_body(const uint16_t* __restrict__ qkv,
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, known uniform
   int kvb, bh;
   attn_order(blockIdx.x, seq / 128, nbh, false, kvb, bh);
-  // SPLIT (grouped heads): one workgroup per query head hd, writing that
-  // head's fp32 share of dK or dV.  Otherwise nq == nkv: one workgroup per
-  // head, writing dK or dV itself.
   const int nh = SPLIT ? nq : nkv;
   const int b = bh / nh, hd = bh % nh;
   const int kvh = SPLIT ? hd / (nq / nkv) : hd;
@@ -804,22 +794,24 @@ __device__ __forceinline__ void dkdv_body(const uint16_t* __restrict__ qkv,
 
   const int kw0 = kvb * 128 + w * 32;
   const int kv = kw0 + (lane & 31);
-  bf16x8_t kf[KS], vf[DK ? KS : 1];
+  bf16x8_t kf[KS], vf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     kf[ks] = ld_frag(Kp + (row0 + kv) * ld + ks * 16 + g * 8);
-    if constexpr (DK) vf[ks] = ld_frag(Vp + (row0 + kv) * ld + ks * 16 + g * 8);
+    vf[ks] = ld_frag(Vp + (row0 + kv) * ld + ks * 16 + g * 8);
   }
-  f32x16_t acc[DT];
+  f32x16_t dk[DT], dv[DT];
 #pragma unroll
-  for (int dd = 0; dd < DT; ++dd) zero(acc[dd]);
+  for (int dd = 0; dd < DT; ++dd) {
+    zero(dk[dd]);
+    zero(dv[dd]);
+  }
   const int qt0 = kvb * 4, nqt = seq / BQ;
   const int n_it = nqt - qt0;  // query tiles from the block's first (a multiple of 4)
-  const int first = qt0 + w;  // the wave's first query tile that sees one of its keys (diagonal)
-  const int rbq = row_base<D, QPE>(lane), rbo = row_base<D, OPE>(lane);
-  const int tbt = tr_base<D, DK ? QPE : OPE>(lane);
-  const TileDma<D, BQ, 2 * QPE> qdma(ld, w, lane);
-  const TileDma<D, BQ, 2 * OPE> odma(ldo, w, lane);
+  const int first = qt0 + w;   // the wave's first query tile that sees one of its keys (diagonal)
+  const int rb = row_base<D, PE>(lane), tb = tr_base<D, PE>(lane);
+  const TileDma<D, BQ, 2 * PE> qdma(ld, w, lane);
+  const TileDma<D, BQ, 2 * PE> odma(ldo, w, lane);
   // statistics: lane l < 32 loads D of query l of the tile, lane l >= 32 its lse log2(e)
   const uint32_t soff = (uint32_t)(((lane < 32) ? lane : stat_off + lane - 32) * 4);
   const int sspan = (stat_off + 32) * 4;
@@ -843,7 +835,7 @@ __device__ __forceinline__ void dkdv_body(const uint16_t* __restrict__ qkv,
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     settle(kf[ks]);
-    if constexpr (DK) settle(vf[ks]);
+    settle(vf[ks]);
   }
   wait_dma();
   __syncthreads();
@@ -851,30 +843,28 @@ __device__ __forceinline__ void dkdv_body(const uint16_t* __restrict__ qkv,
   f32x16_t sc, dp;
   zero(sc);
   zero(dp);
-  bf16x8_t pf[2];  // P (dV) or dS (dK) of the latest tile, rounded to bf16
-  // S (and dP) of sequence element it from stages qs, os, with the causal
-  // mask on the wave's diagonal tile; then P or dS from the statistics st.
-  // Tiles before the wave's first give zeros.
+  bf16x8_t pP[2], pS[2];  // P and dS of the latest tile, rounded to bf16 (B fragments)
+  // S and dP of query tile it from stages qs, os, with the causal mask on
+  // the wave's diagonal tile.  Tiles before the wave's first are skipped
+  // (their P and dS become zeros).
   auto scores = [&](int it, const uint16_t* qs, const uint16_t* os) {
     const int i = qt0 + it;
     if (i < first) return;
-    const uint16_t* qa = qs + opaque(rbq);
-    const uint16_t* oa = os + opaque(rbo);
-    bf16x8_t af[KS], bf[DK ? KS : 1];
+    const uint16_t* qa = qs + opaque(rb);
+    const uint16_t* oa = os + opaque(rb);
+    bf16x8_t af[KS], bf[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       af[ks] = ld_frag(qa + ks * 16);
-      if constexpr (DK) bf[ks] = ld_frag(oa + ks * 16);
+      bf[ks] = ld_frag(oa + ks * 16);
     }
     zero(sc);
-    if constexpr (DK) zero(dp);
+    zero(dp);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       sc = mfma(af[ks], kf[ks], sc);
-      if constexpr (DK) dp = mfma(bf[ks], vf[ks], dp);
+      dp = mfma(bf[ks], vf[ks], dp);
     }
-    // the transpose reads that follow are issued after these products (the
-    // row fragments are then dead: fewer live registers)
     __builtin_amdgcn_sched_barrier(0);
     if (i == first) {
 #pragma unroll
@@ -882,87 +872,92 @@ __device__ __forceinline__ void dkdv_body(const uint16_t* __restrict__ qkv,
         if (kv > i * BQ + (r >> 2) * 8 + g * 4 + (r & 3)) sc[r] = -INFINITY;
     }
   };
-  // Rows rr = 2 h, 2 h + 1 of the lane's probabilities (P, or dS for dK) of
-  // sequence element it, packed into u[4 h .. 4 h + 3]; then the B fragments
-  // (zeros before the wave's first tile).
-  uint32_t u[8];
+  // Rows rr = 2 h, 2 h + 1 of the lane's P and dS, packed into up / us.
+  uint32_t up[8], us[8];
   auto probs_half = [&](int h, const float* st) {
 #pragma unroll
     for (int rr = 2 * h; rr < 2 * h + 2; ++rr) {
       const float4 l4 = *reinterpret_cast<const float4*>(st + 32 + rr * 8 + g * 4);
-      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-      float dv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-      if constexpr (DK) {
-        const float4 d4 = *reinterpret_cast<const float4*>(st + rr * 8 + g * 4);
-        dv[0] = d4.x; dv[1] = d4.y; dv[2] = d4.z; dv[3] = d4.w;
-      }
-      float v[4];
+      const float4 d4 = *reinterpret_cast<const float4*>(st + rr * 8 + g * 4);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dvv[4] = {d4.x, d4.y, d4.z, d4.w};
+      float pv[4], sv[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = rr * 4 + e;
-        const float pr = exp2_hw(fmaf(sc[r], sl2, -lv[e]));
-        v[e] = DK ? pr * (dp[r] - dv[e]) : pr;
+        pv[e] = exp2_hw(fmaf(sc[r], sl2, -lv[e]));
+        sv[e] = pv[e] * (dp[r] - dvv[e]);
       }
-      u[2 * rr] = pack_bf2(v[0], v[1]);
-      u[2 * rr + 1] = pack_bf2(v[2], v[3]);
+      up[2 * rr] = pack_bf2(pv[0], pv[1]);
+      up[2 * rr + 1] = pack_bf2(pv[2], pv[3]);
+      us[2 * rr] = pack_bf2(sv[0], sv[1]);
+      us[2 * rr + 1] = pack_bf2(sv[2], sv[3]);
     }
   };
-  auto probs_frags = [&](int it) {
-    const bool live = qt0 + it >= first;
-    pf[0] = as_frag(live ? u32x4{u[0], u[1], u[2], u[3]} : u32x4{0, 0, 0, 0});
-    pf[1] = as_frag(live ? u32x4{u[4], u[5], u[6], u[7]} : u32x4{0, 0, 0, 0});
+  auto frags = [&](int it) {
+    if (qt0 + it < first) {  // a tile before the wave's first: no contribution
+#pragma unroll
+      for (int k = 0; k < 8; ++k) up[k] = us[k] = 0u;
+    }
+    pP[0] = as_frag(u32x4{up[0], up[1], up[2], up[3]});
+    pP[1] = as_frag(u32x4{up[4], up[5], up[6], up[7]});
+    pS[0] = as_frag(u32x4{us[0], us[1], us[2], us[3]});
+    pS[1] = as_frag(u32x4{us[4], us[5], us[6], us[7]});
   };
   scores(0, Q0, O0);
   probs_half(0, S0);
   probs_half(1, S0);
-  probs_frags(0);
+  frags(0);
 
-  // Step it (1 .. n_it): element it in stages (qc, oc, sc_), it - 1 in
-  // (qp, op); fills (qf_, of_, sf_) with element it + 2.  The accumulation of
-  // element it - 1 runs under the probabilities of element it (formed from
-  // stale scores, and never used, on the last step).  Before the barrier it
-  // waits for element it + 1.
+  // Step it (1 .. n_it): tile it in stages (qc, oc, stc), it - 1 in (qp, op);
+  // fills (qfill, ofill, sfill) with tile it + 2.  The accumulation of tile
+  // it - 1 runs under the VALU of tile it (formed from stale scores, and never
+  // used, on the last step).  Before the barrier it waits for tile it + 1.
   auto step = [&](int it, const uint16_t* qc, const uint16_t* oc, const float* stc,
                   const uint16_t* qp, const uint16_t* op, uint16_t* qfill, uint16_t* ofill,
                   float* sfill) {
     load(it + 2, qfill, ofill, sfill);
-    const bf16x8_t pp[2] = {pf[0], pf[1]};
+    const bf16x8_t pp[2] = {pP[0], pP[1]}, ps[2] = {pS[0], pS[1]};
     if (it < n_it) scores(it, qc, oc);
-    const uint16_t* tt = (DK ? qp : op) + opaque(tbt);
-    auto tr_half = [&](int hh, bf16x8_t (&x)[DT]) {
+    const uint16_t* qt = qp + opaque(tb);
+    const uint16_t* ot = op + opaque(tb);
+    auto tr_half = [&](int hh, bf16x8_t (&xq)[DT], bf16x8_t (&xo)[DT]) {
 #pragma unroll
       for (int dd = 0; dd < DT; ++dd) {
-        const uint16_t* p = tt + hh * 16 * PT + dd * 32;
-        x[dd] = tr_read(p, p + 8 * PT);
+        const int o = hh * 16 * PT + dd * 32;
+        xq[dd] = tr_read(qt + o, qt + o + 8 * PT);
+        xo[dd] = tr_read(ot + o, ot + o + 8 * PT);
       }
     };
-    // half hh of the accumulation under half hh of the probabilities (half
-    // the statistics live at a time); the second half's transpose reads are
-    // issued under the first half's products
-    bf16x8_t xa[DT], xb[DT];
-    tr_half(0, xa);
+    bf16x8_t xq0[DT], xo0[DT], xq1[DT], xo1[DT];
+    tr_half(0, xq0, xo0);
 #pragma unroll
-    for (int dd = 0; dd < DT; ++dd) acc[dd] = mfma(xa[dd], pp[0], acc[dd]);
-    tr_half(1, xb);
+    for (int dd = 0; dd < DT; ++dd) {
+      dv[dd] = mfma(xo0[dd], pp[0], dv[dd]);
+      dk[dd] = mfma(xq0[dd], ps[0], dk[dd]);
+    }
+    tr_half(1, xq1, xo1);
     probs_half(0, stc);
 #pragma unroll
-    for (int k = 0; k < DT; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                     // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                     // two LDS reads
-      __builtin_amdgcn_sched_group_barrier(0x002, (DK ? 36 : 24) / DT, 0);  // its VALU share
+    for (int k = 0; k < 2 * DT; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);           // two LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x002, 40 / (2 * DT), 0);  // its VALU share
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int dd = 0; dd < DT; ++dd) acc[dd] = mfma(xb[dd], pp[1], acc[dd]);
+    for (int dd = 0; dd < DT; ++dd) {
+      dv[dd] = mfma(xo1[dd], pp[1], dv[dd]);
+      dk[dd] = mfma(xq1[dd], ps[1], dk[dd]);
+    }
     probs_half(1, stc);
 #pragma unroll
-    for (int k = 0; k < DT; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                     // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, (DK ? 36 : 24) / DT, 0);  // its VALU share
+    for (int k = 0; k < 2 * DT; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 40 / (2 * DT), 0);  // its VALU share
     }
     __builtin_amdgcn_sched_barrier(0);
-    probs_frags(it);
-    wait_dma_but<QT::V + OT::V + 1>();
+    frags(it);
+    wait_dma_but<2 * TT::V + 1>();
     tile_barrier();
   };
   for (int it = 1; it <= n_it; it += 4) {
@@ -972,20 +967,27 @@ __device__ __forceinline__ void dkdv_body(const uint16_t* __restrict__ qkv,
     step(it + 3, Q0, O0, S0, Q3, O3, Q2, O2, S2);
   }
   if constexpr (SPLIT) {
-    // unscaled fp32 share of query head hd: part [nq][T][D]
-    float* dst = part + ((int64_t)hd * T + row0 + kv) * D;
+    // unscaled fp32 shares of query head hd: part_k, part_v [nq][T][D]
+    float* dsk = part_k + ((int64_t)hd * T + row0 + kv) * D;
+    float* dsv = part_v + ((int64_t)hd * T + row0 + kv) * D;
 #pragma unroll
     for (int dd = 0; dd < DT; ++dd)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-        *reinterpret_cast<float4*>(dst + dd * 32 + rr * 8 + g * 4) =
-            make_float4(acc[dd][rr * 4 + 0], acc[dd][rr * 4 + 1], acc[dd][rr * 4 + 2],
-                        acc[dd][rr * 4 + 3]);
+      for (int rr = 0; rr < 4; ++rr) {
+        *reinterpret_cast<float4*>(dsk + dd * 32 + rr * 8 + g * 4) =
+            make_float4(dk[dd][rr * 4 + 0], dk[dd][rr * 4 + 1], dk[dd][rr * 4 + 2],
+                        dk[dd][rr * 4 + 3]);
+        *reinterpret_cast<float4*>(dsv + dd * 32 + rr * 8 + g * 4) =
+            make_float4(dv[dd][rr * 4 + 0], dv[dd][rr * 4 + 1], dv[dd][rr * 4 + 2],
+                        dv[dd][rr * 4 + 3]);
+      }
   } else {
     // dK is a gradient with respect to rotated keys (rotated back here); dV is not
-    store_head_row<D>(acc, dqkv + (row0 + kv) * ld + (int64_t)(DK ? nq : nq + nkv) * D + kvh * D,
-                      DK ? 1.0f / sqrtf((float)D) : 1.0f, DK ? cos_t : nullptr,
-                      DK ? sin_t : nullptr, kv, g);
+    uint16_t* base = dqkv + (row0 + kv) * ld;
+    store_head_row<D>(dk, base + (int64_t)nq * D + kvh * D, 1.0f / sqrtf((float)D), cos_t, sin_t,
+                      kv, g);
+    store_head_row<D>(dv, base + (int64_t)(nq + nkv) * D + kvh * D, 1.0f, nullptr, nullptr, kv,
+                      g);
   }
 }
 
@@ -1045,25 +1047,6 @@ __global__ __launch_bounds__(256) void attn_gqa_reduce_kernel(const float* __res
   }
 }
 
-template <int D, bool SPLIT>
-__global__ __launch_bounds__(256, 2) void attn_bwd_dv_kernel(
-    const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dout,
-    const float* __restrict__ stats, int stat_off, uint16_t* __restrict__ dqkv,
-    float* __restrict__ part, int seq, int nq, int nkv, int64_t T, int nbh) {
-  dkdv_body<D, false, SPLIT>(qkv, dout, stats, stat_off, dqkv, part, nullptr, nullptr, seq, nq,
-                             nkv, T, nbh);
-}
-
-template <int D, bool SPLIT>
-__global__ __launch_bounds__(256, 2) void attn_bwd_dk_kernel(
-    const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dout,
-    const float* __restrict__ stats, int stat_off, uint16_t* __restrict__ dqkv,
-    float* __restrict__ part, const float* __restrict__ cos_t, const float* __restrict__ sin_t,
-    int seq, int nq, int nkv, int64_t T, int nbh) {
-  dkdv_body<D, true, SPLIT>(qkv, dout, stats, stat_off, dqkv, part, cos_t, sin_t, seq, nq, nkv, T,
-                            nbh);
-}
-
 template <int D>
 hipError_t fwd_d(const uint16_t* qkv, uint16_t* o, float* lse, int batch, int seq, int nq, int nkv,
                  hipStream_t s) {
@@ -1090,21 +1073,18 @@ hipError_t bwd_d(const uint16_t* qkv, const uint16_t* o, const uint16_t* dout, c
   const int stat_off = (int)(lse2 - dsum);
   if (nq == nkv) {
     const int nbh = nkv * batch;
-    hipLaunchKernelGGL((attn_bwd_dv_kernel<D, false>), dim3((unsigned)(nblk * nbh)), dim3(256), 0,
-                       s, qkv, dout, dsum, stat_off, dqkv, nullptr, seq, nq, nkv, T, nbh);
-    hipLaunchKernelGGL((attn_bwd_dk_kernel<D, false>), dim3((unsigned)(nblk * nbh)), dim3(256), 0,
-                       s, qkv, dout, dsum, stat_off, dqkv, nullptr, cos_t, sin_t, seq, nq, nkv, T,
-                       nbh);
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, false>), dim3((unsigned)(nblk * nbh)), dim3(256), 0,
+                       s, qkv, dout, dsum, stat_off, dqkv, nullptr, nullptr, cos_t, sin_t, seq, nq,
+                       nkv, T, nbh);
   } else {
     const int nbh = nq * batch;
+    float* part_v = part + T * nq * D;
     const int64_t nv = T * nkv * (D / 4), nk = T * nkv * (cos_t ? D / 8 : D / 4);
-    hipLaunchKernelGGL((attn_bwd_dv_kernel<D, true>), dim3((unsigned)(nblk * nbh)), dim3(256), 0,
-                       s, qkv, dout, dsum, stat_off, dqkv, part, seq, nq, nkv, T, nbh);
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, true>), dim3((unsigned)(nblk * nbh)), dim3(256), 0,
+                       s, qkv, dout, dsum, stat_off, dqkv, part, part_v, nullptr, nullptr, seq, nq,
+                       nkv, T, nbh);
     hipLaunchKernelGGL(attn_gqa_reduce_kernel<D>, dim3((unsigned)((nv + 255) / 256)), dim3(256), 0,
-                       s, part, dqkv, T, nq, nkv, nq + nkv, 1.0f, nullptr, nullptr, seq);
-    hipLaunchKernelGGL((attn_bwd_dk_kernel<D, true>), dim3((unsigned)(nblk * nbh)), dim3(256), 0,
-                       s, qkv, dout, dsum, stat_off, dqkv, part, nullptr, nullptr, seq, nq, nkv, T,
-                       nbh);
+                       s, part_v, dqkv, T, nq, nkv, nq + nkv, 1.0f, nullptr, nullptr, seq);
     hipLaunchKernelGGL(attn_gqa_reduce_kernel<D>, dim3((unsigned)((nk + 255) / 256)), dim3(256), 0,
                        s, part, dqkv, T, nq, nkv, nq, 1.0f / sqrtf((float)D), cos_t, sin_t, seq);
   }
@@ -1123,12 +1103,12 @@ hipError_t launch_attn_fwd(const uint16_t* qkv, uint16_t* o, float* lse, int bat
 }
 
 // Workspace: the D rows and lse log2(e) (fp32 [nq, T] each), then with
-// grouped heads the per-query-head dK/dV shares (fp32 [nq, T, d]).
+// grouped heads the per-query-head dK and dV shares (fp32 [nq, T, d] each).
 static size_t dsum_bytes(int64_t T, int nq) { return ((size_t)T * nq * 4 + 255) / 256 * 256; }
 
 size_t attn_bwd_workspace_bytes(int batch, int seq, int nq, int nkv, int d) {
   const int64_t T = (int64_t)batch * seq;
-  return 2 * dsum_bytes(T, nq) + (nq != nkv ? (size_t)T * nq * d * 4 : 0);
+  return 2 * dsum_bytes(T, nq) + (nq != nkv ? 2 * (size_t)T * nq * d * 4 : 0);
 }
 
 hipError_t launch_attn_bwd(const uint16_t* qkv, const uint16_t* o, const uint16_t* dout,

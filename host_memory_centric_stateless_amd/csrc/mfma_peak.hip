@@ -10,12 +10,16 @@ namespace {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int CHAINS = 8;  // independent accumulators per wave keep the MFMA pipe full
+// Independent accumulators per wave.  Two (with the other waves of the SIMD)
+// keep the pipe full; a single dependent chain issues at about 0.6 of the
+// rate with one wave per SIMD, and eight per wave measured lower than two
+// (2181 against 2481 TFLOP/s at full occupancy).
+constexpr int CHAINS = 2;
 
 // Every operand element is 1.0, so each v_mfma_f32_32x32x16_bf16 adds 16 to
 // every accumulator element: after `iters` rounds each element is 16 iters
 // (exact in fp32 while 16 iters < 2^24).  out[wave] = sum over the chains of
-// lane 0's first element = CHAINS * 16 * iters.
+// lane 0's first element = CHAINS * 16 * iters (mtk_mfma_peak_chains()).
 __global__ __launch_bounds__(256) void mfma_peak_kernel(float* __restrict__ out, int iters) {
   const __bf16 one = (__bf16)1.0f;
   const bf16x8_t a = {one, one, one, one, one, one, one, one};
@@ -39,6 +43,8 @@ __global__ __launch_bounds__(256) void mfma_peak_kernel(float* __restrict__ out,
 
 }  // namespace
 }  // namespace mt
+
+extern "C" int32_t mtk_mfma_peak_chains(void) { return mt::CHAINS; }
 
 extern "C" mt_status mtk_mfma_peak(float* out, int32_t workgroups, int32_t iters, void* stream) {
   if (!out || workgroups < 1 || workgroups > 65535 || iters < 1 || iters > (1 << 19))

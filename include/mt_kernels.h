@@ -174,13 +174,15 @@ mt_status mtk_cross_entropy(const float* logits, int64_t ld, const int32_t* labe
                             int64_t ld_d, float* loss_rows, float* loss_out, void* stream);
 
 /* MFMA ceiling probe (measurement only, not part of a training step):
- * `workgroups` workgroups of 4 waves, each wave running 8 independent chains
- * of `iters` v_mfma_f32_32x32x16_bf16 on register operands of 1.0.  Writes
- * out[4 * workgroups] (device fp32), every element 8 * 16 * iters, so the
- * caller can check the work was done.  Algorithmic work: workgroups * 4 * 8 *
+ * `workgroups` workgroups of 4 waves, each wave running C =
+ * mtk_mfma_peak_chains() independent chains of `iters`
+ * v_mfma_f32_32x32x16_bf16 on register operands of 1.0.  Writes
+ * out[4 * workgroups] (device fp32), every element C * 16 * iters, so the
+ * caller can check the work was done.  Algorithmic work: workgroups * 4 * C *
  * iters * 32768 flop.  MT_E_ARG for workgroups outside 1..65535 or iters
  * outside 1..2^19. */
 mt_status mtk_mfma_peak(float* out, int32_t workgroups, int32_t iters, void* stream);
+int32_t mtk_mfma_peak_chains(void);
 
 /* Copy `bytes` (multiple of 16, both pointers 16-byte aligned) with a copy
  * kernel of `workgroups` 256-thread workgroups instead of the copy engine.
