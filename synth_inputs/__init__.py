@@ -102,9 +102,10 @@ MOE_PRESETS: Dict[str, ModelConfig] = {
                                 n_experts=8, top_k=2, expert_ffn=1408, moe_every=2,
                                 ckpt_interval=2),
     # 7B-shaped attention with every second block a mixture of 8 experts (top 2) of width
-    # 2752 (a quarter of the dense FFN), 8 layers, 2 x 4096 tokens per micro-batch
+    # 2816 (about a quarter of the dense FFN, a multiple of 128), 8 layers, 2 x 4096 tokens
+    # per micro-batch
     "M3": PRESETS["C3"].replace(name="moe-7B-shape-8L-e8", n_layers=8, micro_batch=2,
-                                grad_accum=1, n_experts=8, top_k=2, expert_ffn=2752,
+                                grad_accum=1, n_experts=8, top_k=2, expert_ffn=2816,
                                 moe_every=2, ckpt_interval=4),
 }
 
