@@ -839,9 +839,8 @@ void worker_main(mt_ctx* c) {
           accumulate(*c->pool, b.grad + j.e0, c->hslab[j.slab], j.n, j.add);
       } else {
         const int64_t h = c->p.c.hidden;
-        if (!j.add) memset(c->embed.grad, 0, (size_t)c->embed.n * sizeof(float));
-        embed_scatter(*c->pool, c->embed.grad, j.tok.data(), (int64_t)j.tok.size(), h,
-                      c->dx0_stage[j.parity]);
+        embed_scatter(*c->pool, c->embed.grad, c->embed.n / h, j.tok.data(),
+                      (int64_t)j.tok.size(), h, c->dx0_stage[j.parity], j.add);
       }
       const double t1 = now_s();
       if (!fused) {  // the staging memory is consumed: hand it back before the optimizer runs

@@ -252,15 +252,31 @@ void embed_gather(ThreadPool& pool, const float* emb, const int32_t* tok, int64_
   });
 }
 
-void embed_scatter(ThreadPool& pool, float* demb, const int32_t* tok, int64_t T, int64_t h,
-                   const float* dx0) {
-  const int64_t cols = 64;
-  pool.run((h + cols - 1) / cols, [&](int64_t k) {
-    const int64_t c0 = k * cols, c1 = std::min(h, c0 + cols);
-    for (int64_t t = 0; t < T; ++t) {
-      float* __restrict dst = demb + (int64_t)tok[t] * h;
-      const float* __restrict s = dx0 + t * h;
-      for (int64_t c = c0; c < c1; ++c) dst[c] += s[c];
+// The tokens are ordered by id with a stable counting sort, so that a task
+// owns a run of embedding rows and adds into each of them its tokens' rows
+// of dx0 in token order: per element the same additions in the same order as
+// one pass over t, with whole rows read and written (a split by columns read
+// dx0 in 256-byte pieces at a 16 KB stride).
+void embed_scatter(ThreadPool& pool, float* demb, int64_t rows, const int32_t* tok, int64_t T,
+                   int64_t h, const float* dx0, bool add) {
+  std::vector<int64_t> start((size_t)rows + 1, 0);
+  for (int64_t t = 0; t < T; ++t) ++start[(size_t)tok[t] + 1];
+  for (int64_t r = 0; r < rows; ++r) start[(size_t)r + 1] += start[(size_t)r];
+  std::vector<int32_t> order((size_t)T);
+  {
+    std::vector<int64_t> next(start.begin(), start.end() - 1);
+    for (int64_t t = 0; t < T; ++t) order[(size_t)next[(size_t)tok[t]]++] = (int32_t)t;
+  }
+  const int64_t nb = std::min<int64_t>(rows, 4 * (int64_t)pool.size());
+  pool.run(nb, [&](int64_t k) {
+    const int64_t r0 = rows * k / nb, r1 = rows * (k + 1) / nb;
+    if (!add) memset(demb + r0 * h, 0, (size_t)((r1 - r0) * h) * sizeof(float));
+    for (int64_t r = r0; r < r1; ++r) {
+      float* __restrict dst = demb + r * h;
+      for (int64_t i = start[(size_t)r]; i < start[(size_t)r + 1]; ++i) {
+        const float* __restrict s = dx0 + (int64_t)order[(size_t)i] * h;
+        for (int64_t c = 0; c < h; ++c) dst[c] += s[c];
+      }
     }
   });
 }

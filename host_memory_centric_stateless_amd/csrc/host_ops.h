@@ -51,9 +51,10 @@ void accumulate_bf16(ThreadPool& pool, float* grad, const uint16_t* src, int64_t
 // x0[t, :] = emb[tok[t], :]
 void embed_gather(ThreadPool& pool, const float* emb, const int32_t* tok, int64_t T, int64_t h,
                   float* x0);
-// demb[tok[t], :] += dx0[t, :] in token order (columns split across threads).
-void embed_scatter(ThreadPool& pool, float* demb, const int32_t* tok, int64_t T, int64_t h,
-                   const float* dx0);
+// demb[tok[t], :] += dx0[t, :] in token order, for demb of `rows` rows
+// (zeroed first unless add).  Token ids must lie in [0, rows).
+void embed_scatter(ThreadPool& pool, float* demb, int64_t rows, const int32_t* tok, int64_t T,
+                   int64_t h, const float* dx0, bool add);
 void rope_table(int seq, int d, float base, float* cos_out, float* sin_out);
 
 }  // namespace mt
