@@ -170,7 +170,7 @@ def head_gemm_shapes(cfg, sess_req=None):
     return [("gemm_tn_bf16 dWhead", mt.MT_GEMM_TN, mt.MT_EPI_BF16, rows, h, T)]
 
 
-def mfma_ceiling(iters: int = 2000, workgroups: int = 2048):
+def mfma_ceiling(iters: int = 8000, workgroups: int = 2048):
     """The MFMA rate of a chain of register-operand MFMAs (mtk_mfma_peak),
     with its output checked: the ceiling next to the nominal peak."""
     import torch

@@ -12,8 +12,7 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 // Independent accumulators per wave.  Two (with the other waves of the SIMD)
 // keep the pipe full; a single dependent chain issues at about 0.6 of the
-// rate with one wave per SIMD, and eight per wave measured lower than two
-// (2181 against 2481 TFLOP/s at full occupancy).
+// rate when it is the only wave on its SIMD.
 constexpr int CHAINS = 2;
 
 // Every operand element is 1.0, so each v_mfma_f32_32x32x16_bf16 adds 16 to
