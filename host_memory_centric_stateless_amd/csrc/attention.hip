@@ -11,18 +11,23 @@
 // Computing the transposed scores S^T = K Q^T puts one query per lane, so the
 // softmax statistics of a query are lane-local (plus the partner lane
 // lane^32).  The probabilities then feed the next product directly as the B
-// operand: element e of a lane's 8-value fragment for k-step (i, hh) is row
-// i*32 + 16*hh + 8*(e/4) + 4*(lane/32) + e%4 -- a permutation of the 16
+// operand: element e of a lane's 8-value fragment for k-step hh of a 32-row
+// tile is row 16*hh + 8*(e/4) + 4*(lane/32) + e%4 -- a permutation of the 16
 // reduction indices that the A operand (read from a transposed LDS tile with
 // two 8-byte reads) follows exactly, so the sum is unchanged.
 //
+// Tiles of 32 rows go from global memory straight into padded LDS stages
+// (buffer_load ... lds), loaded two or three tiles ahead with partial waits
+// and fence-free barriers; the grid runs the heaviest blocks first, each
+// head's workgroups on one XCD.
+//
 // Backward is deterministic, with no floating-point atomics: D = rowsum(dO*O)
-// per query (attn_dsum_kernel); dV and dK, each its own launch with the key
-// block outer (one workgroup per kv head walking its group's query heads in
-// order, or with grouped heads one per query head writing fp32 shares that
-// attn_gqa_reduce_kernel adds in query-head order); dQ with the query block
-// outer.  Given RoPE tables, dQ and dK leave the kernels rotated back to the
-// pre-rotation q and k in fp32, so each is rounded to bf16 once.
+// and lse log2(e) per query (attn_dsum_kernel); dK and dV together in one
+// launch with the key block outer (one workgroup per head, or with grouped
+// heads one per query head writing fp32 shares that attn_gqa_reduce_kernel
+// adds in query-head order); dQ with the query block outer.  Given RoPE
+// tables, dQ and dK leave the kernels rotated back to the pre-rotation q and
+// k in fp32, so each is rounded to bf16 once.
 #include "common.h"
 
 namespace mt {
