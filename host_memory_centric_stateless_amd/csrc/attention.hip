@@ -755,7 +755,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
 // streaming through padded LDS, four stages, one barrier per tile.  Per tile a
 // wave forms S = Q k and dP = dO v on the matrix cores (two chains), then P
 // and dS = P (dP - D) on the VALU while the previous tile's dV^T += dO^T P and
-// dK^T += Q^T dS (eight accumulator chains) run on the matrix cores.  Both
+// dK^T += Q^T dS (eight accumulator chains) run on the matrix cores.  A step
+// issues its LDS fragment reads ahead of their MFMAs: this tile's row
+// fragments first, then the previous tile's transposes, two per MFMA of the S
+// and dP chains, so that no MFMA waits on a read issued just before it.  Both
 // tiles are read by rows and by transposes: 48-byte pads.  Grouped heads
 // (SPLIT): one workgroup per query head, writing fp32 shares of dK and dV.
 template <int D, bool SPLIT>
@@ -922,43 +925,77 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
                   float* sfill) {
     load(it + 2, qfill, ofill, sfill);
     const bf16x8_t pp[2] = {pP[0], pP[1]}, ps[2] = {pS[0], pS[1]};
-    if (it < n_it) scores(it, qc, oc);
     const uint16_t* qt = qp + opaque(tb);
     const uint16_t* ot = op + opaque(tb);
-    auto tr_half = [&](int hh, bf16x8_t (&xq)[DT], bf16x8_t (&xo)[DT]) {
+    bf16x8_t xq[2][DT], xo[2][DT];
+    auto tr_all = [&]() {
 #pragma unroll
-      for (int dd = 0; dd < DT; ++dd) {
-        const int o = hh * 16 * PT + dd * 32;
-        xq[dd] = tr_read(qt + o, qt + o + 8 * PT);
-        xo[dd] = tr_read(ot + o, ot + o + 8 * PT);
-      }
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int dd = 0; dd < DT; ++dd) {
+          const int o = hh * 16 * PT + dd * 32;
+          xq[hh][dd] = tr_read(qt + o, qt + o + 8 * PT);
+          xo[hh][dd] = tr_read(ot + o, ot + o + 8 * PT);
+        }
     };
-    bf16x8_t xq0[DT], xo0[DT], xq1[DT], xo1[DT];
-    tr_half(0, xq0, xo0);
+    const int i = qt0 + it;
+    if (it < n_it && i >= first) {
+      // this tile's row fragments, then the previous tile's transposes, read
+      // a few MFMAs ahead of their use under the S and dP chains
+      const uint16_t* qa = qc + opaque(rb);
+      const uint16_t* oa = oc + opaque(rb);
+      bf16x8_t af[KS], bf[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        af[ks] = ld_frag(qa + ks * 16);
+        bf[ks] = ld_frag(oa + ks * 16);
+      }
+      tr_all();
+      zero(sc);
+      zero(dp);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        sc = mfma(af[ks], kf[ks], sc);
+        dp = mfma(bf[ks], vf[ks], dp);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int k = 0; k < 2 * KS; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i == first) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kv > i * BQ + (r >> 2) * 8 + g * 4 + (r & 3)) sc[r] = -INFINITY;
+      }
+    } else {
+      tr_all();
+    }
 #pragma unroll
     for (int dd = 0; dd < DT; ++dd) {
-      dv[dd] = mfma(xo0[dd], pp[0], dv[dd]);
-      dk[dd] = mfma(xq0[dd], ps[0], dk[dd]);
+      dv[dd] = mfma(xo[0][dd], pp[0], dv[dd]);
+      dk[dd] = mfma(xq[0][dd], ps[0], dk[dd]);
     }
-    tr_half(1, xq1, xo1);
     probs_half(0, stc);
 #pragma unroll
     for (int k = 0; k < 2 * DT; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);           // two LDS reads
-      __builtin_amdgcn_sched_group_barrier(0x002, 40 / (2 * DT), 0);  // its VALU share
+      __builtin_amdgcn_sched_group_barrier(0x002, 48 / (2 * DT), 0);  // its VALU share
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int dd = 0; dd < DT; ++dd) {
-      dv[dd] = mfma(xo1[dd], pp[1], dv[dd]);
-      dk[dd] = mfma(xq1[dd], ps[1], dk[dd]);
+      dv[dd] = mfma(xo[1][dd], pp[1], dv[dd]);
+      dk[dd] = mfma(xq[1][dd], ps[1], dk[dd]);
     }
     probs_half(1, stc);
 #pragma unroll
     for (int k = 0; k < 2 * DT; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 40 / (2 * DT), 0);  // its VALU share
+      __builtin_amdgcn_sched_group_barrier(0x002, 48 / (2 * DT), 0);  // its VALU share
     }
     __builtin_amdgcn_sched_barrier(0);
     frags(it);
