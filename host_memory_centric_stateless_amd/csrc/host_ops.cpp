@@ -11,6 +11,7 @@
 // so results do not depend on the thread count.
 #include "host_ops.h"
 
+#include <immintrin.h>
 #include <math.h>
 #include <string.h>
 
@@ -90,6 +91,27 @@ static inline uint16_t rne_bf16(float f) {
 }
 
 static constexpr int64_t kChunk = 1 << 18;  // elements per task
+static constexpr int64_t kStage = 2048;     // elements staged in L1 before a streaming copy-out
+
+// Copies an L1-resident staging block to dst with non-temporal stores for its
+// 32-byte-aligned middle.  Lines that a loop only writes then go to memory
+// without first being read into the cache (no read-for-ownership), which
+// would otherwise add their size again to the host-memory traffic.  The
+// caller issues an sfence before the data is handed on.
+static inline void stream_out(void* dst, const void* src, size_t bytes) {
+  char* d = static_cast<char*>(dst);
+  const char* s = static_cast<const char*>(src);
+  size_t head = (32 - ((uintptr_t)d & 31)) & 31;
+  if (head > bytes) head = bytes;
+  memcpy(d, s, head);
+  d += head;
+  s += head;
+  bytes -= head;
+  for (; bytes >= 32; bytes -= 32, d += 32, s += 32)
+    _mm256_stream_si256(reinterpret_cast<__m256i*>(d),
+                        _mm256_loadu_si256(reinterpret_cast<const __m256i*>(s)));
+  memcpy(d, s, bytes);
+}
 
 template <class F>
 static void chunked(ThreadPool& pool, int64_t n, F&& f) {
@@ -138,21 +160,28 @@ template <bool BF>
 inline void adam_range(const AdamCoef& k, float* __restrict p, const float* __restrict g,
                        float* __restrict m, float* __restrict v, uint16_t* __restrict bf,
                        int64_t b, int64_t e) {
-  for (int64_t i = b; i < e; ++i) {
-    const float gi = g[i];
-    float pi = p[i] * k.decay;
-    float mi = m[i] * k.b1;
-    mi = mi + k.c1 * gi;
-    float vi = v[i] * k.b2;
-    vi = vi + k.c2 * (gi * gi);
-    const float mh = mi / k.bc1;
-    const float vh = vi / k.bc2;
-    pi = pi - (k.lr * mh) / (sqrtf(vh) + k.eps);
-    p[i] = pi;
-    m[i] = mi;
-    v[i] = vi;
-    if (BF) bf[i] = rne_bf16(pi);
+  alignas(64) uint16_t bs[BF ? kStage : 1];  // the bf16 copy is written only: streamed out
+  for (int64_t b0 = b; b0 < e; b0 += kStage) {
+    const int64_t n = std::min(kStage, e - b0);
+    for (int64_t j = 0; j < n; ++j) {
+      const int64_t i = b0 + j;
+      const float gi = g[i];
+      float pi = p[i] * k.decay;
+      float mi = m[i] * k.b1;
+      mi = mi + k.c1 * gi;
+      float vi = v[i] * k.b2;
+      vi = vi + k.c2 * (gi * gi);
+      const float mh = mi / k.bc1;
+      const float vh = vi / k.bc2;
+      pi = pi - (k.lr * mh) / (sqrtf(vh) + k.eps);
+      p[i] = pi;
+      m[i] = mi;
+      v[i] = vi;
+      if (BF) bs[j] = rne_bf16(pi);
+    }
+    if (BF) stream_out(bf + b0, bs, (size_t)n * sizeof(uint16_t));
   }
+  if (BF) _mm_sfence();
 }
 }  // namespace
 
@@ -164,23 +193,40 @@ inline void adam_slab_range(const AdamCoef& k, float* __restrict p, float* __res
                             const void* __restrict slab, int64_t b, int64_t e) {
   const uint16_t* __restrict s16 = static_cast<const uint16_t*>(slab);
   const float* __restrict s32 = static_cast<const float*>(slab);
-  for (int64_t i = b; i < e; ++i) {
-    const float si = SB ? bf16_bits_to_f32(s16[i]) : s32[i];
-    const float gi = ADD ? g[i] + si : si;
-    g[i] = gi;
-    float pi = p[i] * k.decay;
-    float mi = m[i] * k.b1;
-    mi = mi + k.c1 * gi;
-    float vi = v[i] * k.b2;
-    vi = vi + k.c2 * (gi * gi);
-    const float mh = mi / k.bc1;
-    const float vh = vi / k.bc2;
-    pi = pi - (k.lr * mh) / (sqrtf(vh) + k.eps);
-    p[i] = pi;
-    m[i] = mi;
-    v[i] = vi;
-    if (BF) bf[i] = rne_bf16(pi);
+  // Written-only outputs (the gradient when nothing is added to it, the bf16
+  // copy) are staged and streamed out.
+  alignas(64) float gs[ADD ? 1 : kStage];
+  alignas(64) uint16_t bs[BF ? kStage : 1];
+  for (int64_t b0 = b; b0 < e; b0 += kStage) {
+    const int64_t n = std::min(kStage, e - b0);
+    for (int64_t j = 0; j < n; ++j) {
+      const int64_t i = b0 + j;
+      const float si = SB ? bf16_bits_to_f32(s16[i]) : s32[i];
+      float gi;
+      if constexpr (ADD) {
+        gi = g[i] + si;
+        g[i] = gi;
+      } else {
+        gi = si;
+        gs[j] = gi;
+      }
+      float pi = p[i] * k.decay;
+      float mi = m[i] * k.b1;
+      mi = mi + k.c1 * gi;
+      float vi = v[i] * k.b2;
+      vi = vi + k.c2 * (gi * gi);
+      const float mh = mi / k.bc1;
+      const float vh = vi / k.bc2;
+      pi = pi - (k.lr * mh) / (sqrtf(vh) + k.eps);
+      p[i] = pi;
+      m[i] = mi;
+      v[i] = vi;
+      if (BF) bs[j] = rne_bf16(pi);
+    }
+    if (!ADD) stream_out(g + b0, gs, (size_t)n * sizeof(float));
+    if (BF) stream_out(bf + b0, bs, (size_t)n * sizeof(uint16_t));
   }
+  if (!ADD || BF) _mm_sfence();
 }
 
 void adamw(ThreadPool& pool, float* p, const float* g, float* m, float* v, uint16_t* bf, int64_t n,
@@ -219,7 +265,8 @@ void accumulate(ThreadPool& pool, float* grad, const float* src, int64_t n, bool
     if (add) {
       for (int64_t i = b; i < e; ++i) d[i] += s[i];
     } else {
-      memcpy(d + b, s + b, (size_t)(e - b) * sizeof(float));
+      stream_out(d + b, s + b, (size_t)(e - b) * sizeof(float));
+      _mm_sfence();
     }
   });
 }
@@ -238,7 +285,13 @@ void accumulate_bf16(ThreadPool& pool, float* grad, const uint16_t* src, int64_t
     if (add) {
       for (int64_t i = b; i < e; ++i) d[i] += bf16_to_f32(s[i]);
     } else {
-      for (int64_t i = b; i < e; ++i) d[i] = bf16_to_f32(s[i]);
+      alignas(64) float st[kStage];
+      for (int64_t b0 = b; b0 < e; b0 += kStage) {
+        const int64_t n = std::min(kStage, e - b0);
+        for (int64_t j = 0; j < n; ++j) st[j] = bf16_to_f32(s[b0 + j]);
+        stream_out(d + b0, st, (size_t)n * sizeof(float));
+      }
+      _mm_sfence();
     }
   });
 }
