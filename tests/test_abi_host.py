@@ -316,3 +316,50 @@ def test_kernel_register_budget():
             assert vgpr <= 248, (name, vgpr)
         if "copy16" in name:
             assert vgpr <= 16, (name, vgpr)
+
+
+@pytest.mark.parametrize("offset", [0, 1, 3, 7])
+def test_host_streamed_outputs_at_unaligned_addresses(offset):
+    """The written-only outputs (the bf16 working copy, a gradient set rather
+    than added to) leave through a staging block and 32-byte non-temporal
+    stores with plain copies for the unaligned head and tail; at any element
+    offset the result must equal the scalar definition bit for bit."""
+    rng = np.random.default_rng(11)
+    n = 70_001  # several staging blocks and a ragged tail
+    hp = mt.mt_adamw_hparams(1e-3, 0.9, 0.999, 1e-8, 0.01)
+
+    def views(*arrs):  # the same values starting `offset` elements into a larger buffer
+        out = []
+        for a in arrs:
+            big = np.zeros(a.size + offset, a.dtype)
+            v = big[offset:]
+            v[...] = a
+            out.append(v)
+        return out
+
+    master = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    g32 = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    slab = ((g32.view(np.uint32) + np.uint32(0x8000)) >> np.uint32(16)).astype(np.uint16)
+    zero = np.zeros(n, np.float32)
+    # reference: the aligned arrays through the same calls
+    ra = [master.copy(), zero.copy(), zero.copy(), zero.copy(), np.zeros(n, np.uint16)]
+    mt.mt_host_adamw_slab(*ra, slab, 0, hp, 1, threads=3)
+    ua = views(master, zero, zero, zero, np.zeros(n, np.uint16))
+    mt.mt_host_adamw_slab(*ua, views(slab)[0], 0, hp, 1, threads=3)
+    for x, y, name in zip(ra, ua, ["master", "grad", "m", "v", "bf16"]):
+        np.testing.assert_array_equal(x, y, err_msg=name)
+    # the grad written by the set path is the slab value itself
+    np.testing.assert_array_equal(ua[1], (slab.astype(np.uint32) << np.uint32(16)).view(np.float32))
+    # the bf16 copy is the RNE rounding of the updated master
+    ref = torch.from_numpy(np.ascontiguousarray(ua[0])).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(ua[4], ref)
+    # plain AdamW with a bf16 copy, and the fp32 set-accumulate
+    rb = [master.copy(), g32.copy(), zero.copy(), zero.copy(), np.zeros(n, np.uint16)]
+    mt.mt_host_adamw(*rb, hp, 1, threads=2)
+    ub = views(master, g32, zero, zero, np.zeros(n, np.uint16))
+    mt.mt_host_adamw(*ub, hp, 1, threads=2)
+    for x, y in zip(rb, ub):
+        np.testing.assert_array_equal(x, y)
+    (acc,) = views(np.full(n, np.float32(7.0)))
+    mt.mt_host_accumulate(acc, views(g32)[0], 0, threads=4)
+    np.testing.assert_array_equal(acc, g32)
