@@ -408,7 +408,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the method's multi-GPU "
-              "data parallelism is not part of this build", file=sys.stderr)
+              "data parallelism is not implemented in this library", file=sys.stderr)
         sys.exit(2)
 
     import torch
