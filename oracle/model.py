@@ -322,7 +322,7 @@ def forward_backward_whole(params: Dict[int, Dict[str, np.ndarray]], tokens: np.
 def forward_backward_streamed(flats: Dict[int, np.ndarray], tokens: np.ndarray,
                               labels: np.ndarray, cfg, grad_scale: float, K: int,
                               grad_flats: Dict[int, np.ndarray], accumulate: bool,
-                              stats: Optional[dict] = None, routing=None):
+                              stats: Optional[dict] = None, routing=None, progress=None):
     """Streamed execution with segment recompute.
 
     flats: {group: flat array} holding the weights (lqnn 三.1).  Forward keeps
@@ -332,9 +332,12 @@ def forward_backward_streamed(flats: Dict[int, np.ndarray], tokens: np.ndarray,
     flat array and written (accumulate=False) or added (accumulate=True) into
     ``grad_flats[group]`` -- the host gradient of lqnn 二 / 三.3.
     routing: optional {layer: expert selection} for mixture-of-experts blocks.
+    progress: optional callable taking a short message after each layer (for
+    long runs; it sees no values).
     Returns the micro-batch loss.
     """
     routing = routing or {}
+    say = progress or (lambda msg: None)
     dtype = flats[L.EMBED].dtype
     cos, sin = _tables(cfg, dtype)
     b = tokens.shape[0]
@@ -345,8 +348,10 @@ def forward_backward_streamed(flats: Dict[int, np.ndarray], tokens: np.ndarray,
         if l % K == 0:
             ckpt.append(x)
         x, _ = block_forward(L.unpack(cfg, l, flats[l]), x, cfg, cos, sin, b, routing.get(l))
+        say(f"forward layer {l}")
     loss, dy, gh = head_forward_backward(L.unpack(cfg, L.HEAD, flats[L.HEAD]), x,
                                          labels.reshape(-1), grad_scale, cfg.rms_eps)
+    say("head")
 
     def land(group, gdict):
         gf = L.pack(cfg, group, gdict, dtype=dtype)
@@ -365,10 +370,12 @@ def forward_backward_streamed(flats: Dict[int, np.ndarray], tokens: np.ndarray,
             x, c = block_forward(L.unpack(cfg, l, flats[l]), x, cfg, cos, sin, b, routing.get(l))
             window.append(c)
             recomputed += 1
+            say(f"recompute layer {l}")
         for l in reversed(range(lo, hi)):
             dy, gl = block_backward(L.unpack(cfg, l, flats[l]), window[l - lo], dy, cfg, cos,
                                     sin, b)
             land(l, gl)
+            say(f"backward layer {l}")
     land(L.EMBED, {"emb": embed_bwd(dy, tokens, cfg.vocab)})
     if stats is not None:
         stats["recomputed_layers"] = recomputed

@@ -9,5 +9,7 @@ if ROOT not in sys.path:
 
 
 def pytest_configure(config):
+    from tests import gpu_util
+    gpu_util.PYTEST_CONFIG = config
     config.addinivalue_line("markers", "gpu: needs an MI355X (runs through the C-ABI library)")
     config.addinivalue_line("markers", "slow: CPU test that takes more than a few seconds")

@@ -2,6 +2,19 @@
 import numpy as np
 import torch
 
+PYTEST_CONFIG = None  # set by conftest.py
+
+
+def progress(msg: str) -> None:
+    """A progress line of a long test, shown even when pytest captures output
+    (so that a minutes-long oracle run is not silent)."""
+    capman = PYTEST_CONFIG.pluginmanager.getplugin("capturemanager") if PYTEST_CONFIG else None
+    if capman is None:
+        print(msg, flush=True)
+        return
+    with capman.global_and_fixture_disabled():
+        print(msg, flush=True)
+
 
 def dev():
     return torch.device("cuda:0")

@@ -40,7 +40,7 @@ import torch
 from oracle.model import forward_backward_streamed
 from oracle.train import HostState
 from synth_inputs import PRESETS, make_batch, weight_stream
-from tests.gpu_util import rel_l2
+from tests.gpu_util import progress, rel_l2
 from tests.test_gpu_step import (GRAD_TOL, LOSS_TOL, WEIGHT_TOL, _session, _tensors,
                                  gradients_at_matched_weights, independent_trajectories)
 
@@ -64,7 +64,9 @@ def _oracle_grads(cfg, tok, lab, round_bf16):
             st.master[g][...] = _bf16(st.master[g])
     acc = tok.shape[0]
     losses = [forward_backward_streamed(st.master, tok[i], lab[i], cfg, 1.0 / acc,
-                                        cfg.ckpt_interval, st.grad, accumulate=i > 0)
+                                        cfg.ckpt_interval, st.grad, accumulate=i > 0,
+                                        progress=lambda m, i=i: progress(
+                                            f"  {cfg.name} oracle micro-batch {i}: {m}"))
               for i in range(acc)]
     return float(np.mean([float(x) for x in losses])), _tensors(cfg, st.grad)
 
@@ -76,17 +78,17 @@ def parity_with_floor(cfg, floor=True, **kw):
     tok, lab = make_batch(cfg, 1)
     sess = _session(cfg, **kw)
     try:
-        print(f"{cfg.name}: gpu step", flush=True)
+        progress(f"{cfg.name}: gpu step")
         gl = sess.forward_backward(tok, lab)
         gg = _tensors(cfg, sess.grad)
         stats = sess.stats()
     finally:
         sess.close()
-    print(f"{cfg.name}: oracle at the fp32 masters", flush=True)
+    progress(f"{cfg.name}: oracle at the fp32 masters")
     ol, og = _oracle_grads(cfg, tok, lab, False)
     fb = None
     if floor:
-        print(f"{cfg.name}: oracle at the bf16 working copy", flush=True)
+        progress(f"{cfg.name}: oracle at the bf16 working copy")
         _, fb = _oracle_grads(cfg, tok, lab, True)
     print(f"{cfg.name}: loss gpu {gl:.6f} oracle {ol:.6f}; stats {stats}", flush=True)
     assert abs(gl - ol) <= LOSS_TOL

@@ -14,7 +14,7 @@ import pytest
 from oracle import layout as OL
 from oracle.train import HostState, train_step
 from synth_inputs import PRESETS, make_batch, weight_stream
-from tests.gpu_util import rel_l2
+from tests.gpu_util import progress, rel_l2
 
 pytestmark = pytest.mark.gpu
 
@@ -90,6 +90,7 @@ def independent_trajectories(cfg, steps):
             tok, lab = make_batch(cfg, step)
             gl = sess.forward_backward(tok, lab)
             mt_adamw_step(sess.ctx, mt_adamw_hparams(cfg.lr, 0.9, 0.999, 1e-8, 0.01), step)
+            progress(f"{cfg.name}: step {step} on the GPU done, oracle step")
             ol = train_step(st, tok, lab, step)
             losses.append((gl, ol))
         gw, ow = _tensors(cfg, sess.master), _tensors(cfg, st.master)
