@@ -30,7 +30,7 @@ sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
-KERNEL_COPY_WGS = (4, 8, 32)
+KERNEL_COPY_WGS = (3, 4, 8, 32)
 
 
 def layer_matrix_params(cfg, layer: int) -> int:

@@ -197,7 +197,7 @@ def _stream(s):
 
 
 # ------------------------------------------------------------ config helpers
-DEFAULT_DRAIN_WORKGROUPS = 4  # slabs leave through a 4-workgroup copy kernel
+DEFAULT_DRAIN_WORKGROUPS = 3  # slabs leave through a 3-workgroup copy kernel
 
 
 def make_config(cfg, host_threads: int = 0, slab_bf16: bool = True,
