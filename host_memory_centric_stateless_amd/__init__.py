@@ -197,7 +197,19 @@ def _stream(s):
 
 
 # ------------------------------------------------------------ config helpers
-DEFAULT_DRAIN_WORKGROUPS = 3  # slabs leave through a 3-workgroup copy kernel
+DEFAULT_DRAIN_WORKGROUPS = 4  # slabs leave through a 4-workgroup copy kernel
+
+
+def default_drain_workgroups(cfg, slab_bf16: bool = True, micro_batches_per_pass: int = 1) -> int:
+    """Copy-kernel workgroups for the slab drain.  A drain of three
+    workgroups leaves the weight loads more of the link and trails into the
+    next micro-batch's forward pass, whose device-to-host direction is
+    otherwise idle: that needs a next micro-batch in the step (more passes per
+    step than one) and bf16 slabs (fp32 slabs carry twice the bytes).
+    Otherwise the tail of the drain would hold up the step's end, and four
+    workgroups keep up."""
+    passes = max(1, int(getattr(cfg, "grad_accum", 1)) // max(1, int(micro_batches_per_pass)))
+    return 3 if (slab_bf16 and passes > 1) else DEFAULT_DRAIN_WORKGROUPS
 
 
 def make_config(cfg, host_threads: int = 0, slab_bf16: bool = True,

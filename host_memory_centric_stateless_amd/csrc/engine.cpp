@@ -94,10 +94,11 @@ enum State { ST_UNBOUND, ST_IDLE, ST_FWD, ST_BWD, ST_FLUSHED };
 // fell to 7-16 GB/s on the copy engine.  A 4-workgroup copy kernel keeps
 // ~38 GB/s device->host with host->device unchanged at ~57 GB/s; with 8 or
 // more workgroups the two directions saturate the link and kernels sharing
-// CUs with the copy stall on its host stores for milliseconds.  Inside the
-// streamed step three workgroups do best: the drain (~24 GB/s) then trails
-// into the next forward, whose device->host direction is otherwise idle,
-// and the weight loads keep ~51 GB/s instead of ~46 beside four.
+// CUs with the copy stall on its host stores for milliseconds.  When a step
+// has several micro-batches, three workgroups do better: the drain (~24 GB/s)
+// then trails into the next micro-batch's forward, whose device->host
+// direction is otherwise idle, and the weight loads keep ~51 GB/s instead of
+// ~46 beside four.
 
 double now_s() {
   return std::chrono::duration<double>(std::chrono::steady_clock::now().time_since_epoch())

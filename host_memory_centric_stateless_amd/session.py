@@ -12,7 +12,7 @@ from typing import Dict, Iterable, Optional, Tuple
 import numpy as np
 import torch
 
-from . import (DEFAULT_DRAIN_WORKGROUPS, MT_GROUP_EMBED, MT_GROUP_HEAD, make_config, mt_adamw_hparams, mt_adamw_step,
+from . import (MT_GROUP_EMBED, MT_GROUP_HEAD, default_drain_workgroups, make_config, mt_adamw_hparams, mt_adamw_step,
                mt_backward, mt_backward_step, mt_bind_layer, mt_create, mt_destroy, mt_device_arena,
                mt_device_requirements, mt_flush_grads, mt_forward, mt_get_stats, mt_layout,
                mt_step_loss, mt_sync_loss)
@@ -39,7 +39,8 @@ class Session:
             cfg = cfg.replace(n_grad_slabs=n_grad_slabs)
         self.cfg = cfg
         self.c = make_config(cfg, host_threads, slab_bf16,
-                             DEFAULT_DRAIN_WORKGROUPS if drain_workgroups is None
+                             default_drain_workgroups(cfg, slab_bf16, micro_batches_per_pass)
+                             if drain_workgroups is None
                              else drain_workgroups, micro_batches_per_pass, head_token_chunk)
         self.mb_per_pass = micro_batches_per_pass
         self.req = mt_device_requirements(self.c)
