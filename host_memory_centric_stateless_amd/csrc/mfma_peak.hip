@@ -1,6 +1,6 @@
 // MFMA ceiling probe: the dense bf16 MFMA rate one launch sustains with
 // operands in registers and no memory traffic in the loop.  It measures the
-// ceiling the GEMM and attention kernels are judged against next to the
+// ceiling the GEMM and attention kernels are measured against next to the
 // nominal 2.5 PFLOP/s, on the same clock as they run.
 #include "common.h"
 

@@ -105,7 +105,7 @@ def parity_with_floor(cfg, floor=True, **kw):
 FLOOR_RATIO = 1.5
 
 
-def judge(rows, pinned_floor=()):
+def check_against_floor(rows, pinned_floor=()):
     """Assert the fault bound and, where the floor was measured, that every
     tensor's error stays within FLOOR_RATIO times its weight-copy floor (the
     kernels' bf16 operands add error of the same size as the working copy's
@@ -159,20 +159,22 @@ def test_c2_three_step_trajectory():
 
 @pytest.mark.timeout(400)
 def test_7b_shape_two_layers():
-    judge(parity_with_floor(PRESETS["C3"].replace(n_layers=2, grad_accum=1, ckpt_interval=1)),
-          LAST_BLOCK_QK)
+    cfg = PRESETS["C3"].replace(n_layers=2, grad_accum=1, ckpt_interval=1)
+    check_against_floor(parity_with_floor(cfg), LAST_BLOCK_QK)
 
 
 @pytest.mark.timeout(500)
 def test_14b_gqa_shape_two_layers():
-    judge(parity_with_floor(PRESETS["C4"].replace(n_layers=2, ckpt_interval=2)), LAST_BLOCK_QK)
+    cfg = PRESETS["C4"].replace(n_layers=2, ckpt_interval=2)
+    check_against_floor(parity_with_floor(cfg), LAST_BLOCK_QK)
 
 
 @pytest.mark.timeout(500)
 def test_7b_shape_four_accumulated_microbatches():
     """The 7B shape's own gradient accumulation (4 micro-batches of 1 x 4096
     per step, slabs accumulated on the host) at 2 layers."""
-    judge(parity_with_floor(PRESETS["C3"].replace(n_layers=2, ckpt_interval=1), floor=False))
+    cfg = PRESETS["C3"].replace(n_layers=2, ckpt_interval=1)
+    check_against_floor(parity_with_floor(cfg, floor=False))
 
 
 @pytest.mark.timeout(500)
@@ -183,7 +185,8 @@ def test_7b_shape_four_layers_recompute():
     """4 layers with a checkpoint every 2: the first segment is recomputed
     from its checkpoint before its backward; the error grows with depth at
     the same ratio to the floor."""
-    judge(parity_with_floor(PRESETS["C3"].replace(n_layers=4, grad_accum=1, ckpt_interval=2)))
+    cfg = PRESETS["C3"].replace(n_layers=4, grad_accum=1, ckpt_interval=2)
+    check_against_floor(parity_with_floor(cfg))
 
 
 @pytest.mark.timeout(600)
@@ -191,5 +194,5 @@ def test_7b_layer_long_sequence():
     """One 7B-shaped layer on one sequence of 16,384 tokens: long causal
     attention (256 key tiles, RoPE positions up to 16,383) and weight-gradient
     products that reduce over 16,384 tokens."""
-    judge(parity_with_floor(PRESETS["C3"].replace(n_layers=1, grad_accum=1, ckpt_interval=1,
-                                                  seq_len=16384), floor=False))
+    cfg = PRESETS["C3"].replace(n_layers=1, grad_accum=1, ckpt_interval=1, seq_len=16384)
+    check_against_floor(parity_with_floor(cfg, floor=False))
