@@ -1,6 +1,7 @@
 """Summarise a rocprofv3 kernel + memory-copy trace of a streamed training run.
 
-    python -m host_memory_centric_stateless_amd.trace_summary <dir>/<prefix> [--window last]
+    python -m host_memory_centric_stateless_amd.trace_summary <dir>/<prefix> [--start-frac F]
+        [--micro-batches N]
 
 Reads <prefix>_kernel_trace.csv and <prefix>_memory_copy_trace.csv (rocprofv3
 --kernel-trace --memory-copy-trace --output-format csv) and prints:
@@ -11,10 +12,13 @@ Reads <prefix>_kernel_trace.csv and <prefix>_memory_copy_trace.csv (rocprofv3
   kernel writing pinned host memory and so appears in the kernel trace);
 * copy/compute overlap = |copies AND kernels| / min(|copies|, |kernels|)
   (union measure), for H2D, D2H and both;
-* large-copy durations (copies longer than 1 ms).
+* large-copy durations (copies longer than 1 ms);
+* the host-to-device link idle between weight loads, and the times the
+  micro-batch losses are reduced (step and micro-batch boundaries).
 
---window last restricts everything to the span of the last `--last-frac` of
-the run's copy activity (default: whole trace).
+--start-frac F starts the window F of the way into the trace (default: the
+whole trace); --micro-batches N (micro-batches per step) adds, per step, the
+link's busy and idle time between weight loads.
 """
 from __future__ import annotations
 
@@ -66,7 +70,7 @@ def clip(iv, lo, hi):
     return [(max(a, lo), min(b, hi)) for a, b in iv if b > lo and a < hi]
 
 
-def summarize(prefix: str, t0: int = None, t1: int = None) -> str:
+def summarize(prefix: str, t0: int = None, t1: int = None, micro_batches: int = 0) -> str:
     kt = _read(prefix + "_kernel_trace.csv")
     mc = _read(prefix + "_memory_copy_trace.csv")
     kern = [(int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]) for r in kt]
@@ -107,6 +111,40 @@ def summarize(prefix: str, t0: int = None, t1: int = None) -> str:
     if drain:
         dt = sum(b - a for a, b in clip(drain, lo, hi))
         lines.append(f"drain kernels: n={len(drain)} total {dt / 1e6:.1f} ms")
+    # Link idle between weight loads (host-to-device copies over 1 ms).  With two
+    # weight buffers the short gaps are the bubbles where both buffers hold
+    # blocks still needed; the long ones are step boundaries and the run's end.
+    loads = sorted((a, b) for a, b in h2d if b - a > 1_000_000)
+    gaps = [(s1 - e0, e0) for (_, e0), (s1, _) in zip(loads, loads[1:]) if s1 > e0]
+    if gaps:
+        short = [g for g, _ in gaps if 2_000_000 <= g < 20_000_000]
+        long_ = sorted((gt for gt in gaps if gt[0] >= 20_000_000), reverse=True)
+        lines.append(f"H2D idle between weight loads: {sum(g for g, _ in gaps) / 1e6:.1f} ms in "
+                     f"{len(gaps)} gaps; 2-20 ms: n={len(short)} total {sum(short) / 1e6:.1f} ms"
+                     + (f" (mean {sum(short) / len(short) / 1e6:.2f})" if short else "")
+                     + f"; >= 20 ms: n={len(long_)} total {sum(g for g, _ in long_) / 1e6:.1f} ms")
+        for g, t in long_[:4]:
+            lines.append(f"  gap {g / 1e6:7.1f} ms from {(t - lo) / 1e9:.3f} s")
+    marks = sorted(a for a, _, n in kern if "loss_reduce_kernel" in n)
+    if marks:
+        lines.append("micro-batch losses reduced at (s): "
+                     + " ".join(f"{(t - lo) / 1e9:.3f}" for t in marks))
+    # Per step (from one step's last loss reduction to the next one's): link busy
+    # and idle between weight loads, by gap length.
+    if micro_batches > 0:
+        classes = ((0, 500_000), (500_000, 4_500_000), (4_500_000, 20_000_000), (20_000_000, None))
+        for j in range(micro_batches - 1, len(marks) - micro_batches, micro_batches):
+            a, b = marks[j], marks[j + micro_batches]
+            inside = [(s, e) for s, e in loads if a <= s < b]
+            idle = [g for g, t in gaps if a <= t < b]
+            parts = []
+            for c0, c1 in classes:
+                x = [g for g in idle if g >= c0 and (c1 is None or g < c1)]
+                label = f"{c0 / 1e6:g}-{c1 / 1e6:g} ms" if c1 else f">= {c0 / 1e6:g} ms"
+                parts.append(f"{label}: n={len(x)} {sum(x) / 1e6:.1f} ms")
+            lines.append(f"step {(a - lo) / 1e9:.3f}-{(b - lo) / 1e9:.3f} s ({(b - a) / 1e6:.0f} ms): "
+                         f"{len(inside)} weight loads busy {sum(e - s for s, e in inside) / 1e6:.0f} ms, "
+                         f"link idle {sum(idle) / 1e6:.0f} ms; " + "; ".join(parts))
     # Compute time with no copy in flight, by kernel: what keeps the overlap below 1.
     lone = defaultdict(int)
     cends = [e for _, e in C]
@@ -135,6 +173,8 @@ def main():
     ap.add_argument("prefix")
     ap.add_argument("--start-frac", type=float, default=0.0,
                     help="start the window this fraction into the trace")
+    ap.add_argument("--micro-batches", type=int, default=0,
+                    help="micro-batches per step: break the link idle time down per step")
     a = ap.parse_args()
     t0 = None
     if a.start_frac > 0:
@@ -142,7 +182,7 @@ def main():
         lo = min(int(r["Start_Timestamp"]) for r in kt)
         hi = max(int(r["End_Timestamp"]) for r in kt)
         t0 = int(lo + a.start_frac * (hi - lo))
-    print(summarize(a.prefix, t0=t0))
+    print(summarize(a.prefix, t0=t0, micro_batches=a.micro_batches))
 
 
 if __name__ == "__main__":
