@@ -30,6 +30,8 @@ from typing import List, Tuple
 
 Interval = Tuple[int, int]
 DRAIN = "copy16_kernel"  # gradient slab -> pinned host copy kernel
+# link-idle gap classes, ns: [start, end), end None = open
+GAP_CLASSES = ((0, 500_000), (500_000, 4_500_000), (4_500_000, 20_000_000), (20_000_000, None))
 
 
 def _read(path):
@@ -111,40 +113,41 @@ def summarize(prefix: str, t0: int = None, t1: int = None, micro_batches: int = 
     if drain:
         dt = sum(b - a for a, b in clip(drain, lo, hi))
         lines.append(f"drain kernels: n={len(drain)} total {dt / 1e6:.1f} ms")
-    # Link idle between weight loads (host-to-device copies over 1 ms).  With two
-    # weight buffers the short gaps are the bubbles where both buffers hold
-    # blocks still needed; the long ones are step boundaries and the run's end.
+    # Link idle between weight loads (host-to-device copies over 1 ms), by gap
+    # length.  With two weight buffers the 4.5-20 ms gaps are the bubbles where
+    # both buffers hold blocks still needed; the long ones are step boundaries
+    # and the end of the run.
     loads = sorted((a, b) for a, b in h2d if b - a > 1_000_000)
     gaps = [(s1 - e0, e0) for (_, e0), (s1, _) in zip(loads, loads[1:]) if s1 > e0]
+
+    def by_length(idle):
+        parts = []
+        for c0, c1 in GAP_CLASSES:
+            x = [g for g in idle if g >= c0 and (c1 is None or g < c1)]
+            label = f"{c0 / 1e6:g}-{c1 / 1e6:g} ms" if c1 else f">= {c0 / 1e6:g} ms"
+            parts.append(f"{label}: n={len(x)} {sum(x) / 1e6:.1f} ms")
+        return "; ".join(parts)
+
     if gaps:
-        short = [g for g, _ in gaps if 2_000_000 <= g < 20_000_000]
-        long_ = sorted((gt for gt in gaps if gt[0] >= 20_000_000), reverse=True)
         lines.append(f"H2D idle between weight loads: {sum(g for g, _ in gaps) / 1e6:.1f} ms in "
-                     f"{len(gaps)} gaps; 2-20 ms: n={len(short)} total {sum(short) / 1e6:.1f} ms"
-                     + (f" (mean {sum(short) / len(short) / 1e6:.2f})" if short else "")
-                     + f"; >= 20 ms: n={len(long_)} total {sum(g for g, _ in long_) / 1e6:.1f} ms")
-        for g, t in long_[:4]:
+                     f"{len(gaps)} gaps; " + by_length([g for g, _ in gaps]))
+        for g, t in sorted((gt for gt in gaps if gt[0] >= GAP_CLASSES[-1][0]), reverse=True)[:4]:
             lines.append(f"  gap {g / 1e6:7.1f} ms from {(t - lo) / 1e9:.3f} s")
     marks = sorted(a for a, _, n in kern if "loss_reduce_kernel" in n)
     if marks:
         lines.append("micro-batch losses reduced at (s): "
                      + " ".join(f"{(t - lo) / 1e9:.3f}" for t in marks))
-    # Per step (from one step's last loss reduction to the next one's): link busy
-    # and idle between weight loads, by gap length.
+    # Per step, counting micro-batches from the first loss reduction in the
+    # window (taken as a step's first): from one step's last reduction to the
+    # next one's, the weight loads and the link idle time between them.
     if micro_batches > 0:
-        classes = ((0, 500_000), (500_000, 4_500_000), (4_500_000, 20_000_000), (20_000_000, None))
         for j in range(micro_batches - 1, len(marks) - micro_batches, micro_batches):
             a, b = marks[j], marks[j + micro_batches]
             inside = [(s, e) for s, e in loads if a <= s < b]
             idle = [g for g, t in gaps if a <= t < b]
-            parts = []
-            for c0, c1 in classes:
-                x = [g for g in idle if g >= c0 and (c1 is None or g < c1)]
-                label = f"{c0 / 1e6:g}-{c1 / 1e6:g} ms" if c1 else f">= {c0 / 1e6:g} ms"
-                parts.append(f"{label}: n={len(x)} {sum(x) / 1e6:.1f} ms")
             lines.append(f"step {(a - lo) / 1e9:.3f}-{(b - lo) / 1e9:.3f} s ({(b - a) / 1e6:.0f} ms): "
                          f"{len(inside)} weight loads busy {sum(e - s for s, e in inside) / 1e6:.0f} ms, "
-                         f"link idle {sum(idle) / 1e6:.0f} ms; " + "; ".join(parts))
+                         f"link idle {sum(idle) / 1e6:.0f} ms; " + by_length(idle))
     # Compute time with no copy in flight, by kernel: what keeps the overlap below 1.
     lone = defaultdict(int)
     cends = [e for _, e in C]

@@ -34,9 +34,9 @@ def test_link_idle_and_per_step_split(tmp_path):
                ("loss_reduce_kernel", int(40 * MS), int(40.1 * MS)),
                ("loss_reduce_kernel", int(75 * MS), int(75.1 * MS))]
     out = summarize(_write(tmp_path, kernels, copies), micro_batches=1)
-    assert "H2D idle between weight loads: 38.2 ms in 4 gaps" in out
-    assert "2-20 ms: n=2 total 8.0 ms (mean 4.00)" in out
-    assert ">= 20 ms: n=1 total 30.0 ms" in out
+    assert ("H2D idle between weight loads: 38.2 ms in 4 gaps; 0-0.5 ms: n=1 0.2 ms; "
+            "0.5-4.5 ms: n=1 2.0 ms; 4.5-20 ms: n=1 6.0 ms; >= 20 ms: n=1 30.0 ms") in out
+    assert "  gap    30.0 ms from 0.030 s" in out
     # steps from one loss reduction to the next: [2, 40) ms holds the loads from
     # 8.2 and 22.2 ms and the gaps ending at 8.0 (0.2), 16.2 (6.0) and 30.2 ms
     # (30.0); [40, 75) ms the loads from 60.2 and 70.2 ms and the 2 ms gap
