@@ -363,3 +363,20 @@ def test_host_streamed_outputs_at_unaligned_addresses(offset):
     (acc,) = views(np.full(n, np.float32(7.0)))
     mt.mt_host_accumulate(acc, views(g32)[0], 0, threads=4)
     np.testing.assert_array_equal(acc, g32)
+
+
+def test_default_drain_workgroups_rule():
+    """Three drain workgroups only for bf16 slabs with more than one pass per
+    step (the drain then trails into the next micro-batch's forward); four
+    otherwise (one pass per step, or fp32 slabs with twice the bytes)."""
+    c3, c2 = PRESETS["C3"], PRESETS["C2"]
+    assert c3.grad_accum == 4
+    assert mt.default_drain_workgroups(c3) == 3
+    assert mt.default_drain_workgroups(c3, slab_bf16=False) == mt.DEFAULT_DRAIN_WORKGROUPS == 4
+    assert mt.default_drain_workgroups(c3, micro_batches_per_pass=4) == 4  # one pass per step
+    assert mt.default_drain_workgroups(c3, micro_batches_per_pass=2) == 3  # two passes
+    assert mt.default_drain_workgroups(c3.replace(grad_accum=1)) == 4
+    assert c2.grad_accum == 1 and mt.default_drain_workgroups(c2) == 4  # 4 sequences, one pass
+    # the session passes the rule's value unless the caller chooses one
+    cfg = mt.make_config(c3, drain_workgroups=mt.default_drain_workgroups(c3))
+    assert cfg.drain_workgroups == 3
